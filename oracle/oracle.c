@@ -1,0 +1,198 @@
+/*
+ * CPU oracle for the Linear-layer backward and the fused unscale + AdamW update.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the bench's CPU
+ * baseline leg use it.  It shares no code, header, table or constant with the
+ * HIP library; it is built by gcc with -O2 -ffp-contract=off and no fast-math,
+ * so every float operation below is one IEEE-754 operation, rounded to
+ * nearest even, in the order written.
+ *
+ * What it computes, and where the pages define it:
+ *
+ *  - Linear layer Y = X·W with X[M,K], W[K,N] (batch and sequence flattened
+ *    into M) and upstream gradient G = dL/dY [M,N]:
+ *        dX = G·Wᵀ      dX[m,k] = Σ_n G[m,n]·W[k,n]
+ *        dW = Xᵀ·G      dW[k,n] = Σ_m X[m,k]·G[m,n]
+ *    Pages: "GPU 优化实战 Part 2", section "反向传播——Linear 层的梯度"
+ *    (the two backward products of a Linear layer); "GPU 如何训练模型：从算子
+ *    到 Kernel", section "一个线性层，前向和反向到底在算什么" (shapes with batch
+ *    and sequence merged into M, transposes expressed through strides).
+ *    The oracle evaluates both sums in fp64 on the exact decoded input values,
+ *    as plain loops with no blocking or reordering.
+ *
+ *  - AdamW with decoupled weight decay on an fp32 master copy, after
+ *    unscaling a loss-scaled gradient:
+ *        g  = float(g_in) * inv_scale
+ *        m  = b1*m + (1-b1)*g
+ *        v  = b2*v + (1-b2)*g*g
+ *        mh = m / (1 - b1^t)        vh = v / (1 - b2^t)
+ *        W  = W - lr*( mh/(sqrt(vh)+eps) + wd*W )      (W on the right: old W)
+ *    Pages: "GPU 优化实战 Part 2", sections "AdamW 优化器——融合内核" (the
+ *    per-parameter update and its bias corrections) and "混合精度训练（FP16 /
+ *    BF16）" (loss scale, unscale by multiplying with 1/scale before the
+ *    update); "Mastering LLM Training with CUDA and ROCm", section "AdamW
+ *    Algorithm" (the same update written as θ − η·m̂/(√v̂+ε) − η·λ·θ).
+ *    The oracle is a scalar fp32 loop.  The bias corrections are evaluated
+ *    once per call in double and rounded to float once.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* element types of the caller's buffers */
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+#define ORACLE_F16 2
+
+/* ---- exact decoders ---------------------------------------------------- */
+
+/* bf16 is the upper half of an IEEE binary32: widening is a 16-bit shift. */
+double oracle_bf16_to_f64(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 mantissa bits. */
+double oracle_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int mant = h & 0x3ff;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)mant, -24); /* subnormal: mant * 2^-14 * 2^-10 */
+    else if (e == 31)
+        mag = mant ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(mant | 0x400), e - 25); /* 1.mant * 2^(e-15) */
+    return sign ? -mag : mag;
+}
+
+static double elt(const void *p, int dtype, int64_t i)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)p)[i];
+    if (dtype == ORACLE_BF16)
+        return oracle_bf16_to_f64(((const uint16_t *)p)[i]);
+    return oracle_f16_to_f64(((const uint16_t *)p)[i]);
+}
+
+void oracle_decode(const void *p, int dtype, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = elt(p, dtype, i);
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---- Linear backward, fp64 ---------------------------------------------- */
+
+/* dX[m,k] = Σ_n G[m,n]·W[k,n], all M·K entries.  Row-major, contiguous. */
+void oracle_dx(const void *G, const void *W, int dtype,
+               int64_t M, int64_t K, int64_t N, double *dX)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            double s = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                s += elt(G, dtype, m * N + n) * elt(W, dtype, k * N + n);
+            dX[m * K + k] = s;
+        }
+}
+
+/* dW[k,n] = Σ_m X[m,k]·G[m,n], all K·N entries. */
+void oracle_dw(const void *X, const void *G, int dtype,
+               int64_t M, int64_t K, int64_t N, double *dW)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int64_t m = 0; m < M; ++m)
+                s += elt(X, dtype, m * K + k) * elt(G, dtype, m * N + n);
+            dW[k * N + n] = s;
+        }
+}
+
+/* The same sums at a list of (row, col) positions only: out[i] = dX[rows[i], cols[i]]. */
+void oracle_dx_at(const void *G, const void *W, int dtype,
+                  int64_t M, int64_t K, int64_t N,
+                  const int64_t *rows, const int64_t *cols, int64_t cnt, double *out)
+{
+    (void)M;
+    (void)K;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < cnt; ++i) {
+        int64_t m = rows[i], k = cols[i];
+        double s = 0.0;
+        for (int64_t n = 0; n < N; ++n)
+            s += elt(G, dtype, m * N + n) * elt(W, dtype, k * N + n);
+        out[i] = s;
+    }
+}
+
+/* out[i] = dW[rows[i], cols[i]] (rows index K, cols index N). */
+void oracle_dw_at(const void *X, const void *G, int dtype,
+                  int64_t M, int64_t K, int64_t N,
+                  const int64_t *rows, const int64_t *cols, int64_t cnt, double *out)
+{
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < cnt; ++i) {
+        int64_t k = rows[i], n = cols[i];
+        double s = 0.0;
+        for (int64_t m = 0; m < M; ++m)
+            s += elt(X, dtype, m * K + k) * elt(G, dtype, m * N + n);
+        out[i] = s;
+    }
+}
+
+/* ---- unscale + AdamW, scalar fp32 --------------------------------------- */
+
+static float grad_f32(const void *g, int gtype, int64_t i)
+{
+    if (gtype == ORACLE_F32)
+        return ((const float *)g)[i];
+    /* bf16 and fp16 values are exactly representable in binary32 */
+    return (float)elt(g, gtype, i);
+}
+
+/*
+ * One AdamW step over n parameters, in place on W, m, v.  g is read only.
+ * Returns 0, or -1 for arguments under which the update is undefined
+ * (step < 1, or a beta outside [0,1) which makes a bias correction zero or
+ * meaningless).
+ */
+int oracle_adamw(float *W, const void *g, int gtype, float *m, float *v, int64_t n,
+                 float lr, float b1, float b2, float eps, float wd, int step,
+                 float inv_scale)
+{
+    if (step < 1 || !(b1 >= 0.0f && b1 < 1.0f) || !(b2 >= 0.0f && b2 < 1.0f) || n < 0)
+        return -1;
+    const float bc1 = (float)(1.0 - pow((double)b1, (double)step));
+    const float bc2 = (float)(1.0 - pow((double)b2, (double)step));
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float gi = grad_f32(g, gtype, i) * inv_scale;
+        m[i] = b1 * m[i] + (1.0f - b1) * gi;
+        v[i] = b2 * v[i] + (1.0f - b2) * gi * gi;
+        float mh = m[i] / bc1;
+        float vh = v[i] / bc2;
+        W[i] = W[i] - lr * (mh / (sqrtf(vh) + eps) + wd * W[i]);
+    }
+    return 0;
+}
