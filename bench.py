@@ -1,0 +1,314 @@
+"""Benchmark: Linear backward (dX + dW, bf16 MFMA) + fused unscale/AdamW on one MI355X.
+
+Default workload (one "step" = the whole hot path once): one Transformer
+block's four projections at M = 16384 tokens (QKV 4096->12288, out 4096->4096,
+up 4096->16384, down 16384->4096), lin_bwd on each, then one fused
+unscale + AdamW pass (bf16 gradients x1024, step 100) over all 201,326,592
+parameters.  Inputs are seeded synthetic draws made on the GPU before the
+timed region.
+
+Prints one JSON line.  ``value`` is the whole step's throughput: the step's
+GEMM FLOPs (4·M·K·N per projection) divided by the wall time of the whole
+step including the AdamW pass.  The per-kernel figures come from HIP events
+recorded on the launch stream around every launch of the timed steps.
+
+Roofline model ("GPU 如何训练模型：从算子到 Kernel", section "Roofline：先判断
+“算不动”还是“搬不动”"): an op of F FLOP moving Q bytes cannot finish before
+max(F/P, Q/B); the ideal GEMM traffic is Q = b·(MK + KN + MN).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "lin-bwd TFLOP/s (dX+dW, bf16) + fused AdamW GB/s; % of roofline, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+ADAMW_BYTES_16BIT_GRAD = 26   # read g(2) W m v (12), write W m v (12)
+ADAMW_BYTES_F32_GRAD = 28
+
+
+def ideal_intensity(M, K, N, bytes_per_elem=2):
+    """FLOP per byte of one GEMM of 2MKN FLOP moving b·(MK+KN+MN) bytes."""
+    return 2.0 * M * K * N / (bytes_per_elem * (M * K + K * N + M * N))
+
+
+def lin_bwd_flops(M, K, N):
+    """dX = G·Wᵀ and dW = Xᵀ·G: 2MKN each."""
+    return 4.0 * M * K * N
+
+
+def lin_bwd_min_bytes(M, K, N):
+    """Algorithmic HBM bytes of lin_bwd: read X, W, G (bf16), write dX (bf16) and dW (fp32)."""
+    return 2 * (M * K + K * N + M * N) + 2 * M * K + 4 * K * N
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+class Timer:
+    """HIP events on the current (launch) stream around each launch of the timed steps."""
+
+    def __init__(self, names):
+        self.names = names
+        self.ms = {n: 0.0 for n in names}
+        self.count = {n: 0 for n in names}
+        self.pending = []
+
+    def run(self, name, fn):
+        import torch
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pending.append((name, a, b))
+
+    def collect(self):
+        _sync()
+        for name, a, b in self.pending:
+            self.ms[name] += a.elapsed_time(b)
+            self.count[name] += 1
+        self.pending = []
+
+
+def bench_block(steps, warmup, seed):
+    import torch
+
+    import linear_layer_backward_bwd_amd as lb
+    import synth
+    dev = "cuda"
+    cases, opt = synth.block_case(seed=seed, device=dev)
+    outs = []
+    for c in cases:
+        c.W_master = None
+        outs.append((torch.empty(c.M, c.K, dtype=torch.bfloat16, device=dev),
+                     torch.empty(c.K, c.N, dtype=torch.float32, device=dev)))
+    torch.cuda.empty_cache()
+    names = [c.name for c in cases] + ["adamw"]
+    flops = {c.name: lin_bwd_flops(c.M, c.K, c.N) for c in cases}
+    n_params = opt.W.numel()
+
+    def step(timer=None):
+        for c, (dX, dW) in zip(cases, outs):
+            f = lambda c=c, dX=dX, dW=dW: lb.lin_bwd(c.X, c.W, c.G, dX, dW)
+            timer.run(c.name, f) if timer else f()
+        f = lambda: lb.adamw_step(opt.W, opt.g, opt.m, opt.v, opt.lr, opt.b1, opt.b2, opt.eps,
+                                  opt.wd, opt.steps[0], opt.inv_scale)
+        timer.run("adamw", f) if timer else f()
+
+    for _ in range(warmup):
+        step()
+    # exactly `steps` steps, bracketed by device synchronisation; HIP events on the
+    # launch stream around every launch give the per-kernel durations
+    timer = Timer(names)
+    _sync()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer)
+    _sync()
+    wall = time.perf_counter() - t0
+    timer.collect()
+
+    gemm_flops = sum(flops.values())
+    gemm_ms = sum(timer.ms[c.name] for c in cases) / steps
+    adamw_ms = timer.ms["adamw"] / steps
+    adamw_gbps = ADAMW_BYTES_16BIT_GRAD * n_params / (adamw_ms * 1e-3) / 1e9
+    per_proj = []
+    for c in cases:
+        ms = timer.ms[c.name] / steps
+        per_proj.append({"name": c.name, "M": c.M, "K": c.K, "N": c.N, "ms": round(ms, 4),
+                         "tflops": round(flops[c.name] / (ms * 1e-3) / 1e12, 1)})
+    ms_step = wall / steps * 1e3
+    result = {
+        "value": gemm_flops / (wall / steps) / 1e12,
+        "ms_per_step": ms_step,
+        "config": {"workload": "block_bwd_update_M16384_D4096",
+                   "tokens": synth.BLOCK_TOKENS,
+                   "projections": [[c.name, c.K, c.N] for c in cases],
+                   "params": n_params, "adamw_grad": "bf16 x1024", "adamw_step": opt.steps[0]},
+        "parts": {
+            "lin_bwd": {"ms": round(gemm_ms, 4), "tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
+                        "frac_of_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        "per_projection": per_proj},
+            "adamw": {"ms": round(adamw_ms, 4), "gbps": round(adamw_gbps, 1),
+                      "frac_of_peak": round(adamw_gbps / PEAK_HBM_GBPS, 4),
+                      "gparams_per_s": round(n_params / (adamw_ms * 1e-3) / 1e9, 2),
+                      "bytes_per_param": ADAMW_BYTES_16BIT_GRAD},
+        },
+        "roofline": {"bound": "mfma", "kernel": "k_lin_bwd_mfma",
+                     "achieved": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "per_launch_flops": gemm_flops / len(cases),
+                     "launch_ms": round(gemm_ms / len(cases), 4)},
+    }
+    return result, (cases, opt)
+
+
+def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
+    """lin_bwd alone at one shape; rotates over buffer sets larger than the 256 MB MALL."""
+    import torch
+
+    import linear_layer_backward_bwd_amd as lb
+    import synth
+    dev = "cuda"
+    one = 2 * (M * K + K * N + M * N) + 2 * M * K + 4 * K * N
+    nsets = max(1, min(16, -(-rotate_bytes // one)))
+    sets = []
+    for i in range(nsets):
+        c = synth.linear_case(M, K, N, "bf16", seed=seed + i, device=dev)
+        sets.append((c, torch.empty(M, K, dtype=torch.bfloat16, device=dev),
+                     torch.empty(K, N, dtype=torch.float32, device=dev)))
+    for i in range(warmup):
+        c, dX, dW = sets[i % nsets]
+        lb.lin_bwd(c.X, c.W, c.G, dX, dW)
+    timer = Timer(["lin_bwd"])
+    for i in range(steps):
+        c, dX, dW = sets[i % nsets]
+        timer.run("lin_bwd", lambda: lb.lin_bwd(c.X, c.W, c.G, dX, dW))
+    timer.collect()
+    ms = timer.ms["lin_bwd"] / steps
+    fl = lin_bwd_flops(M, K, N)
+    tf = fl / (ms * 1e-3) / 1e12
+    q = lin_bwd_min_bytes(M, K, N)
+    return {"M": M, "K": K, "N": N, "ms": round(ms, 5), "tflops": round(tf, 1),
+            "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "gbps_alg": round(q / (ms * 1e-3) / 1e9, 1),
+            "intensity_pages": round(ideal_intensity(M, K, N), 2),
+            "rotating_sets": nsets}
+
+
+def bench_adamw(n, steps, warmup, seed):
+    import torch
+
+    import linear_layer_backward_bwd_amd as lb
+    import synth
+    case = synth.adamw_2p28(seed=seed, n=n, device="cuda")
+    for i in range(warmup):
+        lb.adamw_step(case.W, case.g, case.m, case.v, case.lr, case.b1, case.b2, case.eps, case.wd,
+                      1 + i % 10, case.inv_scale)
+    timer = Timer(["adamw"])
+    for i in range(steps):
+        timer.run("adamw", lambda: lb.adamw_step(case.W, case.g, case.m, case.v, case.lr, case.b1,
+                                                 case.b2, case.eps, case.wd, 1 + i % 10, case.inv_scale))
+    timer.collect()
+    ms = timer.ms["adamw"] / steps
+    gbps = ADAMW_BYTES_16BIT_GRAD * n / (ms * 1e-3) / 1e9
+    return {"n": n, "grad": "f16", "ms": round(ms, 4), "gbps": round(gbps, 1),
+            "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+            "gparams_per_s": round(n / (ms * 1e-3) / 1e9, 2)}
+
+
+def cpu_baseline(cases, opt, target_s=12.0):
+    """The CPU oracle on a bounded sample of the block workload, extrapolated to one step."""
+    import numpy as np
+
+    import oracle
+    import synth
+    rng = np.random.default_rng(0)
+    host = [(c, synth.bits(c.X.cpu()), synth.bits(c.W.cpu()), synth.bits(c.G.cpu())) for c in cases]
+
+    # calibrate on a small sample, then size the sample to about target_s of work
+    def gemm_sample(count):
+        macs = 0
+        t0 = time.perf_counter()
+        for c, Xb, Wb, Gb in host:
+            r, k = rng.integers(0, c.M, count), rng.integers(0, c.K, count)
+            oracle.dx_at(Gb, Wb, "bf16", r, k)
+            k2, n2 = rng.integers(0, c.K, count), rng.integers(0, c.N, count)
+            oracle.dw_at(Xb, Gb, "bf16", k2, n2)
+            macs += count * c.N + count * c.M
+        return macs, time.perf_counter() - t0
+    macs, dt = gemm_sample(256)
+    count = int(256 * max(1.0, (0.8 * target_s) / max(dt, 1e-3)))
+    macs, dt = gemm_sample(count)
+    gemm_rate = 2.0 * macs / dt                        # FLOP/s on the host
+    n = 1 << 23
+    sl = slice(0, n)
+    W = opt.W[sl].cpu().numpy()
+    m = opt.m[sl].cpu().numpy()
+    v = opt.v[sl].cpu().numpy()
+    g = synth.bits(opt.g[sl].cpu())
+    t0 = time.perf_counter()
+    oracle.adamw(W, g, m, v, "bf16", opt.lr, opt.b1, opt.b2, opt.eps, opt.wd, opt.steps[0],
+                 opt.inv_scale)
+    adamw_rate = n / (time.perf_counter() - t0)        # params/s on the host
+    step_flops = sum(lin_bwd_flops(c.M, c.K, c.N) for c in cases)
+    step_s = step_flops / gemm_rate + opt.W.numel() / adamw_rate
+    return {"value": step_flops / step_s / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": ("%d dX + %d dW entries per projection (fp64 dot products on the bf16 inputs) "
+                       "and one AdamW step over 2^23 params (scalar fp32), extrapolated to the "
+                       "whole step; host GEMM %.2f GFLOP/s, host AdamW %.1f Mparam/s"
+                       % (count, count, gemm_rate / 1e9, adamw_rate / 1e6)),
+            "oracle_step_s_extrapolated": round(step_s, 1)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the M=32 / M=2048 / 2^28-param AdamW figures")
+    ap.add_argument("--only", choices=["block", "m32", "m2048", "adamw"], default=None,
+                    help="time one workload only (for profiling)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU; --gpus %d is not supported "
+              "(the multi-GPU sharding is a design note, not code)" % args.gpus, file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    import linear_layer_backward_bwd_amd as lb
+    lb.library()
+
+    if args.only in ("m32", "m2048"):
+        M = 32 if args.only == "m32" else 2048
+        print(json.dumps(bench_linear(M, 4096, 4096, args.steps, args.warmup, args.seed)), flush=True)
+        return 0
+    if args.only == "adamw":
+        print(json.dumps(bench_adamw(1 << 28, args.steps, args.warmup, args.seed)), flush=True)
+        return 0
+
+    print("bench: block workload, warmup %d, steps %d" % (args.warmup, args.steps),
+          file=sys.stderr, flush=True)
+    res, (cases, opt) = bench_block(args.steps, args.warmup, args.seed)
+    out = {"metric": METRIC, "value": round(res["value"], 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded normal draws on the GPU; random-init weights)",
+           "config": res["config"], "parts": res["parts"], "roofline": res["roofline"]}
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle on a bounded sample)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cases, opt)
+    del cases, opt
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        print("bench: extra shapes", file=sys.stderr, flush=True)
+        out["also"] = {
+            "lin_bwd_M32_K4096_N4096": bench_linear(32, 4096, 4096, 50, 5, args.seed),
+            "lin_bwd_M2048_K4096_N4096": bench_linear(2048, 4096, 4096, 50, 5, args.seed),
+            "adamw_2p28_f16": bench_adamw(1 << 28, 10, 2, args.seed),
+        }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,131 @@
+/*
+ * linbwd.h -- C ABI of liblinbwd.so: the backward-and-update step of a
+ * Linear layer on one AMD MI355X (gfx950).
+ *
+ * A Linear layer computes Y = X·W with X[M,K] (batch and sequence flattened
+ * into M rows), W[K,N].  Given the upstream gradient dY = dL/dY [M,N] the
+ * library computes the two backward products and then updates an fp32
+ * master copy of the weights with AdamW.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device,
+ *    owned by the caller; the library never allocates, frees or retains them.
+ *  - Matrices are row-major and contiguous (no leading-dimension arguments).
+ *  - Work is enqueued asynchronously on the stream set with lb_set_stream()
+ *    (per calling thread; the null stream by default).  No call synchronises.
+ *  - Argument errors are detected on the host before anything is enqueued or
+ *    written, and return a negative code; lb_last_error() then describes it.
+ *    A failed kernel launch returns LB_EHIP.  Faults during execution surface
+ *    at the caller's next synchronisation, as for any HIP kernel.
+ *  - Outputs must not alias inputs or each other.
+ *  - Calls enqueued on different streams that write the same memory race.
+ */
+#ifndef LINBWD_H
+#define LINBWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of X, W, dY and dX in lin_bwd() */
+#define LB_F32 0  /* IEEE binary32 */
+#define LB_BF16 1 /* bfloat16 (upper half of a binary32) */
+
+/* return codes */
+#define LB_OK 0
+#define LB_EINVAL (-1) /* bad size, null pointer or hyper-parameter */
+#define LB_EDTYPE (-2) /* unknown dtype code */
+#define LB_EHIP (-4)   /* the HIP runtime refused a launch or a query */
+
+/*
+ * lin_bwd -- the two backward products of a Linear layer:
+ *     dX = dY·Wᵀ     dX[m,k] = Σ_n dY[m,n]·W[k,n]     [M,K]
+ *     dW = Xᵀ·dY     dW[k,n] = Σ_m X[m,k]·dY[m,n]     [K,N]
+ * Pages: "GPU 优化实战 Part 2", section "反向传播——Linear 层的梯度" (each
+ * forward product becomes these two products in the backward pass);
+ * "GPU 如何训练模型：从算子到 Kernel", section "一个线性层，前向和反向到底在算
+ * 什么" (shapes X[M,K], W[K,N], G = dL/dY [M,N]; the input gradient is only
+ * needed when the layer below is trained; transposes through strides).
+ *
+ *   X   [M,K]  dtype        read only
+ *   W   [K,N]  dtype        read only
+ *   dY  [M,N]  dtype        read only
+ *   dX  [M,K]  dtype        written (overwritten, not accumulated); NULL skips dX
+ *   dW  [K,N]  fp32 always  written (overwritten, not accumulated); NULL skips dW
+ *   dtype      LB_BF16: bf16 operands, fp32 accumulation, dX rounded to bf16
+ *              (nearest even); LB_F32: fp32 operands and outputs.
+ *
+ * Sizes: 0 <= M, K, N < 2^31.  With M = 0 the sums are empty and dW is filled
+ * with zeros; with N = 0 dX is filled with zeros; K = 0 writes nothing.
+ * Any pointer alignment and any sizes are accepted; 16-byte aligned pointers
+ * with K and N multiples of 8 take the vectorised kernels.
+ * Errors: LB_EINVAL for a negative size, or a NULL operand that a requested
+ * output needs (X for dW; W for dX; dY for either); LB_EDTYPE for another
+ * dtype; LB_EHIP when a launch fails.  Both outputs NULL is a no-op (LB_OK).
+ */
+int lin_bwd(const void *X, const void *W, const void *dY, void *dX, float *dW,
+            int64_t M, int64_t K, int64_t N, int dtype);
+
+/*
+ * adamw_step -- one fused pass over n parameters that unscales the gradient
+ * and applies AdamW with decoupled weight decay to the fp32 master weights:
+ *     g  = float(grad[i]) · inv_scale
+ *     m  = b1·m + (1 − b1)·g
+ *     v  = b2·v + (1 − b2)·g·g
+ *     m̂ = m / (1 − b1^step)      v̂ = v / (1 − b2^step)
+ *     W  = W − lr·( m̂ / (√v̂ + eps) + wd·W )        (W on the right: before the step)
+ * Pages: "GPU 优化实战 Part 2", sections "AdamW 优化器——融合内核" (the fused
+ * per-parameter update with bias corrections) and "混合精度训练（FP16 / BF16）"
+ * (fp32 master weights; a loss-scaled gradient is multiplied by 1/scale
+ * before the update); "Mastering LLM Training with CUDA and ROCm", section
+ * "AdamW Algorithm" (the same update as θ − η·m̂/(√v̂+ε) − η·λ·θ).
+ *
+ *   W, m, v  [n] fp32   read and written once each, in place
+ *   grad     [n]        read only (not zeroed); fp32 for adamw_step, IEEE
+ *                       binary16 bit patterns for adamw_step_f16, bfloat16
+ *                       bit patterns for adamw_step_bf16
+ *   step     the 1-based step number t; the bias corrections 1 − b^t are
+ *            computed once per call on the host in double and rounded to float
+ *   inv_scale  1 / loss scale (1 for an unscaled gradient)
+ *
+ * The fp32 arithmetic is done in the order written above, without fused
+ * multiply-add contraction, with IEEE division and square root.
+ * n = 0 is a no-op.  Any alignment is accepted; 16-byte aligned buffers take
+ * the vectorised path.  NaN and infinity propagate (no skip, no detection).
+ * Errors: LB_EINVAL for n < 0, a NULL buffer with n > 0, step < 1, or b1 / b2
+ * outside [0, 1); LB_EHIP when the launch fails.
+ */
+int adamw_step(float *W, const float *grad, float *m, float *v, int64_t n,
+               float lr, float b1, float b2, float eps, float wd, int step,
+               float inv_scale);
+int adamw_step_f16(float *W, const uint16_t *grad, float *m, float *v, int64_t n,
+                   float lr, float b1, float b2, float eps, float wd, int step,
+                   float inv_scale);
+int adamw_step_bf16(float *W, const uint16_t *grad, float *m, float *v, int64_t n,
+                    float lr, float b1, float b2, float eps, float wd, int step,
+                    float inv_scale);
+
+/*
+ * lb_set_stream -- the HIP stream (a hipStream_t, passed as void*) on which
+ * the calling thread's later calls enqueue their kernels; NULL selects the
+ * null stream.  The setting is per thread.  Returns LB_OK.
+ */
+int lb_set_stream(void *hip_stream);
+
+/*
+ * lb_last_error -- a description of the calling thread's last non-zero
+ * return, or "" if there was none.  The string is owned by the library and
+ * valid until the thread's next call.
+ */
+const char *lb_last_error(void);
+
+/* lb_version -- the library's version string (static storage). */
+const char *lb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINBWD_H */

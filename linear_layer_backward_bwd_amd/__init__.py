@@ -1,0 +1,165 @@
+"""Linear-layer backward (dX = dY·Wᵀ, dW = Xᵀ·dY) and fused unscale + AdamW on MI355X.
+
+A thin binding over the C ABI of ``liblinbwd.so`` (declared in
+``include/linbwd.h``): it checks and marshals torch tensors into device
+pointers and sizes, selects torch's current HIP stream, and raises
+``RuntimeError`` with the library's message when a call fails.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["lin_bwd", "adamw_step", "adamw_step_f16", "adamw_step_bf16", "lb_set_stream",
+           "lb_last_error", "lb_version", "library", "LIB_PATH", "LB_F32", "LB_BF16"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinbwd.so")
+LB_F32, LB_BF16 = 0, 1
+LB_OK, LB_EINVAL, LB_EDTYPE, LB_EHIP = 0, -1, -2, -4
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load liblinbwd.so (built in-tree by ``python -m linear_layer_backward_bwd_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("%s is not built: run `python -m linear_layer_backward_bwd_amd.build` "
+                           "(the HIP library is required; there is no fallback)" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.lin_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32]
+    lib.lin_bwd.restype = i32
+    for name in ("adamw_step", "adamw_step_f16", "adamw_step_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, i64, f32, f32, f32, f32, f32, i32, f32]
+        fn.restype = i32
+    lib.lb_set_stream.argtypes = [vp]
+    lib.lb_set_stream.restype = i32
+    lib.lb_last_error.argtypes = []
+    lib.lb_last_error.restype = ctypes.c_char_p
+    lib.lb_version.argtypes = []
+    lib.lb_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def lb_last_error() -> str:
+    return library().lb_last_error().decode()
+
+
+def lb_version() -> str:
+    return library().lb_version().decode()
+
+
+def lb_set_stream(stream) -> None:
+    """Select the HIP stream (a torch.cuda.Stream, a raw handle int, or None)."""
+    handle = getattr(stream, "cuda_stream", stream)
+    library().lb_set_stream(ctypes.c_void_p(handle or 0))
+
+
+def _check(rc: int, name: str) -> None:
+    if rc != LB_OK:
+        raise RuntimeError("%s failed (code %d): %s" % (name, rc, lb_last_error()))
+
+
+def _ptr(t):
+    return None if t is None else (t.data_ptr() or None)
+
+
+def _device_of(tensors):
+    import torch
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError("all tensors must be on one device, got %s" % devs)
+    dev = devs.pop()
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU (torch 'cuda' device), got %s" % dev)
+    for t in tensors:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return dev
+
+
+def _use_current_stream(dev) -> None:
+    import torch
+    library().lb_set_stream(ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+
+
+def lin_bwd(X, W, dY, dX=None, dW=None) -> None:
+    """dX = dY·Wᵀ (into dX, dtype of the operands) and dW = Xᵀ·dY (into dW, float32).
+
+    X [M,K], W [K,N], dY [M,N]: all bfloat16 or all float32, contiguous, on one GPU.
+    Either output may be None to skip it; outputs are overwritten.
+    """
+    import torch
+    ops = [t for t in (X, W, dY) if t is not None]
+    if not ops:
+        raise ValueError("lin_bwd needs operands")
+    dtype = ops[0].dtype
+    if dtype not in (torch.bfloat16, torch.float32) or any(t.dtype != dtype for t in ops):
+        raise TypeError("X, W, dY must all be bfloat16 or all float32")
+    if X is None or W is None or dY is None:
+        raise ValueError("X, W and dY are required")
+    if X.dim() != 2 or W.dim() != 2 or dY.dim() != 2:
+        raise ValueError("X, W, dY must be 2-D (flatten batch and sequence into M)")
+    M, K = X.shape
+    N = W.shape[1]
+    if W.shape[0] != K or tuple(dY.shape) != (M, N):
+        raise ValueError("shape mismatch: X%s W%s dY%s" % (tuple(X.shape), tuple(W.shape),
+                                                           tuple(dY.shape)))
+    if dX is not None and (dX.dtype != dtype or tuple(dX.shape) != (M, K)):
+        raise ValueError("dX must be %s of shape (%d, %d)" % (dtype, M, K))
+    if dW is not None and (dW.dtype != torch.float32 or tuple(dW.shape) != (K, N)):
+        raise ValueError("dW must be float32 of shape (%d, %d)" % (K, N))
+    dev = _device_of([X, W, dY, dX, dW])
+    _use_current_stream(dev)
+    rc = library().lin_bwd(_ptr(X), _ptr(W), _ptr(dY), _ptr(dX), _ptr(dW), M, K, N,
+                           LB_BF16 if dtype == torch.bfloat16 else LB_F32)
+    _check(rc, "lin_bwd")
+
+
+def _adamw(name, W, grad, m, v, lr, b1, b2, eps, wd, step, inv_scale):
+    import torch
+    for t, nm in ((W, "W"), (m, "m"), (v, "v")):
+        if t.dtype != torch.float32:
+            raise TypeError("%s must be float32" % nm)
+    n = W.numel()
+    if m.numel() != n or v.numel() != n or grad.numel() != n:
+        raise ValueError("W, grad, m, v must have the same number of elements")
+    dev = _device_of([W, grad, m, v])
+    _use_current_stream(dev)
+    rc = getattr(library(), name)(_ptr(W), _ptr(grad), _ptr(m), _ptr(v), n, lr, b1, b2, eps, wd,
+                                  int(step), inv_scale)
+    _check(rc, name)
+
+
+def adamw_step(W, grad, m, v, lr, b1, b2, eps, wd, step, inv_scale=1.0) -> None:
+    """One fused unscale + AdamW step in place on W, m, v (float32); grad is read only.
+
+    The C entry point is chosen by grad's dtype: float32 -> adamw_step,
+    float16 -> adamw_step_f16, bfloat16 -> adamw_step_bf16.
+    """
+    import torch
+    name = {torch.float32: "adamw_step", torch.float16: "adamw_step_f16",
+            torch.bfloat16: "adamw_step_bf16"}.get(grad.dtype)
+    if name is None:
+        raise TypeError("grad must be float32, float16 or bfloat16")
+    _adamw(name, W, grad, m, v, lr, b1, b2, eps, wd, step, inv_scale)
+
+
+def adamw_step_f16(W, grad, m, v, lr, b1, b2, eps, wd, step, inv_scale=1.0) -> None:
+    import torch
+    if grad.dtype != torch.float16:
+        raise TypeError("grad must be float16")
+    _adamw("adamw_step_f16", W, grad, m, v, lr, b1, b2, eps, wd, step, inv_scale)
+
+
+def adamw_step_bf16(W, grad, m, v, lr, b1, b2, eps, wd, step, inv_scale=1.0) -> None:
+    import torch
+    if grad.dtype != torch.bfloat16:
+        raise TypeError("grad must be bfloat16")
+    _adamw("adamw_step_bf16", W, grad, m, v, lr, b1, b2, eps, wd, step, inv_scale)

@@ -1,0 +1,132 @@
+// C ABI of liblinbwd: argument validation, stream selection, error strings.
+// The declarations and their contracts are in include/linbwd.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/linbwd.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local hipStream_t tl_stream = nullptr;
+thread_local std::string tl_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    tl_error = buf;
+    return code;
+}
+
+int hip_fail(const char *what, hipError_t e) {
+    return fail(LB_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; } // false for NaN
+
+template <lb::GradType GT>
+int adamw_impl(const char *name, float *W, const void *g, float *m, float *v, int64_t n, float lr,
+               float b1, float b2, float eps, float wd, int step, float inv_scale) {
+    tl_error.clear();
+    if (n < 0)
+        return fail(LB_EINVAL, "%s: n = %lld is negative", name, (long long)n);
+    if (step < 1)
+        return fail(LB_EINVAL, "%s: step = %d; steps are numbered from 1", name, step);
+    if (!beta_ok(b1) || !beta_ok(b2))
+        return fail(LB_EINVAL, "%s: b1 = %g, b2 = %g must lie in [0, 1)", name, (double)b1, (double)b2);
+    if (n == 0)
+        return LB_OK;
+    if (!W || !g || !m || !v)
+        return fail(LB_EINVAL, "%s: NULL buffer with n = %lld", name, (long long)n);
+    lb::AdamWArgs a;
+    a.W = W;
+    a.g = g;
+    a.m = m;
+    a.v = v;
+    a.n = n;
+    a.lr = lr;
+    a.b1 = b1;
+    a.b2 = b2;
+    a.eps = eps;
+    a.wd = wd;
+    a.one_minus_b1 = 1.0f - b1;
+    a.one_minus_b2 = 1.0f - b2;
+    a.bc1 = (float)(1.0 - std::pow((double)b1, (double)step));
+    a.bc2 = (float)(1.0 - std::pow((double)b2, (double)step));
+    a.inv_scale = inv_scale;
+    hipError_t e = lb::launch_adamw(a, GT, tl_stream);
+    if (e != hipSuccess)
+        return hip_fail(name, e);
+    return LB_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int lin_bwd(const void *X, const void *W, const void *dY, void *dX, float *dW, int64_t M, int64_t K,
+            int64_t N, int dtype) {
+    tl_error.clear();
+    if (dtype != LB_F32 && dtype != LB_BF16)
+        return fail(LB_EDTYPE, "lin_bwd: dtype %d is not LB_F32 (0) or LB_BF16 (1)", dtype);
+    if (M < 0 || K < 0 || N < 0)
+        return fail(LB_EINVAL, "lin_bwd: negative size M=%lld K=%lld N=%lld", (long long)M,
+                    (long long)K, (long long)N);
+    const int64_t lim = (int64_t)1 << 31;
+    if (M >= lim || K >= lim || N >= lim)
+        return fail(LB_EINVAL, "lin_bwd: sizes must be below 2^31 (M=%lld K=%lld N=%lld)",
+                    (long long)M, (long long)K, (long long)N);
+    // dX has M*K entries and sums over N; dW has K*N entries and sums over M.
+    if (dX && M > 0 && K > 0 && N > 0 && (!dY || !W))
+        return fail(LB_EINVAL, "lin_bwd: dX requested but dY or W is NULL");
+    if (dW && K > 0 && N > 0 && M > 0 && (!X || !dY))
+        return fail(LB_EINVAL, "lin_bwd: dW requested but X or dY is NULL");
+    lb::LinBwdArgs a;
+    a.X = X;
+    a.W = W;
+    a.dY = dY;
+    a.dX = dX;
+    a.dW = dW;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.bf16 = dtype == LB_BF16;
+    hipError_t e = lb::launch_lin_bwd(a, tl_stream);
+    if (e != hipSuccess)
+        return hip_fail("lin_bwd", e);
+    return LB_OK;
+}
+
+int adamw_step(float *W, const float *grad, float *m, float *v, int64_t n, float lr, float b1, float b2,
+               float eps, float wd, int step, float inv_scale) {
+    return adamw_impl<lb::GRAD_F32>("adamw_step", W, grad, m, v, n, lr, b1, b2, eps, wd, step,
+                                    inv_scale);
+}
+
+int adamw_step_f16(float *W, const uint16_t *grad, float *m, float *v, int64_t n, float lr, float b1,
+                   float b2, float eps, float wd, int step, float inv_scale) {
+    return adamw_impl<lb::GRAD_F16>("adamw_step_f16", W, grad, m, v, n, lr, b1, b2, eps, wd, step,
+                                    inv_scale);
+}
+
+int adamw_step_bf16(float *W, const uint16_t *grad, float *m, float *v, int64_t n, float lr, float b1,
+                    float b2, float eps, float wd, int step, float inv_scale) {
+    return adamw_impl<lb::GRAD_BF16>("adamw_step_bf16", W, grad, m, v, n, lr, b1, b2, eps, wd, step,
+                                     inv_scale);
+}
+
+int lb_set_stream(void *hip_stream) {
+    tl_stream = static_cast<hipStream_t>(hip_stream);
+    return LB_OK;
+}
+
+const char *lb_last_error(void) { return tl_error.c_str(); }
+
+const char *lb_version(void) { return "linbwd 0.1.0 gfx950"; }
+
+} // extern "C"

@@ -1,0 +1,38 @@
+// Host-side launchers shared between the kernel files and the C ABI (api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lb {
+
+// ---- fused unscale + AdamW ---------------------------------------------
+enum GradType { GRAD_F32 = 0, GRAD_F16 = 1, GRAD_BF16 = 2 };
+
+struct AdamWArgs {
+    float *W;
+    const void *g;
+    float *m;
+    float *v;
+    int64_t n;
+    float lr, b1, b2, eps, wd;
+    float one_minus_b1, one_minus_b2; // 1 - b, rounded to float
+    float bc1, bc2;                   // 1 - b^t, computed in double, rounded once
+    float inv_scale;
+};
+
+hipError_t launch_adamw(const AdamWArgs &a, GradType gt, hipStream_t s);
+
+// ---- Linear backward ----------------------------------------------------
+struct LinBwdArgs {
+    const void *X, *W, *dY;
+    void *dX;  // may be null (skip)
+    float *dW; // may be null (skip)
+    int64_t M, K, N;
+    bool bf16; // operands bf16 (else fp32)
+};
+
+// Chooses kernels by dtype, alignment and M; enqueues 1-2 launches.
+hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s);
+
+} // namespace lb

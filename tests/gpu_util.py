@@ -1,0 +1,87 @@
+"""Helpers for the GPU parity tests: guarded output buffers, metrics, sampling.
+
+Outputs are carved out of a larger buffer whose guard bands hold a canary
+pattern and whose interior is poisoned with NaN, so a kernel that writes out
+of bounds, or leaves an entry unwritten, fails the comparison.
+"""
+import numpy as np
+import torch
+
+GUARD = 64  # elements on each side (128 or 256 bytes: keeps 16-byte alignment)
+
+#: tolerances (written here, used by every parity test)
+DX_RELF = 4e-3        # bf16 dX vs fp64: relative Frobenius error
+DW_RELF = 1e-5        # fp32 dW vs fp64
+F32_OUT_RELF = 1e-5   # fp32 dX (fp32 operands) vs fp64
+ADAMW_ABS = 2e-6      # |gpu - oracle| <= ADAMW_ABS * max(1, |oracle|) for W, m, v
+
+
+class Guarded:
+    """A (rows, cols) tensor inside a canary-banded 1-D buffer."""
+
+    def __init__(self, rows, cols, dtype, device="cuda", offset=0):
+        n = rows * cols
+        self.dtype = dtype
+        self.n = n
+        self.lo = GUARD + offset
+        self.buf = torch.empty(n + 2 * GUARD + offset, dtype=dtype, device=device)
+        self.buf.fill_(-12345.0 if dtype == torch.float32 else -123.0)
+        self.canary = self.buf[0].item()
+        self.t = self.buf[self.lo:self.lo + n].view(rows, cols)
+        self.t.fill_(float("nan"))
+
+    def check_guards(self):
+        host = self.buf.cpu()
+        assert bool((host[:self.lo] == self.canary).all()), "write before the output buffer"
+        assert bool((host[self.lo + self.n:] == self.canary).all()), "write past the output buffer"
+
+
+def relf(a, ref):
+    a = np.asarray(a, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = float(np.linalg.norm(ref))
+    num = float(np.linalg.norm(a - ref))
+    if den == 0.0:
+        return num if num > 1e-30 else 0.0
+    return num / den
+
+
+def host_f64(t):
+    return t.detach().to("cpu", torch.float64).numpy() if t.dtype != torch.bfloat16 \
+        else t.detach().to("cpu").float().double().numpy()
+
+
+def bits(t):
+    """Raw host element view (float32, or 16-bit patterns as uint16) of any tensor."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.float32:
+        return t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def ulp_distance_f32(a, b):
+    """Elementwise distance in units in the last place between two float32 arrays."""
+    ai = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    bi = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    ai = np.where(ai < 0, np.int64(-2 ** 31) - ai, ai)
+    bi = np.where(bi < 0, np.int64(-2 ** 31) - bi, bi)
+    return np.abs(ai - bi)
+
+
+def adamw_ok(gpu, ref):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    both_nan = np.isnan(gpu) & np.isnan(ref)
+    err = np.abs(gpu - ref)
+    ok = (err <= ADAMW_ABS * np.maximum(1.0, np.abs(ref))) | both_nan
+    return bool(ok.all()), float(np.nanmax(err / np.maximum(1.0, np.abs(ref)))) if err.size else 0.0
+
+
+def sample_positions(rows, cols, count, seed):
+    """Random (row, col) pairs plus the four corners and the last row/col edges."""
+    rng = np.random.default_rng(seed)
+    r = rng.integers(0, rows, count)
+    c = rng.integers(0, cols, count)
+    edge_r = np.array([0, 0, rows - 1, rows - 1] + [rows - 1] * 16 + list(rng.integers(0, rows, 16)))
+    edge_c = np.array([0, cols - 1, 0, cols - 1] + list(rng.integers(0, cols, 16)) + [cols - 1] * 16)
+    return np.concatenate([r, edge_r]), np.concatenate([c, edge_c])

@@ -1,0 +1,110 @@
+"""The C-ABI library loads, exports every symbol include/linbwd.h declares, and
+rejects bad arguments on the host before anything is launched (CPU only: no
+call here reaches the GPU).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_layer_backward_bwd_amd as lb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linbwd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("lin_bwd", "adamw_step", "adamw_step_f16", "adamw_step_bf16",
+                 "lb_set_stream", "lb_last_error", "lb_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = lb.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", lb.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in lb.lb_version()
+    lib = lb.library()
+    assert lib.lb_set_stream(None) == 0
+    assert lb.lb_last_error() == ""
+
+
+def test_header_compiles_as_c():
+    src = '#include "linbwd.h"\nint main(void){return LB_OK + LB_BF16 - 1;}\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        "-x", "c", "-", "-o", "/dev/null", "-c"], input=src, text=True,
+                       capture_output=True)
+    assert r.returncode == 0, r.stderr
+
+
+NULL = None
+
+
+@pytest.mark.parametrize("args,code", [
+    ((NULL, NULL, NULL, NULL, NULL, -1, 4, 4, 1), -1),         # negative M
+    ((NULL, NULL, NULL, NULL, NULL, 4, -1, 4, 1), -1),         # negative K
+    ((NULL, NULL, NULL, NULL, NULL, 4, 4, -5, 0), -1),         # negative N
+    ((NULL, NULL, NULL, NULL, NULL, 4, 4, 4, 2), -2),          # unknown dtype
+    ((NULL, NULL, NULL, NULL, NULL, 1 << 31, 4, 4, 1), -1),    # too large
+    ((NULL, NULL, NULL, 16, NULL, 4, 4, 4, 1), -1),            # dX wanted, W/dY NULL
+    ((NULL, NULL, NULL, NULL, 16, 4, 4, 4, 1), -1),            # dW wanted, X/dY NULL
+])
+def test_lin_bwd_rejects_on_host(args, code):
+    lib = lb.library()
+    assert lib.lin_bwd(*args) == code
+    assert lb.lb_last_error() != ""
+
+
+def test_lin_bwd_noop_cases_need_no_gpu():
+    lib = lb.library()
+    assert lib.lin_bwd(NULL, NULL, NULL, NULL, NULL, 8, 8, 8, 1) == 0      # nothing requested
+    assert lib.lin_bwd(NULL, NULL, NULL, 16, 16, 8, 0, 8, 1) == 0          # K = 0: nothing to write
+    assert lb.lb_last_error() == ""
+
+
+@pytest.mark.parametrize("name", ["adamw_step", "adamw_step_f16", "adamw_step_bf16"])
+@pytest.mark.parametrize("over,code", [
+    (dict(n=-1), -1), (dict(step=0), -1), (dict(step=-3), -1), (dict(b1=1.0), -1),
+    (dict(b2=1.0), -1), (dict(b1=-0.5), -1), (dict(b2=float("nan")), -1),
+    (dict(n=10), -1),                                              # NULL buffers with n > 0
+    (dict(n=0), 0),                                                # empty: no-op
+])
+def test_adamw_rejects_on_host(name, over, code):
+    a = dict(n=0, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.01, step=1, inv_scale=1.0)
+    a.update(over)
+    fn = getattr(lb.library(), name)
+    rc = fn(NULL, NULL, NULL, NULL, a["n"], a["lr"], a["b1"], a["b2"], a["eps"], a["wd"],
+            a["step"], a["inv_scale"])
+    assert rc == code
+    assert (lb.lb_last_error() != "") == (code != 0)
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 4, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        lb.lin_bwd(x, x, x, torch.zeros_like(x), torch.zeros(4, 4))
+    with pytest.raises(TypeError):
+        lb.lin_bwd(x, x.float(), x)
+    with pytest.raises(ValueError):
+        lb.lin_bwd(x, torch.zeros(5, 4, dtype=torch.bfloat16), x)
+    w = torch.zeros(8)
+    with pytest.raises(TypeError):
+        lb.adamw_step(w, w.to(torch.int32), w, w, 1e-3, 0.9, 0.99, 1e-8, 0.0, 1)

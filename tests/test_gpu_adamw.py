@@ -1,0 +1,151 @@
+"""GPU parity of the fused unscale + AdamW entry points against the CPU oracle.
+
+Bar (written in gpu_util): |gpu - oracle| <= 2e-6·max(1, |oracle|) for each of
+W, m, v.  Both sides evaluate the same fp32 operation sequence with IEEE
+division and square root and no contraction, so the distance in ulps is
+reported and held to 16.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_layer_backward_bwd_amd as lb
+import oracle
+import synth
+from gpu_util import adamw_ok, bits, ulp_distance_f32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def gpu_steps(case, steps, offset=0):
+    """Run the steps on the GPU; returns host copies of W, m, v."""
+    def place(t):
+        if offset == 0:
+            return t.to(DEV).clone()
+        buf = torch.empty(t.numel() + offset, dtype=t.dtype, device=DEV)
+        view = buf[offset:]
+        view.copy_(t.to(DEV))
+        return view
+    W, m, v, g = (place(t) for t in (case.W, case.m, case.v, case.g))
+    for t in steps:
+        lb.adamw_step(W, g, m, v, case.lr, case.b1, case.b2, case.eps, case.wd, t, case.inv_scale)
+    torch.cuda.synchronize()
+    return W.cpu().numpy(), m.cpu().numpy(), v.cpu().numpy()
+
+
+def oracle_steps(case, steps, idx=None):
+    W, m, v, g = case.W.numpy(), case.m.numpy(), case.v.numpy(), synth.bits(case.g)
+    if idx is not None:
+        W, m, v, g = W[idx], m[idx], v[idx], g[idx]
+    for t in steps:
+        W, m, v = oracle.adamw(W, g, m, v, case.gdtype, case.lr, case.b1, case.b2, case.eps,
+                               case.wd, t, case.inv_scale)
+    return W, m, v
+
+
+def compare(got, ref):
+    worst_ulp = 0
+    for name, a, b in zip("Wmv", got, ref):
+        ok, err = adamw_ok(a, b)
+        assert ok, "%s: max scaled error %.3g" % (name, err)
+        keep = ~(np.isnan(a) & np.isnan(b))   # NaN payloads differ between CPU and GPU
+        if keep.any():
+            worst_ulp = max(worst_ulp, int(ulp_distance_f32(a[keep], b[keep]).max()))
+    assert worst_ulp <= 16, "max ulp distance %d" % worst_ulp
+    return worst_ulp
+
+
+@pytest.mark.parametrize("gdtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("n", [1, 7, 8, 4096 + 5, 1000003])
+def test_grad_types_and_ragged_sizes(gdtype, n):
+    g_scale = 1.0 if gdtype == "f32" else 1024.0
+    case = synth.adamw_case(n, gdtype, g_scale=g_scale, seed=n % 97)
+    steps = [1, 2, 3]
+    compare(gpu_steps(case, steps), oracle_steps(case, steps))
+
+
+@pytest.mark.parametrize("gdtype", ["f32", "f16"])
+def test_misaligned_buffers(gdtype):
+    case = synth.adamw_case(100003, gdtype, g_scale=1.0 if gdtype == "f32" else 1024.0, seed=3)
+    compare(gpu_steps(case, [1, 2], offset=1), oracle_steps(case, [1, 2]))
+
+
+def test_zero_moments_step1():
+    case = synth.adamw_case(65536, "bf16", seed=4, zero_moments=True, lr=1e-3, b2=0.999, wd=0.01)
+    compare(gpu_steps(case, [1]), oracle_steps(case, [1]))
+
+
+def test_lr_zero_keeps_W_and_grad_untouched():
+    case = synth.adamw_case(50000, "f16", seed=5, lr=0.0)
+    g_dev = case.g.to(DEV)
+    W = case.W.to(DEV).clone()
+    m, v = case.m.to(DEV).clone(), case.v.to(DEV).clone()
+    lb.adamw_step(W, g_dev, m, v, 0.0, case.b1, case.b2, case.eps, case.wd, 4, case.inv_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(W.cpu(), case.W)
+    assert torch.equal(g_dev.cpu(), case.g)
+
+
+def test_nan_and_inf_propagate():
+    case = synth.adamw_case(64, "f32", g_scale=1.0, seed=6)
+    case.g[3] = float("nan")
+    case.g[5] = float("inf")
+    got = gpu_steps(case, [1])
+    ref = oracle_steps(case, [1])
+    compare(got, ref)
+    assert np.isnan(got[0][3]) and np.isnan(ref[0][3])
+
+
+def test_explicit_typed_entry_points():
+    case = synth.adamw_case(4099, "f16", seed=7)
+    W, m, v, g = (t.to(DEV).clone() for t in (case.W, case.m, case.v, case.g))
+    lb.adamw_step_f16(W, g, m, v, case.lr, case.b1, case.b2, case.eps, case.wd, 1, case.inv_scale)
+    torch.cuda.synchronize()
+    compare((W.cpu().numpy(), m.cpu().numpy(), v.cpu().numpy()), oracle_steps(case, [1]))
+    with pytest.raises(TypeError):
+        lb.adamw_step_bf16(W, g, m, v, 1e-3, 0.9, 0.95, 1e-8, 0.0, 1)
+
+
+def test_adamw_2p28_ten_steps_sampled():
+    """2^28 fp32 params, fp16 grads x1024, t = 1..10; oracle on a 2^20 sample + both ends."""
+    n = 1 << 28
+    case = synth.adamw_2p28(seed=0, n=n, device=DEV)
+    host = synth.AdamWCase(case.W.cpu(), case.m.cpu(), case.v.cpu(), case.g.cpu(), case.gdtype,
+                           case.lr, case.b1, case.b2, case.eps, case.wd, case.inv_scale, case.steps)
+    W, m, v, g = case.W, case.m, case.v, case.g
+    for t in case.steps:
+        lb.adamw_step(W, g, m, v, case.lr, case.b1, case.b2, case.eps, case.wd, t, case.inv_scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 1 << 20), np.arange(1000),
+                                    np.arange(n - 1000, n)]))
+    tidx = torch.from_numpy(idx).to(DEV)
+    got = tuple(t[tidx].cpu().numpy() for t in (W, m, v))
+    compare(got, oracle_steps(host, case.steps, idx))
+
+
+def test_block_optimizer_sampled():
+    """The block's 201,326,592 params, bf16 grads x1024, step 100, sampled."""
+    cases, opt = synth.block_case(seed=0, device=DEV)
+    del cases
+    n = opt.W.numel()
+    host = synth.AdamWCase(opt.W.cpu(), opt.m.cpu(), opt.v.cpu(), opt.g.cpu(), opt.gdtype,
+                           opt.lr, opt.b1, opt.b2, opt.eps, opt.wd, opt.inv_scale, opt.steps)
+    for t in opt.steps:
+        lb.adamw_step(opt.W, opt.g, opt.m, opt.v, opt.lr, opt.b1, opt.b2, opt.eps, opt.wd, t,
+                      opt.inv_scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 1 << 20), np.arange(n - 100, n)]))
+    tidx = torch.from_numpy(idx).to(DEV)
+    got = tuple(t[tidx].cpu().numpy() for t in (opt.W, opt.m, opt.v))
+    compare(got, oracle_steps(host, opt.steps, idx))
+
+
+def test_run_twice_is_bitwise():
+    case = synth.adamw_case(300001, "bf16", seed=8)
+    a = gpu_steps(case, [1, 2])
+    b = gpu_steps(case, [1, 2])
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)

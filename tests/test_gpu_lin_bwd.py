@@ -1,0 +1,210 @@
+"""GPU parity of lin_bwd (dX = dY·Wᵀ, dW = Xᵀ·dY) against the CPU oracle.
+
+Every call goes through the C ABI of liblinbwd.so.  Bars (written in
+gpu_util): bf16 dX relative Frobenius error <= 4e-3, fp32 dW <= 1e-5, fp32
+dX (fp32 operands) <= 1e-5; integer-valued and identity cases bitwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_layer_backward_bwd_amd as lb
+import oracle
+import synth
+from gpu_util import (DW_RELF, DX_RELF, F32_OUT_RELF, Guarded, bits, host_f64, relf,
+                      sample_positions)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def run(case, need_dx=True, need_dw=True, stream=None, offset=0):
+    X, W, G = (t.to(DEV) for t in (case.X, case.W, case.G))
+    gx = Guarded(case.M, case.K, TDT[case.dtype], offset=offset) if need_dx else None
+    gw = Guarded(case.K, case.N, torch.float32, offset=offset) if need_dw else None
+    if stream is not None:
+        with torch.cuda.stream(stream):
+            lb.lin_bwd(X, W, G, gx.t if gx else None, gw.t if gw else None)
+    else:
+        lb.lin_bwd(X, W, G, gx.t if gx else None, gw.t if gw else None)
+    torch.cuda.synchronize()
+    for g in (gx, gw):
+        if g is not None:
+            g.check_guards()
+    return (gx.t if gx else None), (gw.t if gw else None)
+
+
+def check_full(case, dX, dW):
+    rX, rW = oracle.lin_bwd(synth.bits(case.X), synth.bits(case.W), synth.bits(case.G), case.dtype,
+                            need_dx=dX is not None, need_dw=dW is not None)
+    if dX is not None:
+        hx = host_f64(dX)
+        assert not np.isnan(hx).any(), "dX has unwritten (NaN) entries"
+        bar = DX_RELF if case.dtype == "bf16" else F32_OUT_RELF
+        e = relf(hx, rX)
+        assert e <= bar, "dX relF %.3g > %.3g" % (e, bar)
+    if dW is not None:
+        hw = host_f64(dW)
+        assert not np.isnan(hw).any(), "dW has unwritten (NaN) entries"
+        e = relf(hw, rW)
+        assert e <= DW_RELF, "dW relF %.3g > %.3g" % (e, DW_RELF)
+    return rX, rW
+
+
+SHAPES = [
+    # (M, K, N): MFMA tiles with ragged edges and a partial reduction slab
+    (300, 520, 264), (257, 264, 520), (96, 64, 4104), (200, 256, 256), (512, 512, 512),
+    (65, 128, 384),
+    # small-M dX path (M <= 64), with the MFMA dW path
+    (64, 384, 520), (32, 1024, 1032), (17, 40, 8), (1, 264, 72), (48, 8, 1000),
+    # sizes not multiples of 8: SIMT path
+    (33, 100, 70), (5, 7, 3), (70, 9, 130),
+]
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_bf16_shapes_match_oracle(M, K, N):
+    case = synth.linear_case(M, K, N, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=M + K + N)
+    dX, dW = run(case)
+    check_full(case, dX, dW)
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 64, 64), (33, 100, 70), (130, 264, 96)])
+def test_f32_shapes_match_oracle(M, K, N):
+    case = synth.linear_case(M, K, N, "f32", x_std=1.0, w_std=1.0, g_std=1.0, seed=7)
+    dX, dW = run(case)
+    check_full(case, dX, dW)
+
+
+def test_tiny_f32_workload_then_adamw():
+    """64x64x64 fp32 backward, then one AdamW step on W with g = dW (GPU chain vs oracle chain)."""
+    case, hp = synth.tiny_f32(seed=0)
+    dX, dW = run(case)
+    rX, rW = check_full(case, dX, dW)
+    W = case.W.to(DEV).clone()
+    m = torch.zeros_like(W)
+    v = torch.zeros_like(W)
+    lb.adamw_step(W, dW.contiguous(), m, v, hp["lr"], hp["b1"], hp["b2"], hp["eps"], hp["wd"],
+                  hp["step"], hp["inv_scale"])
+    torch.cuda.synchronize()
+    z = np.zeros((64, 64), np.float32)
+    oW, om, ov = oracle.adamw(synth.bits(case.W), rW.astype(np.float32), z, z, "f32", hp["lr"],
+                              hp["b1"], hp["b2"], hp["eps"], hp["wd"], hp["step"], hp["inv_scale"])
+    from gpu_util import adamw_ok
+    for got, ref in ((W, oW), (m, om), (v, ov)):
+        ok, err = adamw_ok(got.cpu().numpy(), ref)
+        assert ok, err
+
+
+def test_skip_outputs_and_empty_sums():
+    case = synth.linear_case(100, 72, 80, "bf16", seed=3)
+    dX, dW = run(case, need_dx=False)
+    assert dX is None
+    check_full(case, None, dW)
+    dX, dW = run(case, need_dw=False)
+    check_full(case, dX, None)
+    # M = 0: dW is the empty sum, zeros
+    e = synth.linear_case(0, 72, 80, "bf16", seed=4)
+    _, dW = run(e, need_dx=False)
+    assert bool((dW == 0).all())
+    # N = 0: dX is zeros
+    e = synth.linear_case(40, 72, 0, "bf16", seed=5)
+    dX, _ = run(e, need_dw=False)
+    assert bool((dX == 0).all())
+    # small-M shape with N = 0, and fp32 with M = 0
+    e = synth.linear_case(0, 9, 7, "f32", seed=6)
+    _, dW = run(e, need_dx=False)
+    assert bool((dW == 0).all())
+
+
+def test_misaligned_pointers_take_a_correct_path():
+    case = synth.linear_case(64, 136, 136, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=8)
+    dX, dW = run(case, offset=1)
+    check_full(case, dX, dW)
+
+
+@pytest.mark.parametrize("M,K,N", [(96, 256, 264), (24, 264, 256), (300, 520, 136)])
+def test_integer_inputs_are_exact(M, K, N):
+    """Values in {-2..2}: products exact, fp32 sums exact; dW bitwise, dX = RNE(exact)."""
+    rng = np.random.default_rng(M)
+    mk = lambda *s: torch.tensor(rng.integers(-2, 3, size=s), dtype=torch.float32).to(torch.bfloat16)
+    case = synth.LinearCase(M, K, N, "bf16", mk(M, K), mk(K, N), mk(M, N))
+    dX, dW = run(case)
+    rX, rW = oracle.lin_bwd(synth.bits(case.X), synth.bits(case.W), synth.bits(case.G), "bf16")
+    assert np.array_equal(dW.cpu().numpy(), rW.astype(np.float32))
+    want = torch.from_numpy(rX.astype(np.float32)).to(torch.bfloat16)
+    assert torch.equal(dX.cpu(), want)
+
+
+def test_identity_operands_are_bitwise():
+    n = 256
+    G = synth.to_storage(synth.normal((n, n), 1.0, synth._gen(9)), "bf16")
+    eye = torch.eye(n, dtype=torch.bfloat16)
+    # W = I: dX = G exactly;  X = I: dW = G exactly
+    case = synth.LinearCase(n, n, n, "bf16", eye, eye, G)
+    dX, dW = run(case)
+    assert torch.equal(dX.cpu(), G)
+    assert torch.equal(dW.cpu(), G.float())
+
+
+def test_scaling_and_determinism():
+    case = synth.linear_case(384, 512, 520, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=10)
+    dX1, dW1 = run(case)
+    dX2, dW2 = run(case)
+    assert torch.equal(dX1, dX2) and torch.equal(dW1, dW2)
+    twice = synth.LinearCase(case.M, case.K, case.N, "bf16", (case.X.float() * 2).bfloat16(),
+                             case.W, case.G)
+    _, dW3 = run(twice, need_dx=False)
+    assert torch.equal(dW3, dW1 * 2)
+
+
+def test_non_default_stream():
+    case = synth.linear_case(160, 264, 200, "bf16", seed=11)
+    s = torch.cuda.Stream()
+    dX, dW = run(case, stream=s)
+    check_full(case, dX, dW)
+
+
+def test_decode_like_m32_full_compare():
+    """bf16 X[32,4096], W[4096,4096], G[32,4096]: every entry against the oracle."""
+    case = synth.linear_m32(seed=0)
+    dX, dW = run(case)
+    check_full(case, dX, dW)
+
+
+def _sampled_check(case, dX, dW, count, seed):
+    Xb, Wb, Gb = synth.bits(case.X), synth.bits(case.W), synth.bits(case.G)
+    r, c = sample_positions(case.M, case.K, count, seed)
+    ref = oracle.dx_at(Gb, Wb, "bf16", r, c)
+    got = host_f64(dX[torch.from_numpy(r), torch.from_numpy(c)])
+    assert relf(got, ref) <= DX_RELF, "dX sampled relF %.3g" % relf(got, ref)
+    # each bf16 entry is within one rounding (2^-8 relative) of the exact value, plus
+    # the fp32 accumulation error of its sum
+    scale = np.abs(ref) + 1e-3 * np.sqrt(np.mean(ref ** 2))
+    assert np.all(np.abs(got - ref) <= 2 ** -8 * scale)
+    r, c = sample_positions(case.K, case.N, count, seed + 1)
+    ref = oracle.dw_at(Xb, Gb, "bf16", r, c)
+    got = host_f64(dW[torch.from_numpy(r), torch.from_numpy(c)])
+    assert relf(got, ref) <= DW_RELF, "dW sampled relF %.3g" % relf(got, ref)
+
+
+def test_large_m2048_sampled():
+    """bf16 X[2048,4096], W[4096,4096], G[2048,4096]: sampled entries + determinism."""
+    case = synth.linear_m2048(seed=0)
+    dX, dW = run(case)
+    assert not torch.isnan(dX).any() and not torch.isnan(dW).any()
+    _sampled_check(case, dX, dW, 4096, 0)
+    dX2, dW2 = run(case)
+    assert torch.equal(dX, dX2) and torch.equal(dW, dW2)
+
+
+@pytest.mark.parametrize("proj", range(4))
+def test_block_projection_sampled(proj):
+    """One Transformer block's projections at M = 16384 (QKV, out, up, down), sampled."""
+    name, k, n = synth.BLOCK_PROJECTIONS[proj]
+    case = synth.linear_case(synth.BLOCK_TOKENS, k, n, "bf16", x_std=1.0, w_std=0.02,
+                             g_std=1e-4, seed=1 + proj, name=name)
+    dX, dW = run(case)
+    assert not torch.isnan(dX).any() and not torch.isnan(dW).any()
+    _sampled_check(case, dX, dW, 2048, proj)
