@@ -9,9 +9,7 @@
 // The kernel is memory bound: it reads grad, W, m, v once and writes W, m, v
 // once (26 B per parameter with a 16-bit gradient, 28 B with fp32), never
 // writes the gradient, and takes the bias corrections bc1 = 1-b1^t,
-// bc2 = 1-b2^t from the host instead of evaluating pow per thread.  Each
-// thread moves 8 parameters per trip with 16-byte non-temporal accesses, in
-// a grid-stride loop sized to keep every CU's memory pipeline full.
+// bc2 = 1-b2^t from the host instead of evaluating pow per thread.
 //
 // The float arithmetic is evaluated in the order above with contraction off
 // and IEEE division / square root, so each parameter's result does not
@@ -23,28 +21,23 @@ namespace lb {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVec = 8; // parameters per thread per trip
+constexpr int kVec = 4; // parameters per thread
 
 template <int GT> struct Grad;
 template <> struct Grad<GRAD_F32> {
-    static __device__ __forceinline__ void load8(const void *g, int64_t i, float (&out)[8]) {
-        const f32x4_t *p = reinterpret_cast<const f32x4_t *>(static_cast<const float *>(g) + i);
-        f32x4_t a = __builtin_nontemporal_load(p);
-        f32x4_t b = __builtin_nontemporal_load(p + 1);
-        for (int e = 0; e < 4; ++e) {
+    static __device__ __forceinline__ void load4(const void *g, int64_t i, float (&out)[4]) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(g) + i);
+        for (int e = 0; e < 4; ++e)
             out[e] = a[e];
-            out[4 + e] = b[e];
-        }
     }
     static __device__ __forceinline__ float load1(const void *g, int64_t i) {
         return static_cast<const float *>(g)[i];
     }
 };
 template <> struct Grad<GRAD_F16> {
-    static __device__ __forceinline__ void load8(const void *g, int64_t i, float (&out)[8]) {
-        const u32x4_t *p = reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(g) + i);
-        u32x4_t w = __builtin_nontemporal_load(p);
-        for (int e = 0; e < 4; ++e) {
+    static __device__ __forceinline__ void load4(const void *g, int64_t i, float (&out)[4]) {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(g) + i);
+        for (int e = 0; e < 2; ++e) {
             out[2 * e] = f16_bits_to_f32((uint16_t)(w[e] & 0xffffu));
             out[2 * e + 1] = f16_bits_to_f32((uint16_t)(w[e] >> 16));
         }
@@ -54,10 +47,9 @@ template <> struct Grad<GRAD_F16> {
     }
 };
 template <> struct Grad<GRAD_BF16> {
-    static __device__ __forceinline__ void load8(const void *g, int64_t i, float (&out)[8]) {
-        const u32x4_t *p = reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(g) + i);
-        u32x4_t w = __builtin_nontemporal_load(p);
-        for (int e = 0; e < 4; ++e) {
+    static __device__ __forceinline__ void load4(const void *g, int64_t i, float (&out)[4]) {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(g) + i);
+        for (int e = 0; e < 2; ++e) {
             out[2 * e] = bf16_bits_to_f32(w[e] & 0xffffu);
             out[2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);
         }
@@ -77,66 +69,55 @@ __device__ __forceinline__ void update(float &w, float &m, float &v, float graw,
     w = w - a.lr * (mh / (sqrtf(vh) + a.eps) + a.wd * w);
 }
 
-__device__ __forceinline__ void load8f(const float *p, float (&out)[8]) {
-    const f32x4_t *q = reinterpret_cast<const f32x4_t *>(p);
-    f32x4_t x = __builtin_nontemporal_load(q);
-    f32x4_t y = __builtin_nontemporal_load(q + 1);
-    for (int e = 0; e < 4; ++e) {
-        out[e] = x[e];
-        out[4 + e] = y[e];
-    }
-}
-
-__device__ __forceinline__ void store8f(float *p, const float (&in)[8]) {
-    f32x4_t *q = reinterpret_cast<f32x4_t *>(p);
-    f32x4_t x = {in[0], in[1], in[2], in[3]};
-    f32x4_t y = {in[4], in[5], in[6], in[7]};
-    __builtin_nontemporal_store(x, q);
-    __builtin_nontemporal_store(y, q + 1);
-}
-
-// VEC: all four buffers 16-byte aligned; groups of 8 parameters, scalar tail.
+// One thread per group of 4 parameters (the grid covers n exactly): on this
+// part a single 16-byte access per stream per thread, with plain (temporal)
+// loads and stores and no grid-stride loop, streams fastest.  VEC: all four
+// buffers 16-byte aligned (8 for a 16-bit gradient); the last partial group
+// and misaligned buffers take the scalar loop.
 template <int GT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_adamw(AdamWArgs a) {
-    const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t nthreads = (int64_t)gridDim.x * kThreads;
-    int64_t done = 0;
-    if (VEC) {
-        const int64_t groups = a.n / kVec;
-        for (int64_t gi = tid; gi < groups; gi += nthreads) {
-            const int64_t i = gi * kVec;
-            float g[8], w[8], m[8], v[8];
-            Grad<GT>::load8(a.g, i, g);
-            load8f(a.W + i, w);
-            load8f(a.m + i, m);
-            load8f(a.v + i, v);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                update(w[e], m[e], v[e], g[e], a);
-            store8f(a.W + i, w);
-            store8f(a.m + i, m);
-            store8f(a.v + i, v);
+    const int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kVec;
+    if (i >= a.n)
+        return;
+    if (VEC && i + kVec <= a.n) {
+        float g[4], w[4], m[4], v[4];
+        Grad<GT>::load4(a.g, i, g);
+        const f32x4_t W4 = *reinterpret_cast<const f32x4_t *>(a.W + i);
+        const f32x4_t M4 = *reinterpret_cast<const f32x4_t *>(a.m + i);
+        const f32x4_t V4 = *reinterpret_cast<const f32x4_t *>(a.v + i);
+        for (int e = 0; e < 4; ++e) {
+            w[e] = W4[e];
+            m[e] = M4[e];
+            v[e] = V4[e];
         }
-        done = groups * kVec;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            update(w[e], m[e], v[e], g[e], a);
+        *reinterpret_cast<f32x4_t *>(a.W + i) = f32x4_t{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<f32x4_t *>(a.m + i) = f32x4_t{m[0], m[1], m[2], m[3]};
+        *reinterpret_cast<f32x4_t *>(a.v + i) = f32x4_t{v[0], v[1], v[2], v[3]};
+        return;
     }
-    for (int64_t i = done + tid; i < a.n; i += nthreads) {
-        float w = a.W[i], m = a.m[i], v = a.v[i];
-        update(w, m, v, Grad<GT>::load1(a.g, i), a);
-        a.W[i] = w;
-        a.m[i] = m;
-        a.v[i] = v;
+    const int64_t end = i + kVec < a.n ? i + kVec : a.n;
+    for (int64_t j = i; j < end; ++j) {
+        float w = a.W[j], m = a.m[j], v = a.v[j];
+        update(w, m, v, Grad<GT>::load1(a.g, j), a);
+        a.W[j] = w;
+        a.m[j] = m;
+        a.v[j] = v;
     }
 }
 
 template <int GT>
 hipError_t launch_t(const AdamWArgs &a, hipStream_t s) {
+    const uintptr_t galign = GT == GRAD_F32 ? 15u : 7u;
     const bool vec = ((reinterpret_cast<uintptr_t>(a.W) | reinterpret_cast<uintptr_t>(a.m) |
-                       reinterpret_cast<uintptr_t>(a.v) | reinterpret_cast<uintptr_t>(a.g)) & 15u) == 0;
-    // enough resident waves to cover HBM latency: 256 CUs x 8 blocks of 4 waves
-    const int64_t work = vec ? (a.n + kVec - 1) / kVec : a.n;
-    int64_t blocks = (work + kThreads - 1) / kThreads;
-    if (blocks > 2048) blocks = 2048;
-    if (blocks < 1) blocks = 1;
+                       reinterpret_cast<uintptr_t>(a.v)) & 15u) == 0 &&
+                     (reinterpret_cast<uintptr_t>(a.g) & galign) == 0;
+    const int64_t groups = (a.n + kVec - 1) / kVec;
+    const int64_t blocks = (groups + kThreads - 1) / kThreads;
+    if (blocks > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
     if (vec)
         hipLaunchKernelGGL((k_adamw<GT, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     else

@@ -29,6 +29,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace lb {
 namespace {
@@ -39,18 +40,33 @@ namespace {
 constexpr int kTile = 256;                        // output tile edge (i and j)
 constexpr int kBK = 64;                           // reduction slab per stage
 constexpr int kThreads = 256;                     // 4 waves, 2x2, 128x128 each
-constexpr int kRowBytes = kBK * 2;                // one LDS row: 64 bf16
-constexpr int kOperandBytes = kTile * kRowBytes;  // 32 KiB
+constexpr int kOperandBytes = kTile * kBK * 2;    // one operand slab in LDS: 32 KiB
 constexpr int kStageBytes = 2 * kOperandBytes;    // A and B
 constexpr int kLdsBytes = 2 * kStageBytes;        // double buffered: 128 KiB
 constexpr int kGroupI = 4;                        // tile rows per raster group
+constexpr uint32_t kOOB = 0x80000000u;            // buffer offset past num_records: reads 0
 
-// 16-byte chunk c (0..7) of LDS row `row`: XOR swizzle so that the MFMA reads
-// (8 consecutive rows, same chunk) and both store patterns hit distinct banks.
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-    const int swz = (row & 7) ^ ((row >> 3) & 7);
-    return row * kRowBytes + ((chunk ^ swz) << 4);
-}
+#define LDS __attribute__((address_space(3)))
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// Operand slabs live in LDS in one of two layouts, both written by
+// global->LDS DMA (buffer_load_dwordx4 ... lds: lane l of a wave
+// instruction writes 16 bytes at M0 + 16*l, so one instruction fills 1 KiB).
+// The XOR swizzles are applied by choosing which global chunk each lane
+// fetches; the LDS side is always contiguous.
+//
+//  RC ("reduction contiguous", dX operands dY and W): 256 rows (output index)
+//     x 64 r, 128 B per row; 16-byte chunk c of row `row` is stored at
+//     chunk c ^ swz_rc(row).  MFMA fragment = one ds_read_b128 (8 r values).
+//  OC ("outer contiguous", dW operands X and dY): 64 rows (r) x 256 outer
+//     indices, 512 B per row; chunk c of row r is stored at chunk
+//     c ^ swz_oc(r).  MFMA fragment = two ds_read_b64_tr_b16: within each
+//     16-lane group the instruction reads a 4-row x 16-column block (each
+//     lane addresses 4 columns of one row) and hands lane i column i, so a
+//     lane receives 4 consecutive r of its own outer index.
+__device__ __forceinline__ int swz_rc(int row) { return (row & 7) ^ ((row >> 3) & 7); }
+__device__ __forceinline__ int swz_oc(int row) { return 2 * (row & 3); }
+__device__ __forceinline__ int rc_off(int row, int chunk) { return row * 128 + ((chunk ^ swz_rc(row)) << 4); }
 
 enum JobKind { JOB_DX = 0, JOB_DW = 1 };
 
@@ -60,8 +76,9 @@ struct TileJob {
     void *c;           // output, row-major [I, J], leading dim J
     int64_t I, J, R;   // output rows, cols, reduction length
     int64_t lda, ldb;  // leading dims of a and b in elements
+    uint32_t a_bytes, b_bytes; // operand sizes (each < 2 GiB on this path)
     int tiles_i, tiles_j, ntiles;
-    int kind;          // JOB_DX: r-contiguous operands, bf16 out; JOB_DW: outer-contiguous, fp32 out
+    int kind;          // JOB_DX: RC operands, bf16 out; JOB_DW: OC operands, fp32 out
 };
 
 struct MfmaParams {
@@ -69,93 +86,78 @@ struct MfmaParams {
     int njobs;
 };
 
-// r-contiguous operand: element (o, r) at base[o*ld + r].  Thread t loads
-// rows (t>>3) + 32p, chunk t&7 of the slab: each wave instruction reads
-// eight 128-byte row segments.
-__device__ __forceinline__ void load_rc(u32x4_t (&reg)[8], const uint16_t *base, int64_t ld,
-                                        int64_t O, int64_t R, int64_t o0, int64_t r0, int t) {
-    const int c = t & 7;
-    const int orow = t >> 3;
-    const int64_t r = r0 + 8 * c;
-    const bool rok = r < R; // R % 8 == 0: a chunk is entirely in or out
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    // raw buffer: stride 0, num_records in bytes, gfx9 data-format word
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, LDS char *dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void *)dst, 16, (int)off, 0, 0, 0);
+}
+
+// RC slab: element (o, r) at base[o*ld + r].  Wave w, instruction p fills LDS
+// rows 8(8w+p) .. +7; lane -> row (lane>>3), physical chunk (lane&7).
+template <int P0, int NP>
+__device__ __forceinline__ void dma_rc(__amdgpu_buffer_rsrc_t rs, LDS char *op, int64_t ld, int64_t O,
+                                       int64_t R, int64_t o0, int64_t r0, int w, int lane) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int64_t o = o0 + orow + 32 * p;
-        if (rok && o < O)
-            reg[p] = *reinterpret_cast<const u32x4_t *>(base + o * ld + r);
-        else
-            reg[p] = u32x4_t{0, 0, 0, 0};
+    for (int p = P0; p < P0 + NP; ++p) {
+        const int row = (w * 8 + p) * 8 + (lane >> 3);
+        const int lc = (lane & 7) ^ swz_rc(row);
+        const int64_t o = o0 + row;
+        const int64_t r = r0 + 8 * lc;
+        const uint32_t off = (o < O && r < R) ? (uint32_t)((o * ld + r) * 2) : kOOB;
+        dma16(rs, op + (w * 8 + p) * 1024, off);
     }
 }
 
-__device__ __forceinline__ void store_rc(char *lds, const u32x4_t (&reg)[8], int t) {
-    const int c = t & 7;
-    const int orow = t >> 3;
+// OC slab: element (r, o) at base[r*ld + o].  Wave w, instruction p fills LDS
+// rows 2(8w+p), +1; lane -> row (lane>>5), physical chunk (lane&31).
+template <int P0, int NP>
+__device__ __forceinline__ void dma_oc(__amdgpu_buffer_rsrc_t rs, LDS char *op, int64_t ld, int64_t O,
+                                       int64_t R, int64_t r0, int64_t o0, int w, int lane) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
-        *reinterpret_cast<u32x4_t *>(lds + lds_off(orow + 32 * p, c)) = reg[p];
-}
-
-// outer-contiguous operand: element (o, r) at base[r*ld + o].  Thread t
-// loads the 8x8 block r in [8(t>>5), +8), o in [8(t&31), +8): eight 16-byte
-// loads, one per r; a wave instruction reads two 512-byte row segments.
-__device__ __forceinline__ void load_oc(u32x4_t (&reg)[8], const uint16_t *base, int64_t ld,
-                                        int64_t O, int64_t R, int64_t o0, int64_t r0, int t) {
-    const int oc = t & 31;
-    const int rb = t >> 5;
-    const int64_t o = o0 + 8 * oc;
-    const bool ook = o < O; // O % 8 == 0
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int64_t r = r0 + 8 * rb + p;
-        if (ook && r < R)
-            reg[p] = *reinterpret_cast<const u32x4_t *>(base + r * ld + o);
-        else
-            reg[p] = u32x4_t{0, 0, 0, 0};
+    for (int p = P0; p < P0 + NP; ++p) {
+        const int row = (w * 8 + p) * 2 + (lane >> 5);
+        const int lc = (lane & 31) ^ swz_oc(row);
+        const int64_t r = r0 + row;
+        const int64_t o = o0 + 8 * lc;
+        const uint32_t off = (o < O && r < R) ? (uint32_t)((r * ld + o) * 2) : kOOB;
+        dma16(rs, op + (w * 8 + p) * 1024, off);
     }
 }
 
-// Transpose the 8x8 block in registers (reg[p] holds r = p, o = 0..7) and
-// store row o = 8(t&31)+e of the LDS tile with its 8 r values (chunk t>>5).
-__device__ __forceinline__ void store_oc(char *lds, const u32x4_t (&reg)[8], int t) {
-    const int oc = t & 31;
-    const int rb = t >> 5;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int q = e >> 1;
-        u32x4_t out;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const uint32_t lo = reg[2 * h][q];     // r = 2h
-            const uint32_t hi = reg[2 * h + 1][q]; // r = 2h + 1
-            out[h] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                             : ((lo & 0xffffu) | (hi << 16));
-        }
-        *reinterpret_cast<u32x4_t *>(lds + lds_off(8 * oc + e, rb)) = out;
-    }
+// MFMA fragment (8 consecutive r of outer index `ob + (lane&31)`, r half
+// chosen by lane>>5) for k-step ks of the slab.
+__device__ __forceinline__ bf16x8_t frag_rc(const LDS char *op, int ob, int ks, int lane) {
+    const int row = ob + (lane & 31);
+    return *reinterpret_cast<const LDS bf16x8_t *>(op + rc_off(row, 2 * ks + (lane >> 5)));
 }
 
-// One 64-deep slab: 4 MFMA k-steps of 16 over the wave's 4x4 grid of 32x32 blocks.
-// MFMA operand roles are swapped (src A = the j-side tile) so that each lane's
-// accumulators hold 4 consecutive output columns of one output row.
-__device__ __forceinline__ void mma_slab(const char *la, const char *lb, f32x16_t (&acc)[4][4],
-                                         int wm, int wn, int lane) {
-    const int rl = lane & 31;
-    const int half = lane >> 5;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        bf16x8_t af[4], bf[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            af[x] = *reinterpret_cast<const bf16x8_t *>(la + lds_off(wm * 128 + x * 32 + rl, 2 * s + half));
-            bf[x] = *reinterpret_cast<const bf16x8_t *>(lb + lds_off(wn * 128 + x * 32 + rl, 2 * s + half));
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int y = 0; y < 4; ++y)
-                acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[y], af[x], acc[x][y], 0, 0, 0);
-    }
+__device__ __forceinline__ bf16x8_t frag_oc(const LDS char *op, int ob, int ks, int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    const int row = ks * 16 + 8 * (g >> 1) + (s >> 2);
+    const int col = ob + 16 * (g & 1) + 4 * (s & 3);
+    const int lc = col >> 3;
+    const int a0 = row * 512 + ((lc ^ swz_oc(row)) << 4) + (col & 7) * 2;
+    const int a1 = (row + 4) * 512 + ((lc ^ swz_oc(row + 4)) << 4) + (col & 7) * 2;
+    // Issued as inline asm: the compiler's wait insertion treats the builtin as
+    // aliasing the in-flight DMA into the other stage buffer and would stall on
+    // it.  The caller waits for these reads with lgkm_wait() before use.
+    bf16x4_t lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(op + a0));
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(op + a1));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Wait for all of this wave's LDS reads; the fragments are threaded through the
+// asm so no MFMA that consumes them can be scheduled above the wait.
+__device__ __forceinline__ void lgkm_wait(bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]),
+                   "+v"(b[3])
+                 :
+                 : "memory");
 }
 
 // Tile index within a job -> (ti, tj).  Consecutive block ids land on
@@ -176,15 +178,16 @@ __device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, i
 }
 
 template <int KIND>
-__device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, char *smem) {
+__device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS char *smem) {
     int ti, tj;
     tile_coords(jb, t_index, ti, tj);
     const int64_t i0 = (int64_t)ti * kTile;
     const int64_t j0 = (int64_t)tj * kTile;
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int w = t >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
     const int wm = w >> 1, wn = w & 1;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(jb.a, jb.a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(jb.b, jb.b_bytes);
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -193,42 +196,88 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, char *s
         for (int y = 0; y < 4; ++y)
             acc[x][y] = f32x16_t{};
 
-    const int nslab = (int)((jb.R + kBK - 1) / kBK);
-    u32x4_t ra[8], rb[8];
-    auto load = [&](int64_t r0) {
+    // DMA of slab s into its stage buffer, instructions [P0, P0+NP) of each operand
+    auto issue = [&](int s, auto p0, auto np) {
+        constexpr int P0 = decltype(p0)::value, NP = decltype(np)::value;
+        LDS char *st = smem + (s & 1) * kStageBytes;
+        const int64_t r0 = (int64_t)s * kBK;
         if (KIND == JOB_DX) {
-            load_rc(ra, jb.a, jb.lda, jb.I, jb.R, i0, r0, t);
-            load_rc(rb, jb.b, jb.ldb, jb.J, jb.R, j0, r0, t);
+            dma_rc<P0, NP>(ra, st, jb.lda, jb.I, jb.R, i0, r0, w, lane);
+            dma_rc<P0, NP>(rb, st + kOperandBytes, jb.ldb, jb.J, jb.R, j0, r0, w, lane);
         } else {
-            load_oc(ra, jb.a, jb.lda, jb.I, jb.R, i0, r0, t);
-            load_oc(rb, jb.b, jb.ldb, jb.J, jb.R, j0, r0, t);
+            dma_oc<P0, NP>(ra, st, jb.lda, jb.I, jb.R, r0, i0, w, lane);
+            dma_oc<P0, NP>(rb, st + kOperandBytes, jb.ldb, jb.J, jb.R, r0, j0, w, lane);
         }
     };
-    auto store = [&](char *stage) {
-        if (KIND == JOB_DX) {
-            store_rc(stage, ra, t);
-            store_rc(stage + kOperandBytes, rb, t);
-        } else {
-            store_oc(stage, ra, t);
-            store_oc(stage + kOperandBytes, rb, t);
-        }
+    auto frag = [&](const LDS char *op, int ob, int ks) {
+        return KIND == JOB_DX ? frag_rc(op, ob, ks, lane) : frag_oc(op, ob, ks, lane);
     };
+    using C0 = std::integral_constant<int, 0>;
+    using C2 = std::integral_constant<int, 2>;
+    using C8 = std::integral_constant<int, 8>;
+    // LDS reads per fragment: one b128 (RC) or two transposing b64 (OC)
+    constexpr int kReadsPerFrag = KIND == JOB_DX ? 1 : 2;
 
-    if (nslab > 0) {
-        load(0);
-        store(smem);
-        __syncthreads();
-    }
+    const int nslab = (int)((jb.R + kBK - 1) / kBK);
+    if (nslab > 0)
+        issue(0, C0{}, C8{});
     for (int s = 0; s < nslab; ++s) {
-        char *cur = smem + (s & 1) * kStageBytes;
-        char *nxt = smem + ((s + 1) & 1) * kStageBytes;
-        const bool more = s + 1 < nslab;
-        if (more)
-            load((int64_t)(s + 1) * kBK); // global loads in flight during the MFMAs
-        mma_slab(cur, cur + kOperandBytes, acc, wm, wn, lane);
-        if (more)
-            store(nxt);
+        // this wave's DMA of slab s has landed; after the barrier, everyone's has,
+        // and every wave is done reading the buffer that slab s+1 will fill
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        const bool more = s + 1 < nslab;
+        const LDS char *la = smem + (s & 1) * kStageBytes;
+        const LDS char *lb = la + kOperandBytes;
+        bf16x8_t af[4], bf[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            af[x] = frag(la, wm * 128 + x * 32, 0);
+            bf[x] = frag(lb, wn * 128 + x * 32, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            // one scheduling region per k-step: the next step's fragment reads and a
+            // quarter of the next slab's DMA are interleaved with this step's 16 MFMAs
+            if (KIND == JOB_DW)
+                lgkm_wait(af, bf); // the asm transposing reads of this step's fragments
+            bf16x8_t an[4], bn[4];
+            if (ks + 1 < 4) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    an[x] = frag(la, wm * 128 + x * 32, ks + 1);
+                    bn[x] = frag(lb, wn * 128 + x * 32, ks + 1);
+                }
+            }
+            if (more) {
+                if (ks == 0) issue(s + 1, std::integral_constant<int, 0>{}, C2{});
+                if (ks == 1) issue(s + 1, std::integral_constant<int, 2>{}, C2{});
+                if (ks == 2) issue(s + 1, std::integral_constant<int, 4>{}, C2{});
+                if (ks == 3) issue(s + 1, std::integral_constant<int, 6>{}, C2{});
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y)
+                    acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[y], af[x], acc[x][y], 0, 0, 0);
+            if (ks + 1 < 4) {
+                // 8 fragments = 8 (RC) or 16 (OC) LDS reads spread over the 16 MFMAs
+#pragma unroll
+                for (int i = 0; i < 8 * kReadsPerFrag; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 16 / (8 * kReadsPerFrag), 0); // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        // DS read
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < 4) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    af[x] = an[x];
+                    bf[x] = bn[x];
+                }
+            }
+        }
     }
 
     // Epilogue: lane holds C[i][j..j+3] for i = .. + (lane&31), j = .. + 8g + 4(lane>>5).
@@ -260,7 +309,8 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, char *s
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
-    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
+    LDS char *smem = (LDS char *)smem_raw;
     int b = blockIdx.x;
     const TileJob *jb = &p.job[0];
     if (b >= p.job[0].ntiles) {
@@ -429,6 +479,11 @@ TileJob make_tile_job(int kind, const void *a, const void *b, void *c, int64_t I
     j.R = R;
     j.lda = lda;
     j.ldb = ldb;
+    // RC operands have I (resp. J) rows of ld elements; OC operands have R rows
+    const int64_t a_rows = kind == JOB_DX ? I : R;
+    const int64_t b_rows = kind == JOB_DX ? J : R;
+    j.a_bytes = (uint32_t)(a_rows * lda * 2);
+    j.b_bytes = (uint32_t)(b_rows * ldb * 2);
     j.tiles_i = ceil_div(I, kTile);
     j.tiles_j = ceil_div(J, kTile);
     j.ntiles = j.tiles_i * j.tiles_j;
@@ -477,6 +532,12 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
     if (need_dw)
         vec = vec && is_aligned16(a.dW) && (a.M == 0 || (is_aligned16(a.X) && is_aligned16(a.dY)));
     if (!vec)
+        return launch_simt(a, need_dx, need_dw, s);
+
+    // buffer offsets are 32-bit with 2^31 marking "out of range": each operand
+    // of the MFMA path must be smaller than 2 GiB
+    const int64_t lim = (int64_t)1 << 31;
+    if (2 * a.M * a.K >= lim || 2 * a.K * a.N >= lim || 2 * a.M * a.N >= lim)
         return launch_simt(a, need_dx, need_dw, s);
 
     const bool small_dx = need_dx && a.M <= kSmallMaxM && a.N > 0;

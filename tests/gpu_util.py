@@ -71,10 +71,12 @@ def ulp_distance_f32(a, b):
 def adamw_ok(gpu, ref):
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
-    both_nan = np.isnan(gpu) & np.isnan(ref)
-    err = np.abs(gpu - ref)
-    ok = (err <= ADAMW_ABS * np.maximum(1.0, np.abs(ref))) | both_nan
-    return bool(ok.all()), float(np.nanmax(err / np.maximum(1.0, np.abs(ref)))) if err.size else 0.0
+    same = (np.isnan(gpu) & np.isnan(ref)) | (gpu == ref)   # NaN vs NaN, inf vs inf
+    with np.errstate(invalid="ignore"):
+        err = np.where(same, 0.0, np.abs(gpu - ref))
+    ok = same | (err <= ADAMW_ABS * np.maximum(1.0, np.abs(ref)))
+    worst = float(np.nanmax(err / np.maximum(1.0, np.abs(ref)))) if err.size else 0.0
+    return bool(ok.all()), worst
 
 
 def sample_positions(rows, cols, count, seed):
