@@ -38,11 +38,14 @@ namespace {
 // MFMA tile kernel
 // ------------------------------------------------------------------------
 constexpr int kTile = 256;                        // output tile edge (i and j)
-constexpr int kBK = 64;                           // reduction slab per stage
+constexpr int kBK = 32;                           // reduction slab per stage
+constexpr int kStages = 4;                        // LDS ring: 3 slabs in flight
 constexpr int kThreads = 256;                     // 4 waves, 2x2, 128x128 each
-constexpr int kOperandBytes = kTile * kBK * 2;    // one operand slab in LDS: 32 KiB
+constexpr int kOperandBytes = kTile * kBK * 2;    // one operand slab in LDS: 16 KiB
 constexpr int kStageBytes = 2 * kOperandBytes;    // A and B
-constexpr int kLdsBytes = 2 * kStageBytes;        // double buffered: 128 KiB
+constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
+constexpr int kKSteps = kBK / 16;                 // MFMA k-steps per slab
+constexpr int kDmaPerOp = kBK / 8;                // DMA instructions per wave per operand per slab
 constexpr int kGroupI = 4;                        // tile rows per raster group
 constexpr uint32_t kOOB = 0x80000000u;            // buffer offset past num_records: reads 0
 
@@ -53,20 +56,33 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 // global->LDS DMA (buffer_load_dwordx4 ... lds: lane l of a wave
 // instruction writes 16 bytes at M0 + 16*l, so one instruction fills 1 KiB).
 // The XOR swizzles are applied by choosing which global chunk each lane
-// fetches; the LDS side is always contiguous.
+// fetches; the LDS side is always contiguous.  Both swizzles are free of bank
+// conflicts whether the LDS serves 8 or 16 lanes of a 16-byte read (resp. 16
+// or 32 lanes of an 8-byte read) per cycle.
 //
-//  RC ("reduction contiguous", dX operands dY and W): 256 rows (output index)
-//     x 64 r, 128 B per row; 16-byte chunk c of row `row` is stored at
-//     chunk c ^ swz_rc(row).  MFMA fragment = one ds_read_b128 (8 r values).
-//  OC ("outer contiguous", dW operands X and dY): 64 rows (r) x 256 outer
+//  RC ("reduction contiguous", dX operands dY and W): 128 lines of 128 B;
+//     line k holds the 32 r of output rows k (chunks 0-3) and k + 128
+//     (chunks 4-7), and 16-byte chunk c of line k is stored at chunk
+//     c ^ swz_rc(k).  An MFMA fragment (one ds_read_b128, 8 r values) then
+//     reads 32 consecutive lines at one chunk, which this swizzle serves
+//     without bank conflicts.
+//  OC ("outer contiguous", dW operands X and dY): 32 rows (r) x 256 outer
 //     indices, 512 B per row; chunk c of row r is stored at chunk
 //     c ^ swz_oc(r).  MFMA fragment = two ds_read_b64_tr_b16: within each
 //     16-lane group the instruction reads a 4-row x 16-column block (each
 //     lane addresses 4 columns of one row) and hands lane i column i, so a
 //     lane receives 4 consecutive r of its own outer index.
-__device__ __forceinline__ int swz_rc(int row) { return (row & 7) ^ ((row >> 3) & 7); }
-__device__ __forceinline__ int swz_oc(int row) { return 2 * (row & 3); }
-__device__ __forceinline__ int rc_off(int row, int chunk) { return row * 128 + ((chunk ^ swz_rc(row)) << 4); }
+static_assert(kBK == 32, "the RC line layout packs two 32-deep rows per 128-byte line");
+__device__ __forceinline__ int swz_rc(int line) { return (line & 7) ^ ((line >> 3) & 7); }
+__device__ __forceinline__ int swz_oc(int row) {
+    // 32-byte segment s of row r moves to s ^ {0,3,5,6}[r & 3] (chunk pairs stay together)
+    return 2 * ((0x6530 >> (4 * (row & 3))) & 7);
+}
+// LDS byte offset of 16-byte chunk c (0..3) of output row o (0..255) in an RC slab
+__device__ __forceinline__ int rc_off(int o, int c) {
+    const int line = o & 127;
+    return line * 128 + (((4 * (o >> 7) + c) ^ swz_rc(line)) << 4);
+}
 
 enum JobKind { JOB_DX = 0, JOB_DW = 1 };
 
@@ -95,59 +111,67 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, LDS char *dst, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void *)dst, 16, (int)off, 0, 0, 0);
 }
 
-// RC slab: element (o, r) at base[o*ld + r].  Wave w, instruction p fills LDS
-// rows 8(8w+p) .. +7; lane -> row (lane>>3), physical chunk (lane&7).
-template <int P0, int NP>
-__device__ __forceinline__ void dma_rc(__amdgpu_buffer_rsrc_t rs, LDS char *op, int64_t ld, int64_t O,
-                                       int64_t R, int64_t o0, int64_t r0, int w, int lane) {
-#pragma unroll
-    for (int p = P0; p < P0 + NP; ++p) {
-        const int row = (w * 8 + p) * 8 + (lane >> 3);
-        const int lc = (lane & 7) ^ swz_rc(row);
-        const int64_t o = o0 + row;
-        const int64_t r = r0 + 8 * lc;
-        const uint32_t off = (o < O && r < R) ? (uint32_t)((o * ld + r) * 2) : kOOB;
-        dma16(rs, op + (w * 8 + p) * 1024, off);
-    }
-}
-
-// OC slab: element (r, o) at base[r*ld + o].  Wave w, instruction p fills LDS
-// rows 2(8w+p), +1; lane -> row (lane>>5), physical chunk (lane&31).
-template <int P0, int NP>
-__device__ __forceinline__ void dma_oc(__amdgpu_buffer_rsrc_t rs, LDS char *op, int64_t ld, int64_t O,
-                                       int64_t R, int64_t r0, int64_t o0, int w, int lane) {
-#pragma unroll
-    for (int p = P0; p < P0 + NP; ++p) {
-        const int row = (w * 8 + p) * 2 + (lane >> 5);
+// Per-lane DMA source offsets, fixed for a tile.  Instruction p of wave w
+// fills 1 KiB of the operand slab at q = kDmaPerOp*w + p:
+//  RC: LDS line 8q + (lane>>3), physical chunk lane&7, which holds logical
+//      chunk (lane&7) ^ swz_rc(line) = 4*half + c: r-chunk c of output row
+//      line + 128*half.  Offset (o*ld + 8c)*2 relative to the slab's first r.
+//  OC: LDS row 2q + (lane>>5) (an r), physical chunk lane&31 holding outer
+//      chunk (lane&31) ^ swz_oc(row).  Offset (row*ld + o)*2 relative to the
+//      slab's first row.
+// Lanes whose row (RC) or outer chunk (OC) lies outside the operand get kOOB.
+template <int KIND>
+__device__ __forceinline__ uint32_t dma_lane_off(int p, int64_t ld, int64_t O, int64_t o0, int w, int lane) {
+    const int q = w * kDmaPerOp + p;
+    if (KIND == JOB_DX) {
+        const int line = q * 8 + (lane >> 3);
+        const int lc = (lane & 7) ^ swz_rc(line);
+        const int64_t o = o0 + line + 128 * (lc >> 2);
+        return o < O ? (uint32_t)((o * ld + 8 * (lc & 3)) * 2) : kOOB;
+    } else {
+        const int row = q * 2 + (lane >> 5);
         const int lc = (lane & 31) ^ swz_oc(row);
-        const int64_t r = r0 + row;
         const int64_t o = o0 + 8 * lc;
-        const uint32_t off = (o < O && r < R) ? (uint32_t)((r * ld + o) * 2) : kOOB;
-        dma16(rs, op + (w * 8 + p) * 1024, off);
+        return o < O ? (uint32_t)((row * ld + o) * 2) : kOOB;
     }
 }
 
-// MFMA fragment (8 consecutive r of outer index `ob + (lane&31)`, r half
-// chosen by lane>>5) for k-step ks of the slab.
-__device__ __forceinline__ bf16x8_t frag_rc(const LDS char *op, int ob, int ks, int lane) {
-    const int row = ob + (lane & 31);
-    return *reinterpret_cast<const LDS bf16x8_t *>(op + rc_off(row, 2 * ks + (lane >> 5)));
+// The last RC slab when R % kBK != 0: r-chunks past R must read as zero, and
+// (as ld == R) they would otherwise read the next row, so each lane checks r.
+__device__ __forceinline__ uint32_t dma_rc_tail_off(int p, int64_t ld, int64_t O, int64_t R, int64_t o0,
+                                                    int64_t r0, int w, int lane) {
+    const int q = w * kDmaPerOp + p;
+    const int line = q * 8 + (lane >> 3);
+    const int lc = (lane & 7) ^ swz_rc(line);
+    const int64_t o = o0 + line + 128 * (lc >> 2);
+    const int64_t r = r0 + 8 * (lc & 3);
+    return (o < O && r < R) ? (uint32_t)((o * ld + r) * 2) : kOOB;
 }
 
-__device__ __forceinline__ bf16x8_t frag_oc(const LDS char *op, int ob, int ks, int lane) {
+// Per-lane LDS byte offsets (within an operand slab) of the fragment for outer
+// block ob (32 wide) at k-step ks: one ds_read_b128 (RC) or two
+// ds_read_b64_tr_b16 (OC, rows r and r+4 of the 4x16 transposing read).
+__device__ __forceinline__ int frag_off_rc(int ob, int ks, int lane) {
+    return rc_off(ob + (lane & 31), 2 * ks + (lane >> 5));
+}
+__device__ __forceinline__ int frag_off_oc(int ob, int ks, int lane, int half) {
     const int g = lane >> 4, s = lane & 15;
-    const int row = ks * 16 + 8 * (g >> 1) + (s >> 2);
+    const int row = ks * 16 + 8 * (g >> 1) + (s >> 2) + 4 * half;
     const int col = ob + 16 * (g & 1) + 4 * (s & 3);
     const int lc = col >> 3;
-    const int a0 = row * 512 + ((lc ^ swz_oc(row)) << 4) + (col & 7) * 2;
-    const int a1 = (row + 4) * 512 + ((lc ^ swz_oc(row + 4)) << 4) + (col & 7) * 2;
-    // Issued as inline asm: the compiler's wait insertion treats the builtin as
-    // aliasing the in-flight DMA into the other stage buffer and would stall on
-    // it.  The caller waits for these reads with lgkm_wait() before use.
-    bf16x4_t lo, hi;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(op + a0));
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(op + a1));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return row * 512 + ((lc ^ swz_oc(row)) << 4) + (col & 7) * 2;
+}
+
+__device__ __forceinline__ bf16x8_t read_rc(const LDS char *p) {
+    return *reinterpret_cast<const LDS bf16x8_t *>(p);
+}
+// Issued as inline asm: the compiler's wait insertion treats the builtin as
+// aliasing the in-flight DMA into other stage buffers and would stall on it.
+// Callers wait for these reads with lgkm_wait() before use.
+__device__ __forceinline__ bf16x4_t read_tr(const LDS char *p) {
+    bf16x4_t v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(p));
+    return v;
 }
 
 // Wait for all of this wave's LDS reads; the fragments are threaded through the
@@ -158,6 +182,29 @@ __device__ __forceinline__ void lgkm_wait(bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
                    "+v"(b[3])
                  :
                  : "memory");
+}
+
+// Wait until at most `n` of this wave's DMA instructions are still in flight
+// (DMA completes in issue order).
+__device__ __forceinline__ void dma_wait(int n) {
+    if (n >= 16)
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (n >= 12)
+        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if (n >= 8)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (n >= 4)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Workgroup barrier that publishes this wave's landed DMA and retires its LDS
+// reads.  A plain s_barrier: __syncthreads() would add a release fence that
+// waits for *all* outstanding DMA (vmcnt(0)) and drains the ring.  The memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void slab_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Tile index within a job -> (ti, tj).  Consecutive block ids land on
@@ -179,6 +226,10 @@ __device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, i
 
 template <int KIND>
 __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS char *smem) {
+    static_assert(kKSteps == 2 && kStages == 4 && kDmaPerOp == 4, "pipeline below assumes 2 k-steps, 4 stages");
+    constexpr int kRPF = KIND == JOB_DX ? 1 : 2; // LDS reads per fragment
+    constexpr int kReads = 8 * kRPF;             // LDS reads per k-step (4 A + 4 B fragments)
+    constexpr int kDmaPerSlab = 2 * kDmaPerOp;
     int ti, tj;
     tile_coords(jb, t_index, ti, tj);
     const int64_t i0 = (int64_t)ti * kTile;
@@ -186,8 +237,29 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int wm = w >> 1, wn = w & 1;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(jb.a, jb.a_bytes);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(jb.b, jb.b_bytes);
+
+    // slab-independent per-lane offsets: DMA sources and LDS fragment addresses
+    uint32_t va[kDmaPerOp], vb[kDmaPerOp];
+#pragma unroll
+    for (int p = 0; p < kDmaPerOp; ++p) {
+        va[p] = dma_lane_off<KIND>(p, jb.lda, jb.I, i0, w, lane);
+        vb[p] = dma_lane_off<KIND>(p, jb.ldb, jb.J, j0, w, lane);
+    }
+    int fo[kKSteps][2][4][kRPF]; // [k-step][A/B][block][half]
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int h = 0; h < kRPF; ++h) {
+                if (KIND == JOB_DX) {
+                    fo[ks][0][x][h] = frag_off_rc(wm * 128 + x * 32, ks, lane);
+                    fo[ks][1][x][h] = kOperandBytes + frag_off_rc(wn * 128 + x * 32, ks, lane);
+                } else {
+                    fo[ks][0][x][h] = frag_off_oc(wm * 128 + x * 32, ks, lane, h);
+                    fo[ks][1][x][h] = kOperandBytes + frag_off_oc(wn * 128 + x * 32, ks, lane, h);
+                }
+            }
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -196,87 +268,117 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
         for (int y = 0; y < 4; ++y)
             acc[x][y] = f32x16_t{};
 
-    // DMA of slab s into its stage buffer, instructions [P0, P0+NP) of each operand
-    auto issue = [&](int s, auto p0, auto np) {
-        constexpr int P0 = decltype(p0)::value, NP = decltype(np)::value;
-        LDS char *st = smem + (s & 1) * kStageBytes;
+    const int nslab = (int)((jb.R + kBK - 1) / kBK);
+    const bool rc_tail = KIND == JOB_DX && (jb.R % kBK) != 0;
+
+    // DMA instruction p (of kDmaPerOp) of both operands for slab s.  The buffer
+    // descriptor's base advances to the slab (scalar work only); for OC its size
+    // shrinks to the rows left, so rows past R read as zero.
+    auto dma = [&](int s, int p) {
+        LDS char *st = smem + (s % kStages) * kStageBytes + (w * kDmaPerOp + p) * 1024;
         const int64_t r0 = (int64_t)s * kBK;
         if (KIND == JOB_DX) {
-            dma_rc<P0, NP>(ra, st, jb.lda, jb.I, jb.R, i0, r0, w, lane);
-            dma_rc<P0, NP>(rb, st + kOperandBytes, jb.ldb, jb.J, jb.R, j0, r0, w, lane);
+            if (rc_tail && s == nslab - 1) {
+                dma16(make_rsrc(jb.a, jb.a_bytes), st, dma_rc_tail_off(p, jb.lda, jb.I, jb.R, i0, r0, w, lane));
+                dma16(make_rsrc(jb.b, jb.b_bytes), st + kOperandBytes,
+                      dma_rc_tail_off(p, jb.ldb, jb.J, jb.R, j0, r0, w, lane));
+            } else {
+                dma16(make_rsrc(jb.a + r0, jb.a_bytes - (uint32_t)(2 * r0)), st, va[p]);
+                dma16(make_rsrc(jb.b + r0, jb.b_bytes - (uint32_t)(2 * r0)), st + kOperandBytes, vb[p]);
+            }
         } else {
-            dma_oc<P0, NP>(ra, st, jb.lda, jb.I, jb.R, r0, i0, w, lane);
-            dma_oc<P0, NP>(rb, st + kOperandBytes, jb.ldb, jb.J, jb.R, r0, j0, w, lane);
+            dma16(make_rsrc(jb.a + r0 * jb.lda, (uint32_t)(2 * (jb.R - r0) * jb.lda)), st, va[p]);
+            dma16(make_rsrc(jb.b + r0 * jb.ldb, (uint32_t)(2 * (jb.R - r0) * jb.ldb)), st + kOperandBytes, vb[p]);
         }
     };
-    auto frag = [&](const LDS char *op, int ob, int ks) {
-        return KIND == JOB_DX ? frag_rc(op, ob, ks, lane) : frag_oc(op, ob, ks, lane);
-    };
-    using C0 = std::integral_constant<int, 0>;
-    using C2 = std::integral_constant<int, 2>;
-    using C8 = std::integral_constant<int, 8>;
-    // LDS reads per fragment: one b128 (RC) or two transposing b64 (OC)
-    constexpr int kReadsPerFrag = KIND == JOB_DX ? 1 : 2;
 
-    const int nslab = (int)((jb.R + kBK - 1) / kBK);
-    if (nslab > 0)
-        issue(0, C0{}, C8{});
-    for (int s = 0; s < nslab; ++s) {
-        // this wave's DMA of slab s has landed; after the barrier, everyone's has,
-        // and every wave is done reading the buffer that slab s+1 will fill
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        const bool more = s + 1 < nslab;
-        const LDS char *la = smem + (s & 1) * kStageBytes;
-        const LDS char *lb = la + kOperandBytes;
-        bf16x8_t af[4], bf[4];
+    // One k-step: 16 MFMAs on (af, bf), each followed by at most one LDS read of
+    // the next fragments into (an, bn) and, in the last slots, one DMA
+    // instruction pair of slab `ds` (if ds >= 0).  sched_barrier pins the order
+    // so the matrix pipe never waits behind a run of address or memory work.
+    auto kstep = [&](bf16x8_t (&af)[4], bf16x8_t (&bf)[4], const LDS char *stage_next, int ks_next,
+                     bf16x8_t (&an)[4], bf16x8_t (&bn)[4], bool reads, int ds, int dp0) {
+        bf16x4_t tr[2][4][2];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            af[x] = frag(la, wm * 128 + x * 32, 0);
-            bf[x] = frag(lb, wn * 128 + x * 32, 0);
+        for (int i = 0; i < 16; ++i) {
+            const int x = i >> 2, y = i & 3;
+            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[y], af[x], acc[x][y], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (reads && i < kReads) {
+                const int op = i / (4 * kRPF), xb = (i % (4 * kRPF)) / kRPF, h = i % kRPF;
+                const LDS char *a = stage_next + fo[ks_next][op][xb][h];
+                if (KIND == JOB_DX)
+                    (op == 0 ? an : bn)[xb] = read_rc(a);
+                else
+                    tr[op][xb][h] = read_tr(a);
+            }
+            if (ds >= 0 && i >= 12 && i < 12 + kDmaPerOp / 2)
+                dma(ds, dp0 + (i - 12));
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        if (KIND == JOB_DW && reads) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            // one scheduling region per k-step: the next step's fragment reads and a
-            // quarter of the next slab's DMA are interleaved with this step's 16 MFMAs
+            for (int xb = 0; xb < 4; ++xb) {
+                an[xb] = __builtin_shufflevector(tr[0][xb][0], tr[0][xb][1], 0, 1, 2, 3, 4, 5, 6, 7);
+                bn[xb] = __builtin_shufflevector(tr[1][xb][0], tr[1][xb][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+    };
+
+    if (nslab > 0) {
+        for (int s = 0; s < kStages - 1 && s < nslab; ++s)
+#pragma unroll
+            for (int p = 0; p < kDmaPerOp; ++p)
+                dma(s, p);
+        // slab 0 visible to all waves; later slabs may stay in flight
+        dma_wait(kDmaPerSlab * (min(nslab, kStages - 1) - 1));
+        slab_barrier();
+        bf16x8_t af[4], bf[4], an[4], bn[4];
+        {
+            bf16x4_t tr[2][4][2];
+#pragma unroll
+            for (int op = 0; op < 2; ++op)
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+#pragma unroll
+                    for (int h = 0; h < kRPF; ++h) {
+                        const LDS char *a = smem + fo[0][op][x][h];
+                        if (KIND == JOB_DX)
+                            (op == 0 ? af : bf)[x] = read_rc(a);
+                        else
+                            tr[op][x][h] = read_tr(a);
+                    }
             if (KIND == JOB_DW)
-                lgkm_wait(af, bf); // the asm transposing reads of this step's fragments
-            bf16x8_t an[4], bn[4];
-            if (ks + 1 < 4) {
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    an[x] = frag(la, wm * 128 + x * 32, ks + 1);
-                    bn[x] = frag(lb, wn * 128 + x * 32, ks + 1);
+                    af[x] = __builtin_shufflevector(tr[0][x][0], tr[0][x][1], 0, 1, 2, 3, 4, 5, 6, 7);
+                    bf[x] = __builtin_shufflevector(tr[1][x][0], tr[1][x][1], 0, 1, 2, 3, 4, 5, 6, 7);
                 }
-            }
-            if (more) {
-                if (ks == 0) issue(s + 1, std::integral_constant<int, 0>{}, C2{});
-                if (ks == 1) issue(s + 1, std::integral_constant<int, 2>{}, C2{});
-                if (ks == 2) issue(s + 1, std::integral_constant<int, 4>{}, C2{});
-                if (ks == 3) issue(s + 1, std::integral_constant<int, 6>{}, C2{});
-            }
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-#pragma unroll
-                for (int y = 0; y < 4; ++y)
-                    acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[y], af[x], acc[x][y], 0, 0, 0);
-            if (ks + 1 < 4) {
-                // 8 fragments = 8 (RC) or 16 (OC) LDS reads spread over the 16 MFMAs
-#pragma unroll
-                for (int i = 0; i < 8 * kReadsPerFrag; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 16 / (8 * kReadsPerFrag), 0); // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        // DS read
-                }
+        }
+        for (int s = 0; s < nslab; ++s) {
+            // Slab s: k-step 0 (region A), then the barrier that opens slab s+1,
+            // then k-step 1 (region B), which already reads slab s+1's first
+            // fragments.  DMA of slab s+3 fills the buffer of slab s-1, which every
+            // wave stopped reading before the barrier that opened slab s.
+            const bool more = s + kStages - 1 < nslab;
+            const bool next = s + 1 < nslab;
+            const LDS char *cur = smem + (s % kStages) * kStageBytes;
+            if (KIND == JOB_DW)
+                lgkm_wait(af, bf);
+            __builtin_amdgcn_sched_barrier(0);
+            kstep(af, bf, cur, 1, an, bn, true, more ? s + kStages - 1 : -1, 0);
+            if (next) {
+                // slab s+1's DMA came before slab s+2's (8, if any) and the first
+                // half of slab s+3's (4, if any)
+                dma_wait((s + 2 < nslab ? kDmaPerSlab : 0) + (more ? kDmaPerOp : 0));
+                slab_barrier();
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (ks + 1 < 4) {
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    af[x] = an[x];
-                    bf[x] = bn[x];
-                }
-            }
+            if (KIND == JOB_DW)
+                lgkm_wait(an, bn);
+            __builtin_amdgcn_sched_barrier(0);
+            kstep(an, bn, smem + ((s + 1) % kStages) * kStageBytes, 0, af, bf, next,
+                  more ? s + kStages - 1 : -1, kDmaPerOp / 2);
         }
     }
 
