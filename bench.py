@@ -55,6 +55,42 @@ def _sync():
     torch.cuda.synchronize()
 
 
+KERNEL_SOURCES = {"k_lin_bwd_mfma": "linear_layer_backward_bwd_amd/csrc/lin_bwd.hip",
+                  "k_adamw": "linear_layer_backward_bwd_amd/csrc/adamw.hip"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash(kernel):
+    import hashlib
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a copy
+    kernel of known size), as recorded in profiles/traffic.json -- or None when there is no
+    record for this kernel and workload or the kernel's source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel][workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def copy_calibration(steps):
+    """A plain copy of exactly 1 GiB, `steps` times: the reference for scaling counter bytes."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    _sync()
+    return {"copy_bytes_per_launch": 1 << 30, "launches": steps}
+
+
 class Timer:
     """HIP events on the current (launch) stream around each launch of the timed steps."""
 
@@ -142,6 +178,7 @@ def bench_block(steps, warmup, seed):
                         "per_projection": per_proj},
             "adamw": {"ms": round(adamw_ms, 4), "gbps": round(adamw_gbps, 1),
                       "frac_of_peak": round(adamw_gbps / PEAK_HBM_GBPS, 4),
+                      "traffic": recorded_traffic("k_adamw", "block_bwd_update_M16384_D4096"),
                       "gparams_per_s": round(n_params / (adamw_ms * 1e-3) / 1e9, 2),
                       "bytes_per_param": ADAMW_BYTES_16BIT_GRAD},
         },
@@ -149,7 +186,9 @@ def bench_block(steps, warmup, seed):
                      "achieved": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": recorded_traffic("k_lin_bwd_mfma", "block_bwd_update_M16384_D4096"),
+                     "algorithmic_bytes_per_launch": sum(lin_bwd_min_bytes(c.M, c.K, c.N)
+                                                         for c in cases) / len(cases),
                      "per_launch_flops": gemm_flops / len(cases),
                      "launch_ms": round(gemm_ms / len(cases), 4)},
     }
@@ -264,8 +303,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the M=32 / M=2048 / 2^28-param AdamW figures")
-    ap.add_argument("--only", choices=["block", "m32", "m2048", "adamw"], default=None,
-                    help="time one workload only (for profiling)")
+    ap.add_argument("--only", choices=["block", "m32", "m2048", "adamw", "copycal"], default=None,
+                    help="time one workload only (for profiling); copycal = 1 GiB copies for "
+                         "scaling HBM byte counters")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus %d is not supported "
@@ -285,6 +325,9 @@ def main(argv=None):
     if args.only == "adamw":
         print(json.dumps(bench_adamw(1 << 28, args.steps, args.warmup, args.seed)), flush=True)
         return 0
+    if args.only == "copycal":
+        print(json.dumps(copy_calibration(args.steps)), flush=True)
+        return 0
 
     print("bench: block workload, warmup %d, steps %d" % (args.warmup, args.steps),
           file=sys.stderr, flush=True)
@@ -294,6 +337,9 @@ def main(argv=None):
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded normal draws on the GPU; random-init weights)",
            "config": res["config"], "parts": res["parts"], "roofline": res["roofline"]}
+    if args.only == "block":
+        print(json.dumps(out), flush=True)
+        return 0
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle on a bounded sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cases, opt)
