@@ -187,7 +187,13 @@ __device__ __forceinline__ void lgkm_wait(bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
 // Wait until at most `n` of this wave's DMA instructions are still in flight
 // (DMA completes in issue order).
 __device__ __forceinline__ void dma_wait(int n) {
-    if (n >= 16)
+    if (n >= 28)
+        asm volatile("s_waitcnt vmcnt(28)" ::: "memory");
+    else if (n >= 24)
+        asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else if (n >= 20)
+        asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+    else if (n >= 16)
         asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     else if (n >= 12)
         asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
@@ -226,7 +232,7 @@ __device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, i
 
 template <int KIND>
 __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS char *smem) {
-    static_assert(kKSteps == 2 && kStages == 4 && kDmaPerOp == 4, "pipeline below assumes 2 k-steps, 4 stages");
+    static_assert(kKSteps == 2 && kDmaPerOp == 4 && kStages == 4, "pipeline below assumes 2 k-steps, 4 stages");
     constexpr int kRPF = KIND == JOB_DX ? 1 : 2; // LDS reads per fragment
     constexpr int kReads = 8 * kRPF;             // LDS reads per k-step (4 A + 4 B fragments)
     constexpr int kDmaPerSlab = 2 * kDmaPerOp;
@@ -235,7 +241,7 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
     const int64_t i0 = (int64_t)ti * kTile;
     const int64_t j0 = (int64_t)tj * kTile;
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // wave-uniform
     const int wm = w >> 1, wn = w & 1;
 
     // slab-independent per-lane offsets: DMA sources and LDS fragment addresses
@@ -270,41 +276,56 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
 
     const int nslab = (int)((jb.R + kBK - 1) / kBK);
     const bool rc_tail = KIND == JOB_DX && (jb.R % kBK) != 0;
+    // per-slab source advance (elements) of each operand
+    const int64_t step_a = KIND == JOB_DX ? kBK : (int64_t)kBK * jb.lda;
+    const int64_t step_b = KIND == JOB_DX ? kBK : (int64_t)kBK * jb.ldb;
+    LDS char *const wdst = smem + w * kDmaPerOp * 1024; // this wave's DMA destinations
 
-    // DMA instruction p (of kDmaPerOp) of both operands for slab s.  The buffer
-    // descriptor's base advances to the slab (scalar work only); for OC its size
-    // shrinks to the rows left, so rows past R read as zero.
-    auto dma = [&](int s, int p) {
-        LDS char *st = smem + (s % kStages) * kStageBytes + (w * kDmaPerOp + p) * 1024;
+    // Buffer descriptors for slab s: the base advances to the slab (scalar work
+    // only); for OC the size shrinks to the rows left, so rows past R read zero.
+    struct SlabSrc {
+        __amdgpu_buffer_rsrc_t a, b;
+    };
+    auto slab_src = [&](int s) {
         const int64_t r0 = (int64_t)s * kBK;
+        SlabSrc r;
         if (KIND == JOB_DX) {
-            if (rc_tail && s == nslab - 1) {
-                dma16(make_rsrc(jb.a, jb.a_bytes), st, dma_rc_tail_off(p, jb.lda, jb.I, jb.R, i0, r0, w, lane));
-                dma16(make_rsrc(jb.b, jb.b_bytes), st + kOperandBytes,
-                      dma_rc_tail_off(p, jb.ldb, jb.J, jb.R, j0, r0, w, lane));
-            } else {
-                dma16(make_rsrc(jb.a + r0, jb.a_bytes - (uint32_t)(2 * r0)), st, va[p]);
-                dma16(make_rsrc(jb.b + r0, jb.b_bytes - (uint32_t)(2 * r0)), st + kOperandBytes, vb[p]);
-            }
+            r.a = make_rsrc(jb.a + s * step_a, jb.a_bytes - (uint32_t)(2 * r0));
+            r.b = make_rsrc(jb.b + s * step_b, jb.b_bytes - (uint32_t)(2 * r0));
         } else {
-            dma16(make_rsrc(jb.a + r0 * jb.lda, (uint32_t)(2 * (jb.R - r0) * jb.lda)), st, va[p]);
-            dma16(make_rsrc(jb.b + r0 * jb.ldb, (uint32_t)(2 * (jb.R - r0) * jb.ldb)), st + kOperandBytes, vb[p]);
+            r.a = make_rsrc(jb.a + s * step_a, (uint32_t)(2 * (jb.R - r0) * jb.lda));
+            r.b = make_rsrc(jb.b + s * step_b, (uint32_t)(2 * (jb.R - r0) * jb.ldb));
+        }
+        return r;
+    };
+    // DMA instruction p of both operands for slab s (TAIL: the partial last RC slab)
+    auto dma = [&](const SlabSrc &src, int s, int p, bool tail) {
+        LDS char *st = wdst + (s % kStages) * kStageBytes + p * 1024;
+        if (tail) {
+            const int64_t r0 = (int64_t)s * kBK;
+            dma16(make_rsrc(jb.a, jb.a_bytes), st, dma_rc_tail_off(p, jb.lda, jb.I, jb.R, i0, r0, w, lane));
+            dma16(make_rsrc(jb.b, jb.b_bytes), st + kOperandBytes,
+                  dma_rc_tail_off(p, jb.ldb, jb.J, jb.R, j0, r0, w, lane));
+        } else {
+            dma16(src.a, st, va[p]);
+            dma16(src.b, st + kOperandBytes, vb[p]);
         }
     };
 
     // One k-step: 16 MFMAs on (af, bf), each followed by at most one LDS read of
-    // the next fragments into (an, bn) and, in the last slots, one DMA
-    // instruction pair of slab `ds` (if ds >= 0).  sched_barrier pins the order
-    // so the matrix pipe never waits behind a run of address or memory work.
-    auto kstep = [&](bf16x8_t (&af)[4], bf16x8_t (&bf)[4], const LDS char *stage_next, int ks_next,
-                     bf16x8_t (&an)[4], bf16x8_t (&bn)[4], bool reads, int ds, int dp0) {
+    // the next fragments into (an, bn) and, in slots 12-13, one DMA instruction
+    // pair of slab ds.  sched_barrier pins the order so the matrix pipe never
+    // waits behind a run of address or memory work.
+    auto kstep = [&](bf16x8_t(&af)[4], bf16x8_t(&bf)[4], const LDS char *stage_next, int ks_next,
+                     bf16x8_t(&an)[4], bf16x8_t(&bn)[4], bool R, bool D, bool tail,
+                     const SlabSrc &src, int ds, int dp0) {
         bf16x4_t tr[2][4][2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int x = i >> 2, y = i & 3;
             acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[y], af[x], acc[x][y], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if (reads && i < kReads) {
+            if (R && i < kReads) {
                 const int op = i / (4 * kRPF), xb = (i % (4 * kRPF)) / kRPF, h = i % kRPF;
                 const LDS char *a = stage_next + fo[ks_next][op][xb][h];
                 if (KIND == JOB_DX)
@@ -312,11 +333,11 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
                 else
                     tr[op][xb][h] = read_tr(a);
             }
-            if (ds >= 0 && i >= 12 && i < 12 + kDmaPerOp / 2)
-                dma(ds, dp0 + (i - 12));
+            if (D && i >= 12 && i < 12 + kDmaPerOp / 2)
+                dma(src, ds, dp0 + (i - 12), tail);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (KIND == JOB_DW && reads) {
+        if (KIND == JOB_DW && R) {
 #pragma unroll
             for (int xb = 0; xb < 4; ++xb) {
                 an[xb] = __builtin_shufflevector(tr[0][xb][0], tr[0][xb][1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -325,15 +346,44 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
         }
     };
 
+    bf16x8_t af[4], bf[4], an[4], bn[4];
+    // Slab s: k-step 0 (region A), then -- if there is a slab s+1 -- the barrier
+    // that opens it, then k-step 1 (region B), which already reads slab s+1's
+    // first fragments.  DMA of slab s+3 fills the buffer of slab s-1, which every
+    // wave stopped reading before the barrier that opened slab s.  wait_n: this
+    // wave's DMA instructions issued after slab s+1's.
+    // Called with constant flags in the steady state (inlining folds them away)
+    // and with run-time flags in the few peeled and draining iterations.
+    auto slab = [&](int s, bool dmas, bool tail, bool N, int wait_n) {
+        const SlabSrc src = dmas ? slab_src(s + kStages - 1) : SlabSrc{};
+        const LDS char *cur = smem + (s % kStages) * kStageBytes;
+        if (KIND == JOB_DW)
+            lgkm_wait(af, bf);
+        __builtin_amdgcn_sched_barrier(0);
+        kstep(af, bf, cur, 1, an, bn, true, dmas, tail, src, s + kStages - 1, 0);
+        if (N) {
+            dma_wait(wait_n);
+            slab_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (KIND == JOB_DW)
+            lgkm_wait(an, bn);
+        __builtin_amdgcn_sched_barrier(0);
+        kstep(an, bn, smem + ((s + 1) % kStages) * kStageBytes, 0, af, bf, N, dmas, tail, src,
+              s + kStages - 1, kDmaPerOp / 2);
+    };
+
     if (nslab > 0) {
-        for (int s = 0; s < kStages - 1 && s < nslab; ++s)
+        for (int s = 0; s < kStages - 1 && s < nslab; ++s) {
+            const SlabSrc src = slab_src(s);
+            const bool tail = rc_tail && s == nslab - 1;
 #pragma unroll
             for (int p = 0; p < kDmaPerOp; ++p)
-                dma(s, p);
+                dma(src, s, p, tail);
+        }
         // slab 0 visible to all waves; later slabs may stay in flight
         dma_wait(kDmaPerSlab * (min(nslab, kStages - 1) - 1));
         slab_barrier();
-        bf16x8_t af[4], bf[4], an[4], bn[4];
         {
             bf16x4_t tr[2][4][2];
 #pragma unroll
@@ -355,30 +405,17 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
                     bf[x] = __builtin_shufflevector(tr[1][x][0], tr[1][x][1], 0, 1, 2, 3, 4, 5, 6, 7);
                 }
         }
-        for (int s = 0; s < nslab; ++s) {
-            // Slab s: k-step 0 (region A), then the barrier that opens slab s+1,
-            // then k-step 1 (region B), which already reads slab s+1's first
-            // fragments.  DMA of slab s+3 fills the buffer of slab s-1, which every
-            // wave stopped reading before the barrier that opened slab s.
-            const bool more = s + kStages - 1 < nslab;
+        // steady state: DMA of a slab that is not the last one, branch free
+        int s = 0;
+        for (; s < nslab - kStages; ++s)
+            slab(s, true, false, true, kDmaPerSlab + kDmaPerOp);
+        // the iteration that issues the last slab (partial for RC when R % kBK != 0),
+        // then the draining ones, which issue no DMA
+        for (; s < nslab; ++s) {
+            const bool dmas = s + kStages - 1 < nslab;
             const bool next = s + 1 < nslab;
-            const LDS char *cur = smem + (s % kStages) * kStageBytes;
-            if (KIND == JOB_DW)
-                lgkm_wait(af, bf);
-            __builtin_amdgcn_sched_barrier(0);
-            kstep(af, bf, cur, 1, an, bn, true, more ? s + kStages - 1 : -1, 0);
-            if (next) {
-                // slab s+1's DMA came before slab s+2's (8, if any) and the first
-                // half of slab s+3's (4, if any)
-                dma_wait((s + 2 < nslab ? kDmaPerSlab : 0) + (more ? kDmaPerOp : 0));
-                slab_barrier();
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if (KIND == JOB_DW)
-                lgkm_wait(an, bn);
-            __builtin_amdgcn_sched_barrier(0);
-            kstep(an, bn, smem + ((s + 1) % kStages) * kStageBytes, 0, af, bf, next,
-                  more ? s + kStages - 1 : -1, kDmaPerOp / 2);
+            const int full = max(0, min(s + kStages - 2, nslab - 1) - (s + 1));
+            slab(s, dmas, dmas && rc_tail, next, kDmaPerSlab * full + (dmas ? kDmaPerOp : 0));
         }
     }
 
