@@ -43,6 +43,7 @@ constexpr int kStages = 4;                        // LDS ring: 3 slabs in flight
 constexpr int kThreads = 256;                     // 4 waves, 2x2, 128x128 each
 constexpr int kOperandBytes = kTile * kBK * 2;    // one operand slab in LDS: 16 KiB
 constexpr int kStageBytes = 2 * kOperandBytes;    // A and B
+constexpr int kBOffset = kStages * kOperandBytes;  // all A slabs first, then all B slabs
 constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
 constexpr int kKSteps = kBK / 16;                 // MFMA k-steps per slab
 constexpr int kDmaPerOp = kBK / 8;                // DMA instructions per wave per operand per slab
@@ -173,6 +174,14 @@ __device__ __forceinline__ bf16x4_t read_tr(const LDS char *p) {
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(p));
     return v;
 }
+// Same, with a constant byte offset carried in the instruction's immediate field.
+template <int OFF>
+__device__ __forceinline__ bf16x4_t read_tr_off(const LDS char *p) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+    bf16x4_t v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(p), "n"(OFF));
+    return v;
+}
 
 // Wait for all of this wave's LDS reads; the fragments are threaded through the
 // asm so no MFMA that consumes them can be scheduled above the wait.
@@ -234,7 +243,6 @@ template <int KIND>
 __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS char *smem) {
     static_assert(kKSteps == 2 && kDmaPerOp == 4 && kStages == 4, "pipeline below assumes 2 k-steps, 4 stages");
     constexpr int kRPF = KIND == JOB_DX ? 1 : 2; // LDS reads per fragment
-    constexpr int kReads = 8 * kRPF;             // LDS reads per k-step (4 A + 4 B fragments)
     constexpr int kDmaPerSlab = 2 * kDmaPerOp;
     int ti, tj;
     tile_coords(jb, t_index, ti, tj);
@@ -260,10 +268,10 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
             for (int h = 0; h < kRPF; ++h) {
                 if (KIND == JOB_DX) {
                     fo[ks][0][x][h] = frag_off_rc(wm * 128 + x * 32, ks, lane);
-                    fo[ks][1][x][h] = kOperandBytes + frag_off_rc(wn * 128 + x * 32, ks, lane);
+                    fo[ks][1][x][h] = kBOffset + frag_off_rc(wn * 128 + x * 32, ks, lane);
                 } else {
                     fo[ks][0][x][h] = frag_off_oc(wm * 128 + x * 32, ks, lane, h);
-                    fo[ks][1][x][h] = kOperandBytes + frag_off_oc(wn * 128 + x * 32, ks, lane, h);
+                    fo[ks][1][x][h] = kBOffset + frag_off_oc(wn * 128 + x * 32, ks, lane, h);
                 }
             }
 
@@ -300,23 +308,23 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
     };
     // DMA instruction p of both operands for slab s (TAIL: the partial last RC slab)
     auto dma = [&](const SlabSrc &src, int s, int p, bool tail) {
-        LDS char *st = wdst + (s % kStages) * kStageBytes + p * 1024;
+        LDS char *st = wdst + (s % kStages) * kOperandBytes + p * 1024;
         if (tail) {
             const int64_t r0 = (int64_t)s * kBK;
             dma16(make_rsrc(jb.a, jb.a_bytes), st, dma_rc_tail_off(p, jb.lda, jb.I, jb.R, i0, r0, w, lane));
-            dma16(make_rsrc(jb.b, jb.b_bytes), st + kOperandBytes,
+            dma16(make_rsrc(jb.b, jb.b_bytes), st + kBOffset,
                   dma_rc_tail_off(p, jb.ldb, jb.J, jb.R, j0, r0, w, lane));
         } else {
             dma16(src.a, st, va[p]);
-            dma16(src.b, st + kOperandBytes, vb[p]);
+            dma16(src.b, st + kBOffset, vb[p]);
         }
     };
 
-    // One k-step: 16 MFMAs on (af, bf), each followed by at most one LDS read of
-    // the next fragments into (an, bn) and, in slots 12-13, one DMA instruction
-    // pair of slab ds.  sched_barrier pins the order so the matrix pipe never
-    // waits behind a run of address or memory work.
-    auto kstep = [&](bf16x8_t(&af)[4], bf16x8_t(&bf)[4], const LDS char *stage_next, int ks_next,
+    // One k-step: 16 MFMAs on (af, bf); after each of the first 8, the LDS read(s)
+    // of one next fragment into (an, bn), and after MFMAs 12-13 one DMA
+    // instruction pair of slab ds.  sched_barrier pins the order so the matrix
+    // pipe never waits behind a run of address or memory work.
+    auto kstep = [&](bf16x8_t(&af)[4], bf16x8_t(&bf)[4], auto stage_next, int ks_next,
                      bf16x8_t(&an)[4], bf16x8_t(&bn)[4], bool R, bool D, bool tail,
                      const SlabSrc &src, int ds, int dp0) {
         bf16x4_t tr[2][4][2];
@@ -325,13 +333,27 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
             const int x = i >> 2, y = i & 3;
             acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[y], af[x], acc[x][y], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if (R && i < kReads) {
-                const int op = i / (4 * kRPF), xb = (i % (4 * kRPF)) / kRPF, h = i % kRPF;
-                const LDS char *a = stage_next + fo[ks_next][op][xb][h];
-                if (KIND == JOB_DX)
-                    (op == 0 ? an : bn)[xb] = read_rc(a);
-                else
-                    tr[op][xb][h] = read_tr(a);
+            // LDS reads go in the first 8 slots (two per slot for the transposing
+            // reads) so they complete long before the wait at the next region
+#pragma unroll
+            for (int j = kRPF * i; j < kRPF * (i + 1); ++j) {
+                if (!R || i >= 8)
+                    break;
+                const int op = j / (4 * kRPF), xb = (j % (4 * kRPF)) / kRPF, h = j % kRPF;
+                const LDS char *lane_base = smem + fo[ks_next][op][xb][h];
+                if constexpr (std::is_integral_v<decltype(stage_next)>) {
+                    const LDS char *a = lane_base + stage_next * kOperandBytes;
+                    if (KIND == JOB_DX)
+                        (op == 0 ? an : bn)[xb] = read_rc(a);
+                    else
+                        tr[op][xb][h] = read_tr(a);
+                } else {
+                    constexpr int off = decltype(stage_next)::value * kOperandBytes;
+                    if (KIND == JOB_DX)
+                        (op == 0 ? an : bn)[xb] = read_rc(lane_base + off);
+                    else
+                        tr[op][xb][h] = read_tr_off<off>(lane_base);
+                }
             }
             if (D && i >= 12 && i < 12 + kDmaPerOp / 2)
                 dma(src, ds, dp0 + (i - 12), tail);
@@ -354,13 +376,20 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
     // wave's DMA instructions issued after slab s+1's.
     // Called with constant flags in the steady state (inlining folds them away)
     // and with run-time flags in the few peeled and draining iterations.
-    auto slab = [&](int s, bool dmas, bool tail, bool N, int wait_n) {
+    // stage: the ring slot of slab s, as a compile-time constant (unrolled steady
+    // state) or an int; the next slab's slot is derived the same way.
+    auto next_stage = [](auto st) {
+        if constexpr (std::is_integral_v<decltype(st)>)
+            return (st + 1) % kStages;
+        else
+            return std::integral_constant<int, (decltype(st)::value + 1) % kStages>{};
+    };
+    auto slab = [&](int s, auto stage, bool dmas, bool tail, bool N, int wait_n) {
         const SlabSrc src = dmas ? slab_src(s + kStages - 1) : SlabSrc{};
-        const LDS char *cur = smem + (s % kStages) * kStageBytes;
         if (KIND == JOB_DW)
             lgkm_wait(af, bf);
         __builtin_amdgcn_sched_barrier(0);
-        kstep(af, bf, cur, 1, an, bn, true, dmas, tail, src, s + kStages - 1, 0);
+        kstep(af, bf, stage, 1, an, bn, true, dmas, tail, src, s + kStages - 1, 0);
         if (N) {
             dma_wait(wait_n);
             slab_barrier();
@@ -369,8 +398,7 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
         if (KIND == JOB_DW)
             lgkm_wait(an, bn);
         __builtin_amdgcn_sched_barrier(0);
-        kstep(an, bn, smem + ((s + 1) % kStages) * kStageBytes, 0, af, bf, N, dmas, tail, src,
-              s + kStages - 1, kDmaPerOp / 2);
+        kstep(an, bn, next_stage(stage), 0, af, bf, N, dmas, tail, src, s + kStages - 1, kDmaPerOp / 2);
     };
 
     if (nslab > 0) {
@@ -407,15 +435,23 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
         }
         // steady state: DMA of a slab that is not the last one, branch free
         int s = 0;
+        // unrolled by the ring size so each stage offset is a constant that folds
+        // into the LDS instructions' immediate offsets
+        for (; s + kStages - 1 < nslab - kStages; s += kStages) {
+            slab(s + 0, std::integral_constant<int, 0>{}, true, false, true, kDmaPerSlab + kDmaPerOp);
+            slab(s + 1, std::integral_constant<int, 1>{}, true, false, true, kDmaPerSlab + kDmaPerOp);
+            slab(s + 2, std::integral_constant<int, 2>{}, true, false, true, kDmaPerSlab + kDmaPerOp);
+            slab(s + 3, std::integral_constant<int, 3>{}, true, false, true, kDmaPerSlab + kDmaPerOp);
+        }
         for (; s < nslab - kStages; ++s)
-            slab(s, true, false, true, kDmaPerSlab + kDmaPerOp);
+            slab(s, s % kStages, true, false, true, kDmaPerSlab + kDmaPerOp);
         // the iteration that issues the last slab (partial for RC when R % kBK != 0),
         // then the draining ones, which issue no DMA
         for (; s < nslab; ++s) {
             const bool dmas = s + kStages - 1 < nslab;
             const bool next = s + 1 < nslab;
             const int full = max(0, min(s + kStages - 2, nslab - 1) - (s + 1));
-            slab(s, dmas, dmas && rc_tail, next, kDmaPerSlab * full + (dmas ? kDmaPerOp : 0));
+            slab(s, s % kStages, dmas, dmas && rc_tail, next, kDmaPerSlab * full + (dmas ? kDmaPerOp : 0));
         }
     }
 
