@@ -96,6 +96,9 @@ struct TileJob {
     uint32_t a_bytes, b_bytes; // operand sizes (each < 2 GiB on this path)
     int tiles_i, tiles_j, ntiles;
     int kind;          // JOB_DX: RC operands, bf16 out; JOB_DW: OC operands, fp32 out
+    // k rotation: the tile at (ti, tj) walks the slabs starting at
+    // (rot_i*(ti%4) + rot_j*(tj%8)) mod nslab (0 for a ragged RC reduction)
+    int rot_i, rot_j;
 };
 
 struct MfmaParams {
@@ -163,12 +166,22 @@ __device__ __forceinline__ int frag_off_oc(int ob, int ks, int lane, int half) {
     return row * 512 + ((lc ^ swz_oc(row)) << 4) + (col & 7) * 2;
 }
 
+// LDS fragment reads are issued as inline asm: the compiler's wait insertion
+// treats them as aliasing the in-flight DMA into other stage buffers and would
+// stall on it, or would place a wait before every MFMA.  Callers wait for these
+// reads with lgkm_wait() before use.
 __device__ __forceinline__ bf16x8_t read_rc(const LDS char *p) {
-    return *reinterpret_cast<const LDS bf16x8_t *>(p);
+    bf16x8_t v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(p));
+    return v;
 }
-// Issued as inline asm: the compiler's wait insertion treats the builtin as
-// aliasing the in-flight DMA into other stage buffers and would stall on it.
-// Callers wait for these reads with lgkm_wait() before use.
+template <int OFF>
+__device__ __forceinline__ bf16x8_t read_rc_off(const LDS char *p) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+    bf16x8_t v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(p), "n"(OFF));
+    return v;
+}
 __device__ __forceinline__ bf16x4_t read_tr(const LDS char *p) {
     bf16x4_t v;
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(p));
@@ -284,6 +297,12 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
 
     const int nslab = (int)((jb.R + kBK - 1) / kBK);
     const bool rc_tail = KIND == JOB_DX && (jb.R % kBK) != 0;
+    // Tiles that run together on one XCD start the reduction at different
+    // slabs.  With RC operands whose rows are a large power of two of bytes
+    // apart, all rows of every concurrent tile otherwise share their low
+    // address bits and crowd into a few L2 sets.  (The sum is the same set of
+    // slab products taken in a rotated order.)
+    const int rot = rc_tail || nslab == 0 ? 0 : (jb.rot_i * (ti & 3) + jb.rot_j * (tj & 7)) % nslab;
     // per-slab source advance (elements) of each operand
     const int64_t step_a = KIND == JOB_DX ? kBK : (int64_t)kBK * jb.lda;
     const int64_t step_b = KIND == JOB_DX ? kBK : (int64_t)kBK * jb.ldb;
@@ -295,6 +314,8 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
         __amdgpu_buffer_rsrc_t a, b;
     };
     auto slab_src = [&](int s) {
+        s += rot;
+        s = s >= nslab ? s - nslab : s;
         const int64_t r0 = (int64_t)s * kBK;
         SlabSrc r;
         if (KIND == JOB_DX) {
@@ -350,7 +371,7 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
                 } else {
                     constexpr int off = decltype(stage_next)::value * kOperandBytes;
                     if (KIND == JOB_DX)
-                        (op == 0 ? an : bn)[xb] = read_rc(lane_base + off);
+                        (op == 0 ? an : bn)[xb] = read_rc_off<off>(lane_base);
                     else
                         tr[op][xb][h] = read_tr_off<off>(lane_base);
                 }
@@ -371,34 +392,42 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
     bf16x8_t af[4], bf[4], an[4], bn[4];
     // Slab s: k-step 0 (region A), then -- if there is a slab s+1 -- the barrier
     // that opens it, then k-step 1 (region B), which already reads slab s+1's
-    // first fragments.  DMA of slab s+3 fills the buffer of slab s-1, which every
-    // wave stopped reading before the barrier that opened slab s.  wait_n: this
-    // wave's DMA instructions issued after slab s+1's.
+    // first fragments.  After the barrier in slab s no wave reads slab s's ring
+    // slot any more, so the DMA of slab s+4 may start in region B.
+    //   early (RC): region A issues the second half of slab s+3, region B the
+    //               first half of slab s+4 -- one k-step more lead, which the
+    //               64-byte row segments of RC slabs need;
+    //   otherwise:  regions A and B issue the two halves of slab s+3.
+    // wait_n: this wave's DMA instructions issued after slab s+1's.
     // Called with constant flags in the steady state (inlining folds them away)
     // and with run-time flags in the few peeled and draining iterations.
     // stage: the ring slot of slab s, as a compile-time constant (unrolled steady
     // state) or an int; the next slab's slot is derived the same way.
+    constexpr bool kEarly = KIND == JOB_DX;
+    constexpr int kAheadB = kEarly ? kStages : kStages - 1; // slab whose DMA region B issues
+    constexpr int kHalf = kDmaPerOp / 2;
     auto next_stage = [](auto st) {
         if constexpr (std::is_integral_v<decltype(st)>)
             return (st + 1) % kStages;
         else
             return std::integral_constant<int, (decltype(st)::value + 1) % kStages>{};
     };
-    auto slab = [&](int s, auto stage, bool dmas, bool tail, bool N, int wait_n) {
-        const SlabSrc src = dmas ? slab_src(s + kStages - 1) : SlabSrc{};
-        if (KIND == JOB_DW)
-            lgkm_wait(af, bf);
+    auto slab = [&](int s, auto stage, bool dA, bool tA, bool dB, bool tB, bool N, int wait_n) {
+        const SlabSrc srcA = dA ? slab_src(s + kStages - 1) : SlabSrc{};
+        SlabSrc srcB = srcA;
+        if constexpr (kEarly)
+            srcB = dB ? slab_src(s + kStages) : SlabSrc{};
+        lgkm_wait(af, bf);
         __builtin_amdgcn_sched_barrier(0);
-        kstep(af, bf, stage, 1, an, bn, true, dmas, tail, src, s + kStages - 1, 0);
+        kstep(af, bf, stage, 1, an, bn, true, dA, tA, srcA, s + kStages - 1, kEarly ? kHalf : 0);
         if (N) {
             dma_wait(wait_n);
             slab_barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (KIND == JOB_DW)
-            lgkm_wait(an, bn);
+        lgkm_wait(an, bn);
         __builtin_amdgcn_sched_barrier(0);
-        kstep(an, bn, next_stage(stage), 0, af, bf, N, dmas, tail, src, s + kStages - 1, kDmaPerOp / 2);
+        kstep(an, bn, next_stage(stage), 0, af, bf, N, dB, tB, srcB, s + kAheadB, kEarly ? 0 : kHalf);
     };
 
     if (nslab > 0) {
@@ -409,8 +438,16 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
             for (int p = 0; p < kDmaPerOp; ++p)
                 dma(src, s, p, tail);
         }
+        const bool half3 = kEarly && nslab > kStages - 1; // early: first half of slab 3 as well
+        if (half3) {
+            const SlabSrc src = slab_src(kStages - 1);
+            const bool tail = rc_tail && kStages - 1 == nslab - 1;
+#pragma unroll
+            for (int p = 0; p < kHalf; ++p)
+                dma(src, kStages - 1, p, tail);
+        }
         // slab 0 visible to all waves; later slabs may stay in flight
-        dma_wait(kDmaPerSlab * (min(nslab, kStages - 1) - 1));
+        dma_wait(kDmaPerSlab * (min(nslab, kStages - 1) - 1) + (half3 ? kHalf * 2 : 0));
         slab_barrier();
         {
             bf16x4_t tr[2][4][2];
@@ -426,32 +463,55 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
                         else
                             tr[op][x][h] = read_tr(a);
                     }
-            if (KIND == JOB_DW)
+            if (KIND == JOB_DW) {
+                lgkm_wait(af, bf);
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     af[x] = __builtin_shufflevector(tr[0][x][0], tr[0][x][1], 0, 1, 2, 3, 4, 5, 6, 7);
                     bf[x] = __builtin_shufflevector(tr[1][x][0], tr[1][x][1], 0, 1, 2, 3, 4, 5, 6, 7);
                 }
+            }
         }
-        // steady state: DMA of a slab that is not the last one, branch free
+        // steady state: every DMA is of a full slab, branch free; unrolled by the
+        // ring size so each stage offset is a constant that folds into the LDS
+        // instructions' immediate offsets
         int s = 0;
-        // unrolled by the ring size so each stage offset is a constant that folds
-        // into the LDS instructions' immediate offsets
-        for (; s + kStages - 1 < nslab - kStages; s += kStages) {
-            slab(s + 0, std::integral_constant<int, 0>{}, true, false, true, kDmaPerSlab + kDmaPerOp);
-            slab(s + 1, std::integral_constant<int, 1>{}, true, false, true, kDmaPerSlab + kDmaPerOp);
-            slab(s + 2, std::integral_constant<int, 2>{}, true, false, true, kDmaPerSlab + kDmaPerOp);
-            slab(s + 3, std::integral_constant<int, 3>{}, true, false, true, kDmaPerSlab + kDmaPerOp);
-        }
-        for (; s < nslab - kStages; ++s)
-            slab(s, s % kStages, true, false, true, kDmaPerSlab + kDmaPerOp);
-        // the iteration that issues the last slab (partial for RC when R % kBK != 0),
-        // then the draining ones, which issue no DMA
-        for (; s < nslab; ++s) {
-            const bool dmas = s + kStages - 1 < nslab;
-            const bool next = s + 1 < nslab;
-            const int full = max(0, min(s + kStages - 2, nslab - 1) - (s + 1));
-            slab(s, s % kStages, dmas, dmas && rc_tail, next, kDmaPerSlab * full + (dmas ? kDmaPerOp : 0));
+        if constexpr (kEarly) {
+            constexpr int kW = 2 * kDmaPerSlab; // slabs s+2 and s+3 may be in flight
+            for (; s + 2 * kStages < nslab; s += kStages) {
+                slab(s + 0, std::integral_constant<int, 0>{}, true, false, true, false, true, kW);
+                slab(s + 1, std::integral_constant<int, 1>{}, true, false, true, false, true, kW);
+                slab(s + 2, std::integral_constant<int, 2>{}, true, false, true, false, true, kW);
+                slab(s + 3, std::integral_constant<int, 3>{}, true, false, true, false, true, kW);
+            }
+            for (; s + kStages + 1 < nslab; ++s)
+                slab(s, s % kStages, true, false, true, false, true, kW);
+            // the iterations that issue the last slab (partial when R % kBK != 0),
+            // then the draining ones, which issue no DMA
+            for (; s < nslab; ++s) {
+                const bool dA = s + kStages - 1 < nslab, dB = s + kStages < nslab;
+                const bool tA = dA && rc_tail && s + kStages - 1 == nslab - 1;
+                const bool tB = dB && rc_tail && s + kStages == nslab - 1;
+                const int w = kDmaPerSlab * ((s + 2 < nslab) + (s + 3 < nslab));
+                slab(s, s % kStages, dA, tA, dB, tB, s + 1 < nslab, w);
+            }
+        } else {
+            constexpr int kW = kDmaPerSlab + kDmaPerOp; // slab s+2 and half of s+3
+            for (; s + kStages - 1 < nslab - kStages; s += kStages) {
+                slab(s + 0, std::integral_constant<int, 0>{}, true, false, true, false, true, kW);
+                slab(s + 1, std::integral_constant<int, 1>{}, true, false, true, false, true, kW);
+                slab(s + 2, std::integral_constant<int, 2>{}, true, false, true, false, true, kW);
+                slab(s + 3, std::integral_constant<int, 3>{}, true, false, true, false, true, kW);
+            }
+            for (; s < nslab - kStages; ++s)
+                slab(s, s % kStages, true, false, true, false, true, kW);
+            for (; s < nslab; ++s) {
+                const bool dmas = s + kStages - 1 < nslab;
+                const bool tail = dmas && rc_tail;
+                const int full = max(0, min(s + kStages - 2, nslab - 1) - (s + 1));
+                slab(s, s % kStages, dmas, tail, dmas, tail, s + 1 < nslab,
+                     kDmaPerSlab * full + (dmas ? kDmaPerOp : 0));
+            }
         }
     }
 
@@ -663,6 +723,8 @@ TileJob make_tile_job(int kind, const void *a, const void *b, void *c, int64_t I
     j.tiles_j = ceil_div(J, kTile);
     j.ntiles = j.tiles_i * j.tiles_j;
     j.kind = kind;
+    j.rot_i = 0;
+    j.rot_j = 0;
     return j;
 }
 
@@ -722,6 +784,16 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
     bool have_x = false, have_w = false;
     if (need_dx && !small_dx) {
         jx = make_tile_job(JOB_DX, a.dY, a.W, a.dX, a.M, a.K, a.N, a.N, a.N);
+        // Rows of both RC operands are 2N bytes apart.  When that is a multiple
+        // of 32 KiB, the same k of every row maps to one small group of L2 sets
+        // and the tiles running together on an XCD evict each other's lines;
+        // giving each of them its own starting slab spreads them out (measured
+        // on 16384x4096x16384: 860 -> 1090 TFLOP/s for dX).  Other strides are
+        // left alone: there the lockstep order shares lines in L2 best.
+        if ((2 * a.N) % 32768 == 0) {
+            jx.rot_i = 4;
+            jx.rot_j = 16;
+        }
         have_x = true;
     }
     if (need_dw) {
