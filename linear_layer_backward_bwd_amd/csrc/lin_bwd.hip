@@ -11,16 +11,17 @@
 //   dW[k,n] = Σ_m X[m,k]·dY[m,n]   i=k, j=n, r=m   A, B "outer-contiguous" (columns of X, dY)
 //
 // Kernels:
-//   k_lin_bwd_mfma   bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate), 256x256
-//                    output tile per 4-wave workgroup, reduction in slabs of 64 staged
-//                    through a double-buffered, XOR-swizzled LDS tile.  One launch runs
-//                    the tiles of both products; blocks are ordered longest reduction
-//                    first and mapped so that each XCD works on a compact group of tiles.
-//                    For dW the reduction index is the slow index of both operands; each
-//                    thread loads an 8x8 block (8 rows of 16 bytes) and transposes it in
-//                    registers before the LDS store, so LDS always holds tiles with the
-//                    reduction index contiguous and every MFMA operand is one 16-byte
-//                    LDS read.
+//   k_lin_bwd_mfma   bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulate), 256x256
+//                    output tile per 4-wave workgroup (128x128 per wave).  The reduction
+//                    runs in slabs of 32 that global->LDS DMA streams into a 4-slot,
+//                    XOR-swizzled LDS ring three slabs ahead of the MFMAs; one barrier
+//                    per slab.  For dX both operands are reduction-contiguous rows (one
+//                    16-byte LDS read per fragment); for dW the reduction index is the
+//                    slow index of both operands, and the transposing LDS read
+//                    (ds_read_b64_tr_b16) turns the row-major slab into MFMA fragments.
+//                    One launch runs the tiles of both products; blocks are ordered
+//                    longest reduction first and mapped so that each XCD works on a
+//                    compact group of tiles.
 //   k_dx_smallm      dX for M <= 64 (decode-like): bound by streaming W once, so the
 //                    reduction over n is split across the waves of a block and
 //                    operands go straight from global memory into MFMA registers.
@@ -45,7 +46,6 @@ constexpr int kOperandBytes = kTile * kBK * 2;    // one operand slab in LDS: 16
 constexpr int kStageBytes = 2 * kOperandBytes;    // A and B
 constexpr int kBOffset = kStages * kOperandBytes;  // all A slabs first, then all B slabs
 constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
-constexpr int kKSteps = kBK / 16;                 // MFMA k-steps per slab
 constexpr int kDmaPerOp = kBK / 8;                // DMA instructions per wave per operand per slab
 constexpr int kGroupI = 4;                        // tile rows per raster group
 constexpr uint32_t kOOB = 0x80000000u;            // buffer offset past num_records: reads 0
@@ -64,9 +64,9 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 //  RC ("reduction contiguous", dX operands dY and W): 128 lines of 128 B;
 //     line k holds the 32 r of output rows k (chunks 0-3) and k + 128
 //     (chunks 4-7), and 16-byte chunk c of line k is stored at chunk
-//     c ^ swz_rc(k).  An MFMA fragment (one ds_read_b128, 8 r values) then
-//     reads 32 consecutive lines at one chunk, which this swizzle serves
-//     without bank conflicts.
+//     c ^ swz_rc(k).  An MFMA fragment (one ds_read_b128, 8 r values per
+//     lane) reads 16 consecutive lines at each of four chunks; any 16
+//     consecutive lines at one chunk cover all banks under this swizzle.
 //  OC ("outer contiguous", dW operands X and dY): 32 rows (r) x 256 outer
 //     indices, 512 B per row; chunk c of row r is stored at chunk
 //     c ^ swz_oc(r).  MFMA fragment = two ds_read_b64_tr_b16: within each
@@ -76,8 +76,10 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 static_assert(kBK == 32, "the RC line layout packs two 32-deep rows per 128-byte line");
 __device__ __forceinline__ int swz_rc(int line) { return (line & 7) ^ ((line >> 3) & 7); }
 __device__ __forceinline__ int swz_oc(int row) {
-    // 32-byte segment s of row r moves to s ^ {0,3,5,6}[r & 3] (chunk pairs stay together)
-    return 2 * ((0x6530 >> (4 * (row & 3))) & 7);
+    // 32-byte segment s of row r moves to s ^ ((r & 3) | 4*((r >> 3) & 1)): the
+    // rows r..r+3 and r+8..r+11 that one 32-lane read touches land on eight
+    // different segments (chunk pairs stay together)
+    return 2 * ((row & 3) | (((row >> 3) & 1) << 2));
 }
 // LDS byte offset of 16-byte chunk c (0..3) of output row o (0..255) in an RC slab
 __device__ __forceinline__ int rc_off(int o, int c) {
@@ -152,16 +154,16 @@ __device__ __forceinline__ uint32_t dma_rc_tail_off(int p, int64_t ld, int64_t O
     return (o < O && r < R) ? (uint32_t)((o * ld + r) * 2) : kOOB;
 }
 
-// Per-lane LDS byte offsets (within an operand slab) of the fragment for outer
-// block ob (32 wide) at k-step ks: one ds_read_b128 (RC) or two
-// ds_read_b64_tr_b16 (OC, rows r and r+4 of the 4x16 transposing read).
-__device__ __forceinline__ int frag_off_rc(int ob, int ks, int lane) {
-    return rc_off(ob + (lane & 31), 2 * ks + (lane >> 5));
-}
-__device__ __forceinline__ int frag_off_oc(int ob, int ks, int lane, int half) {
+// Per-lane LDS byte offsets (within an operand slab) of the fragment for the
+// 16 outer indices ob..ob+15, all 32 r of the slab: lane l holds outer index
+// ob + l%16 and r = 8*(l/16) .. +7 (the operand layout of a 16x16x32 MFMA).
+// RC: one ds_read_b128.  OC: two ds_read_b64_tr_b16 (half h = r 4h..4h+3 of
+// each 8): each 16-lane group reads a 4-row x 16-column block.
+__device__ __forceinline__ int frag_off_rc(int ob, int lane) { return rc_off(ob + (lane & 15), lane >> 4); }
+__device__ __forceinline__ int frag_off_oc(int ob, int lane, int half) {
     const int g = lane >> 4, s = lane & 15;
-    const int row = ks * 16 + 8 * (g >> 1) + (s >> 2) + 4 * half;
-    const int col = ob + 16 * (g & 1) + 4 * (s & 3);
+    const int row = 8 * g + 4 * half + (s >> 2);
+    const int col = ob + 4 * (s & 3);
     const int lc = col >> 3;
     return row * 512 + ((lc ^ swz_oc(row)) << 4) + (col & 7) * 2;
 }
@@ -170,59 +172,67 @@ __device__ __forceinline__ int frag_off_oc(int ob, int ks, int lane, int half) {
 // treats them as aliasing the in-flight DMA into other stage buffers and would
 // stall on it, or would place a wait before every MFMA.  Callers wait for these
 // reads with lgkm_wait() before use.
-__device__ __forceinline__ bf16x8_t read_rc(const LDS char *p) {
-    bf16x8_t v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(p));
-    return v;
-}
 template <int OFF>
-__device__ __forceinline__ bf16x8_t read_rc_off(const LDS char *p) {
+__device__ __forceinline__ bf16x8_t read_rc(const LDS char *p) {
     static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
     bf16x8_t v;
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(p), "n"(OFF));
     return v;
 }
-__device__ __forceinline__ bf16x4_t read_tr(const LDS char *p) {
-    bf16x4_t v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(p));
-    return v;
-}
-// Same, with a constant byte offset carried in the instruction's immediate field.
 template <int OFF>
-__device__ __forceinline__ bf16x4_t read_tr_off(const LDS char *p) {
+__device__ __forceinline__ bf16x4_t read_tr(const LDS char *p) {
     static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
     bf16x4_t v;
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(p), "n"(OFF));
     return v;
 }
 
+constexpr int kFrags = 8; // fragments per operand per wave (128 outer indices / 16)
+
+// acc += A·B on a 16x16x32 block.  Written as inline asm so the 64
+// accumulators of a wave stay in AGPRs: with the builtin the register
+// allocator splits them between register files and shuffles them inside the
+// main loop.  The accumulators are only read after mfma_drain().
+__device__ __forceinline__ void mfma16(f32x4_t &acc, const bf16x8_t &a, const bf16x8_t &b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last MFMA and any other instruction reading its
+// accumulator (more than the deepest MFMA pipeline needs).
+__device__ __forceinline__ void mfma_drain() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+typedef bf16x8_t Frags[kFrags];
+
+typedef bf16x4_t TrHalves[kFrags][2];
+
 // Wait for all of this wave's LDS reads; the fragments are threaded through the
-// asm so no MFMA that consumes them can be scheduled above the wait.
-__device__ __forceinline__ void lgkm_wait(bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
+// asm so no instruction that consumes them can be placed above the wait.
+__device__ __forceinline__ void lgkm_wait_tr(TrHalves &t) {
     asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]),
-                   "+v"(b[3])
+                 : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]), "+v"(t[2][0]), "+v"(t[2][1]),
+                   "+v"(t[3][0]), "+v"(t[3][1]), "+v"(t[4][0]), "+v"(t[4][1]), "+v"(t[5][0]), "+v"(t[5][1]),
+                   "+v"(t[6][0]), "+v"(t[6][1]), "+v"(t[7][0]), "+v"(t[7][1])
+                 :
+                 : "memory");
+}
+__device__ __forceinline__ void lgkm_wait(Frags &a, Frags &b) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
+                   "+v"(a[7]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4]), "+v"(b[5]),
+                   "+v"(b[6]), "+v"(b[7])
                  :
                  : "memory");
 }
 
-// Wait until at most `n` of this wave's DMA instructions are still in flight
-// (DMA completes in issue order).
+// Wait until at most `n` (a multiple of 8, <= 24) of this wave's DMA
+// instructions are still in flight (DMA completes in issue order).
 __device__ __forceinline__ void dma_wait(int n) {
-    if (n >= 28)
-        asm volatile("s_waitcnt vmcnt(28)" ::: "memory");
-    else if (n >= 24)
+    if (n >= 24)
         asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-    else if (n >= 20)
-        asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
     else if (n >= 16)
         asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if (n >= 12)
-        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     else if (n >= 8)
         asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if (n >= 4)
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -252,10 +262,15 @@ __device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, i
     tj = in_group / rows;
 }
 
+// One 256x256 output tile.  Wave w = 2*wm + wn owns the 128x128 quadrant
+// (wm, wn) as 8x8 blocks of 16x16 (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
+// The reduction runs in slabs of 32 through a 4-slot LDS ring; one slab is one
+// k-step of 64 MFMAs per wave.
 template <int KIND>
 __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS char *smem) {
-    static_assert(kKSteps == 2 && kDmaPerOp == 4 && kStages == 4, "pipeline below assumes 2 k-steps, 4 stages");
+    static_assert(kDmaPerOp == 4 && kStages == 4, "pipeline below assumes 4 DMAs per operand, 4 stages");
     constexpr int kRPF = KIND == JOB_DX ? 1 : 2; // LDS reads per fragment
+    constexpr int kReads = 2 * kFrags * kRPF;    // per wave per slab
     constexpr int kDmaPerSlab = 2 * kDmaPerOp;
     int ti, tj;
     tile_coords(jb, t_index, ti, tj);
@@ -272,28 +287,26 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
         va[p] = dma_lane_off<KIND>(p, jb.lda, jb.I, i0, w, lane);
         vb[p] = dma_lane_off<KIND>(p, jb.ldb, jb.J, j0, w, lane);
     }
-    int fo[kKSteps][2][4][kRPF]; // [k-step][A/B][block][half]
+    int fo[2][kFrags][kRPF]; // [A/B][block][half]
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
+    for (int x = 0; x < kFrags; ++x)
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int h = 0; h < kRPF; ++h) {
-                if (KIND == JOB_DX) {
-                    fo[ks][0][x][h] = frag_off_rc(wm * 128 + x * 32, ks, lane);
-                    fo[ks][1][x][h] = kBOffset + frag_off_rc(wn * 128 + x * 32, ks, lane);
-                } else {
-                    fo[ks][0][x][h] = frag_off_oc(wm * 128 + x * 32, ks, lane, h);
-                    fo[ks][1][x][h] = kBOffset + frag_off_oc(wn * 128 + x * 32, ks, lane, h);
-                }
+        for (int h = 0; h < kRPF; ++h) {
+            if (KIND == JOB_DX) {
+                fo[0][x][h] = frag_off_rc(wm * 128 + x * 16, lane);
+                fo[1][x][h] = kBOffset + frag_off_rc(wn * 128 + x * 16, lane);
+            } else {
+                fo[0][x][h] = frag_off_oc(wm * 128 + x * 16, lane, h);
+                fo[1][x][h] = kBOffset + frag_off_oc(wn * 128 + x * 16, lane, h);
             }
+        }
 
-    f32x16_t acc[4][4];
+    f32x4_t acc[kFrags][kFrags];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < kFrags; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y)
-            acc[x][y] = f32x16_t{};
+        for (int y = 0; y < kFrags; ++y)
+            acc[x][y] = f32x4_t{};
 
     const int nslab = (int)((jb.R + kBK - 1) / kBK);
     const bool rc_tail = KIND == JOB_DX && (jb.R % kBK) != 0;
@@ -314,10 +327,15 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
         __amdgpu_buffer_rsrc_t a, b;
     };
     auto slab_src = [&](int s) {
+        SlabSrc r;
+        if (s >= nslab) { // padding slab: every lane out of range, reads zero
+            r.a = make_rsrc(jb.a, 0);
+            r.b = make_rsrc(jb.b, 0);
+            return r;
+        }
         s += rot;
         s = s >= nslab ? s - nslab : s;
         const int64_t r0 = (int64_t)s * kBK;
-        SlabSrc r;
         if (KIND == JOB_DX) {
             r.a = make_rsrc(jb.a + s * step_a, jb.a_bytes - (uint32_t)(2 * r0));
             r.b = make_rsrc(jb.b + s * step_b, jb.b_bytes - (uint32_t)(2 * r0));
@@ -327,219 +345,174 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
         }
         return r;
     };
-    // DMA instruction p of both operands for slab s (TAIL: the partial last RC slab)
-    auto dma = [&](const SlabSrc &src, int s, int p, bool tail) {
-        LDS char *st = wdst + (s % kStages) * kOperandBytes + p * 1024;
+    // DMA instruction p of operand op for slab s (TAIL: the partial last RC slab)
+    auto dma = [&](const SlabSrc &src, int s, int op, int p, bool tail) {
+        LDS char *st = wdst + (s % kStages) * kOperandBytes + p * 1024 + op * kBOffset;
         if (tail) {
             const int64_t r0 = (int64_t)s * kBK;
-            dma16(make_rsrc(jb.a, jb.a_bytes), st, dma_rc_tail_off(p, jb.lda, jb.I, jb.R, i0, r0, w, lane));
-            dma16(make_rsrc(jb.b, jb.b_bytes), st + kBOffset,
-                  dma_rc_tail_off(p, jb.ldb, jb.J, jb.R, j0, r0, w, lane));
+            if (op == 0)
+                dma16(make_rsrc(jb.a, jb.a_bytes), st, dma_rc_tail_off(p, jb.lda, jb.I, jb.R, i0, r0, w, lane));
+            else
+                dma16(make_rsrc(jb.b, jb.b_bytes), st, dma_rc_tail_off(p, jb.ldb, jb.J, jb.R, j0, r0, w, lane));
         } else {
-            dma16(src.a, st, va[p]);
-            dma16(src.b, st + kBOffset, vb[p]);
+            dma16(op == 0 ? src.a : src.b, st, op == 0 ? va[p] : vb[p]);
         }
     };
-
-    // One k-step: 16 MFMAs on (af, bf); after each of the first 8, the LDS read(s)
-    // of one next fragment into (an, bn), and after MFMAs 12-13 one DMA
-    // instruction pair of slab ds.  sched_barrier pins the order so the matrix
-    // pipe never waits behind a run of address or memory work.
-    auto kstep = [&](bf16x8_t(&af)[4], bf16x8_t(&bf)[4], auto stage_next, int ks_next,
-                     bf16x8_t(&an)[4], bf16x8_t(&bn)[4], bool R, bool D, bool tail,
-                     const SlabSrc &src, int ds, int dp0) {
-        bf16x4_t tr[2][4][2];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int x = i >> 2, y = i & 3;
-            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[y], af[x], acc[x][y], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            // LDS reads go in the first 8 slots (two per slot for the transposing
-            // reads) so they complete long before the wait at the next region
-#pragma unroll
-            for (int j = kRPF * i; j < kRPF * (i + 1); ++j) {
-                if (!R || i >= 8)
-                    break;
-                const int op = j / (4 * kRPF), xb = (j % (4 * kRPF)) / kRPF, h = j % kRPF;
-                const LDS char *lane_base = smem + fo[ks_next][op][xb][h];
-                if constexpr (std::is_integral_v<decltype(stage_next)>) {
-                    const LDS char *a = lane_base + stage_next * kOperandBytes;
-                    if (KIND == JOB_DX)
-                        (op == 0 ? an : bn)[xb] = read_rc(a);
-                    else
-                        tr[op][xb][h] = read_tr(a);
-                } else {
-                    constexpr int off = decltype(stage_next)::value * kOperandBytes;
-                    if (KIND == JOB_DX)
-                        (op == 0 ? an : bn)[xb] = read_rc_off<off>(lane_base);
-                    else
-                        tr[op][xb][h] = read_tr_off<off>(lane_base);
-                }
-            }
-            if (D && i >= 12 && i < 12 + kDmaPerOp / 2)
-                dma(src, ds, dp0 + (i - 12), tail);
-            __builtin_amdgcn_sched_barrier(0);
+    // Read LDS read number j (0 .. kReads-1) of a slab held in ring slot `stage`
+    // (an int, or a compile-time constant that becomes the immediate offset).
+    auto read_frag = [&](auto stage, int j, Frags &an, Frags &bn, TrHalves (&tr)[2]) {
+        const int op = j / (kFrags * kRPF), xb = (j % (kFrags * kRPF)) / kRPF, h = j % kRPF;
+        const LDS char *base = smem + fo[op][xb][h];
+        if constexpr (std::is_integral_v<decltype(stage)>) {
+            base += stage * kOperandBytes;
+            if (KIND == JOB_DX)
+                (op == 0 ? an : bn)[xb] = read_rc<0>(base);
+            else
+                tr[op][xb][h] = read_tr<0>(base);
+        } else {
+            constexpr int off = decltype(stage)::value * kOperandBytes;
+            if (KIND == JOB_DX)
+                (op == 0 ? an : bn)[xb] = read_rc<off>(base);
+            else
+                tr[op][xb][h] = read_tr<off>(base);
         }
-        if (KIND == JOB_DW && R) {
+    };
+    // wait for the slab's reads, then (OC) join the two transposed halves
+    auto finish_reads = [&](Frags &an, Frags &bn, TrHalves (&tr)[2]) {
+        if (KIND == JOB_DX) {
+            lgkm_wait(an, bn);
+        } else {
+            lgkm_wait_tr(tr[0]);
+            lgkm_wait_tr(tr[1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int xb = 0; xb < 4; ++xb) {
+            for (int xb = 0; xb < kFrags; ++xb) {
                 an[xb] = __builtin_shufflevector(tr[0][xb][0], tr[0][xb][1], 0, 1, 2, 3, 4, 5, 6, 7);
                 bn[xb] = __builtin_shufflevector(tr[1][xb][0], tr[1][xb][1], 0, 1, 2, 3, 4, 5, 6, 7);
             }
         }
     };
 
-    bf16x8_t af[4], bf[4], an[4], bn[4];
-    // Slab s: k-step 0 (region A), then -- if there is a slab s+1 -- the barrier
-    // that opens it, then k-step 1 (region B), which already reads slab s+1's
-    // first fragments.  After the barrier in slab s no wave reads slab s's ring
-    // slot any more, so the DMA of slab s+4 may start in region B.
-    //   early (RC): region A issues the second half of slab s+3, region B the
-    //               first half of slab s+4 -- one k-step more lead, which the
-    //               64-byte row segments of RC slabs need;
-    //   otherwise:  regions A and B issue the two halves of slab s+3.
+    // Slab s (fragments already in af/bf):
+    //   if there is a slab s+1: wait for its DMA and barrier.  After the
+    //   barrier every wave has its slab-s fragments in registers, so ring slot
+    //   s%4 is free and takes the DMA of slab s+4;
+    //   64 MFMAs on (af, bf); the LDS reads of slab s+1 into (an, bn) go with
+    //   the first MFMAs, the DMA of slab s+4 with later ones (sched_barrier pins
+    //   the order, so the matrix pipe never waits behind address or memory work).
+    //   The last slab reads its successor's ring slot too (stale data, never
+    //   used): keeping the reads unconditional lets the transposed halves share
+    //   registers with the fragments they form.
     // wait_n: this wave's DMA instructions issued after slab s+1's.
     // Called with constant flags in the steady state (inlining folds them away)
     // and with run-time flags in the few peeled and draining iterations.
     // stage: the ring slot of slab s, as a compile-time constant (unrolled steady
     // state) or an int; the next slab's slot is derived the same way.
-    constexpr bool kEarly = KIND == JOB_DX;
-    constexpr int kAheadB = kEarly ? kStages : kStages - 1; // slab whose DMA region B issues
-    constexpr int kHalf = kDmaPerOp / 2;
     auto next_stage = [](auto st) {
         if constexpr (std::is_integral_v<decltype(st)>)
             return (st + 1) % kStages;
         else
             return std::integral_constant<int, (decltype(st)::value + 1) % kStages>{};
     };
-    auto slab = [&](int s, auto stage, bool dA, bool tA, bool dB, bool tB, bool N, int wait_n) {
-        const SlabSrc srcA = dA ? slab_src(s + kStages - 1) : SlabSrc{};
-        SlabSrc srcB = srcA;
-        if constexpr (kEarly)
-            srcB = dB ? slab_src(s + kStages) : SlabSrc{};
-        lgkm_wait(af, bf);
-        __builtin_amdgcn_sched_barrier(0);
-        kstep(af, bf, stage, 1, an, bn, true, dA, tA, srcA, s + kStages - 1, kEarly ? kHalf : 0);
+    constexpr int kReadSlot = KIND == JOB_DX ? 2 : 1; // MFMA slots per LDS read
+    constexpr int kDmaSlot0 = 36;                      // DMA j after MFMA kDmaSlot0 + 2j
+    auto slab = [&](int s, auto stage, bool dmas, bool tail, bool N, int wait_n, Frags &af, Frags &bf,
+                    Frags &an, Frags &bn) {
+        const SlabSrc src = dmas ? slab_src(s + kStages) : SlabSrc{};
         if (N) {
             dma_wait(wait_n);
             slab_barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
-        lgkm_wait(an, bn);
+        TrHalves tr[2];
+#pragma unroll
+        for (int i = 0; i < kFrags * kFrags; ++i) {
+            const int x = i / kFrags, y = i % kFrags;
+            mfma16(acc[x][y], bf[y], af[x]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i % kReadSlot == 0 && i / kReadSlot < kReads)
+                read_frag(next_stage(stage), i / kReadSlot, an, bn, tr);
+            if (dmas && i >= kDmaSlot0 && i < kDmaSlot0 + 2 * kDmaPerSlab && (i - kDmaSlot0) % 2 == 0) {
+                const int d = (i - kDmaSlot0) / 2;
+                dma(src, s + kStages, d & 1, d >> 1, tail);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        finish_reads(an, bn, tr);
         __builtin_amdgcn_sched_barrier(0);
-        kstep(an, bn, next_stage(stage), 0, af, bf, N, dB, tB, srcB, s + kAheadB, kEarly ? 0 : kHalf);
     };
-
+    Frags af, bf, an, bn;
+    // The slab count is padded to a multiple of the ring size with slabs that
+    // read zero, so every pass of the loops below runs four whole slabs with
+    // compile-time ring slots and no early exit.
+    const int nslab4 = (nslab + kStages - 1) / kStages * kStages;
     if (nslab > 0) {
-        for (int s = 0; s < kStages - 1 && s < nslab; ++s) {
+        // prologue: slabs 0..3 fill the ring; wait for slab 0 and read it
+        for (int s = 0; s < kStages; ++s) {
             const SlabSrc src = slab_src(s);
             const bool tail = rc_tail && s == nslab - 1;
 #pragma unroll
-            for (int p = 0; p < kDmaPerOp; ++p)
-                dma(src, s, p, tail);
+            for (int p = 0; p < kDmaPerOp; ++p) {
+                dma(src, s, 0, p, tail);
+                dma(src, s, 1, p, tail);
+            }
         }
-        const bool half3 = kEarly && nslab > kStages - 1; // early: first half of slab 3 as well
-        if (half3) {
-            const SlabSrc src = slab_src(kStages - 1);
-            const bool tail = rc_tail && kStages - 1 == nslab - 1;
-#pragma unroll
-            for (int p = 0; p < kHalf; ++p)
-                dma(src, kStages - 1, p, tail);
-        }
-        // slab 0 visible to all waves; later slabs may stay in flight
-        dma_wait(kDmaPerSlab * (min(nslab, kStages - 1) - 1) + (half3 ? kHalf * 2 : 0));
+        dma_wait(kDmaPerSlab * (kStages - 1));
         slab_barrier();
         {
-            bf16x4_t tr[2][4][2];
+            TrHalves tr[2];
 #pragma unroll
-            for (int op = 0; op < 2; ++op)
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-#pragma unroll
-                    for (int h = 0; h < kRPF; ++h) {
-                        const LDS char *a = smem + fo[0][op][x][h];
-                        if (KIND == JOB_DX)
-                            (op == 0 ? af : bf)[x] = read_rc(a);
-                        else
-                            tr[op][x][h] = read_tr(a);
-                    }
-            if (KIND == JOB_DW) {
-                lgkm_wait(af, bf);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    af[x] = __builtin_shufflevector(tr[0][x][0], tr[0][x][1], 0, 1, 2, 3, 4, 5, 6, 7);
-                    bf[x] = __builtin_shufflevector(tr[1][x][0], tr[1][x][1], 0, 1, 2, 3, 4, 5, 6, 7);
-                }
-            }
+            for (int j = 0; j < kReads; ++j)
+                read_frag(0, j, af, bf, tr);
+            finish_reads(af, bf, tr);
         }
-        // steady state: every DMA is of a full slab, branch free; unrolled by the
-        // ring size so each stage offset is a constant that folds into the LDS
-        // instructions' immediate offsets
+        // steady state: slabs s+1..s+3 exist and slab s+4 is a full slab, branch free
+        constexpr int kW = 2 * kDmaPerSlab; // slabs s+2 and s+3 may be in flight
         int s = 0;
-        if constexpr (kEarly) {
-            constexpr int kW = 2 * kDmaPerSlab; // slabs s+2 and s+3 may be in flight
-            for (; s + 2 * kStages < nslab; s += kStages) {
-                slab(s + 0, std::integral_constant<int, 0>{}, true, false, true, false, true, kW);
-                slab(s + 1, std::integral_constant<int, 1>{}, true, false, true, false, true, kW);
-                slab(s + 2, std::integral_constant<int, 2>{}, true, false, true, false, true, kW);
-                slab(s + 3, std::integral_constant<int, 3>{}, true, false, true, false, true, kW);
-            }
-            for (; s + kStages + 1 < nslab; ++s)
-                slab(s, s % kStages, true, false, true, false, true, kW);
-            // the iterations that issue the last slab (partial when R % kBK != 0),
-            // then the draining ones, which issue no DMA
-            for (; s < nslab; ++s) {
-                const bool dA = s + kStages - 1 < nslab, dB = s + kStages < nslab;
-                const bool tA = dA && rc_tail && s + kStages - 1 == nslab - 1;
-                const bool tB = dB && rc_tail && s + kStages == nslab - 1;
-                const int w = kDmaPerSlab * ((s + 2 < nslab) + (s + 3 < nslab));
-                slab(s, s % kStages, dA, tA, dB, tB, s + 1 < nslab, w);
-            }
-        } else {
-            constexpr int kW = kDmaPerSlab + kDmaPerOp; // slab s+2 and half of s+3
-            for (; s + kStages - 1 < nslab - kStages; s += kStages) {
-                slab(s + 0, std::integral_constant<int, 0>{}, true, false, true, false, true, kW);
-                slab(s + 1, std::integral_constant<int, 1>{}, true, false, true, false, true, kW);
-                slab(s + 2, std::integral_constant<int, 2>{}, true, false, true, false, true, kW);
-                slab(s + 3, std::integral_constant<int, 3>{}, true, false, true, false, true, kW);
-            }
-            for (; s < nslab - kStages; ++s)
-                slab(s, s % kStages, true, false, true, false, true, kW);
-            for (; s < nslab; ++s) {
-                const bool dmas = s + kStages - 1 < nslab;
-                const bool tail = dmas && rc_tail;
-                const int full = max(0, min(s + kStages - 2, nslab - 1) - (s + 1));
-                slab(s, s % kStages, dmas, tail, dmas, tail, s + 1 < nslab,
-                     kDmaPerSlab * full + (dmas ? kDmaPerOp : 0));
-            }
+        for (; s + 2 * kStages < nslab; s += kStages) {
+            slab(s + 0, std::integral_constant<int, 0>{}, true, false, true, kW, af, bf, an, bn);
+            slab(s + 1, std::integral_constant<int, 1>{}, true, false, true, kW, an, bn, af, bf);
+            slab(s + 2, std::integral_constant<int, 2>{}, true, false, true, kW, af, bf, an, bn);
+            slab(s + 3, std::integral_constant<int, 3>{}, true, false, true, kW, an, bn, af, bf);
+        }
+        // the rest (last DMAs, possibly the partial RC slab, then draining), with
+        // run-time flags that only gate DMA issue and barriers
+        auto slab_rt = [&](int t, auto stage, Frags &a, Frags &b, Frags &a2, Frags &b2) {
+            const bool dmas = t + kStages < nslab4;
+            slab(t, stage, dmas, dmas && rc_tail && t + kStages == nslab - 1, t + 1 < nslab4,
+                 kDmaPerSlab * ((t + 2 < nslab4) + (t + 3 < nslab4)), a, b, a2, b2);
+        };
+        for (; s < nslab4; s += kStages) {
+            slab_rt(s + 0, std::integral_constant<int, 0>{}, af, bf, an, bn);
+            slab_rt(s + 1, std::integral_constant<int, 1>{}, an, bn, af, bf);
+            slab_rt(s + 2, std::integral_constant<int, 2>{}, af, bf, an, bn);
+            slab_rt(s + 3, std::integral_constant<int, 3>{}, an, bn, af, bf);
         }
     }
 
-    // Epilogue: lane holds C[i][j..j+3] for i = .. + (lane&31), j = .. + 8g + 4(lane>>5).
-    const int64_t ib = i0 + wm * 128 + (lane & 31);
-    const int64_t jb0 = j0 + wn * 128 + 4 * (lane >> 5);
+    mfma_drain();
+    // Epilogue: block (x, y) of lane l holds C[i][j..j+3] for
+    // i = 16x + l%16, j = 16y + 4*(l/16) within the wave's quadrant.
+    const int64_t ib = i0 + wm * 128 + (lane & 15);
+    const int64_t jb0 = j0 + wn * 128 + 4 * (lane >> 4);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        const int64_t i = ib + x * 32;
+    for (int x = 0; x < kFrags; ++x) {
+        const int64_t i = ib + x * 16;
         if (i >= jb.I)
             continue;
 #pragma unroll
-        for (int y = 0; y < 4; ++y)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t j = jb0 + y * 32 + 8 * g;
-                if (j >= jb.J)
-                    continue; // J % 8 == 0: j..j+3 all in range
-                const f32x16_t &a = acc[x][y];
-                if (KIND == JOB_DX) {
-                    u32x2_t pk = {pack_bf16x2(a[4 * g], a[4 * g + 1]),
-                                  pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
-                    *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(jb.c) + i * jb.J + j) = pk;
-                } else {
-                    f32x4_t v = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-                    *reinterpret_cast<f32x4_t *>(static_cast<float *>(jb.c) + i * jb.J + j) = v;
-                }
+        for (int y = 0; y < kFrags; ++y) {
+            const int64_t j = jb0 + y * 16;
+            if (j >= jb.J)
+                continue; // J % 8 == 0: j..j+3 all in range
+            const f32x4_t &a = acc[x][y];
+            if (KIND == JOB_DX) {
+                u32x2_t pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+                *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(jb.c) + i * jb.J + j) = pk;
+            } else {
+                *reinterpret_cast<f32x4_t *>(static_cast<float *>(jb.c) + i * jb.J + j) = a;
             }
+        }
     }
 }
 
