@@ -262,6 +262,227 @@ __device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, i
     tj = in_group / rows;
 }
 
+// Epilogue: block (x, y) of lane l holds C[i][j..j+3] for i = 16x + l%16,
+// j = 16y + 4*(l/16) within the wave's quadrant; bf16 (dX) or fp32 (dW) out.
+template <int KIND>
+__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[kFrags][kFrags], const TileJob &jb, int64_t i0,
+                                           int64_t j0, int wm, int wn, int lane) {
+    const int64_t ib = i0 + wm * 128 + (lane & 15);
+    const int64_t jb0 = j0 + wn * 128 + 4 * (lane >> 4);
+#pragma unroll
+    for (int x = 0; x < kFrags; ++x) {
+        const int64_t i = ib + x * 16;
+        if (i >= jb.I)
+            continue;
+#pragma unroll
+        for (int y = 0; y < kFrags; ++y) {
+            const int64_t j = jb0 + y * 16;
+            if (j >= jb.J)
+                continue; // J % 8 == 0: j..j+3 all in range
+            const f32x4_t &a = acc[x][y];
+            if (KIND == JOB_DX) {
+                u32x2_t pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+                *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(jb.c) + i * jb.J + j) = pk;
+            } else {
+                *reinterpret_cast<f32x4_t *>(static_cast<float *>(jb.c) + i * jb.J + j) = a;
+            }
+        }
+    }
+}
+
+// ---- RC operands (dX): slab pairs ----
+// Two consecutive 32-deep slabs are stored together, as 256 rows of 128 B
+// (r 0..63 of the pair), so each 8-lane group of a DMA instruction fetches one
+// whole 128-byte line: half-line requests would double the L1->L2 request
+// count.  The 128 KiB hold two such pairs per operand.  16-byte chunk c of row
+// o is stored at chunk c ^ swz_rcp(o), which keeps any 8 (or any 16, on two
+// 128-byte rows per bank sweep) consecutive rows of one chunk on distinct banks.
+constexpr int kPairBytes = 2 * kOperandBytes; // 32 KiB per operand
+constexpr int kDmaPerOpPair = 8;              // DMA instructions per wave per operand per pair
+__device__ __forceinline__ int swz_rcp(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int rcp_off(int o, int c) { return o * 128 + ((c ^ swz_rcp(o)) << 4); }
+// fragment of outer block ob (16 wide) for slab half h of a pair
+__device__ __forceinline__ int frag_off_rcp(int ob, int lane, int h) {
+    return rcp_off(ob + (lane & 15), 4 * h + (lane >> 4));
+}
+// DMA instruction p of wave w fills pair rows 8q .. 8q+7, q = 8w + p; lane l
+// fetches logical chunk (l & 7) ^ swz_rcp(row) of row 8q + l/8.  Offset
+// relative to the pair's first r; rows outside the operand (or, for the
+// partial last pair, r >= R) read zero.
+__device__ __forceinline__ uint32_t dma_rcp_off(int p, int64_t ld, int64_t O, int64_t o0, int w, int lane,
+                                                int64_t k0 = 0, int64_t R = -1) {
+    const int row = (w * kDmaPerOpPair + p) * 8 + (lane >> 3);
+    const int lc = (lane & 7) ^ swz_rcp(row);
+    const int64_t o = o0 + row;
+    const int64_t k = k0 + 8 * lc;
+    const bool ok = o < O && (R < 0 || k < R);
+    return ok ? (uint32_t)((o * ld + (R < 0 ? 0 : k0) + 8 * lc) * 2) : kOOB;
+}
+
+// dX tile.  Slab t lives in pair t/2, ring slot (t/2)%2, half t%2.  During
+// slab t the MFMAs use slab t's fragments (in registers) while slab t+1's are
+// read; an odd slab t first waits for pair (t+1)/2 and barriers (after which
+// the slot of pair (t-1)/2, whose fragments are all in registers, is free),
+// then issues the DMA of pair (t+3)/2 into that slot: a pair is fetched one to
+// two slabs ahead of its first use, with one barrier per pair.
+__device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS char *smem) {
+    static_assert(kStages * kOperandBytes == 2 * kPairBytes, "two pairs per operand");
+    constexpr int kReads = 2 * kFrags; // ds_read_b128 per wave per slab
+    int ti, tj;
+    tile_coords(jb, t_index, ti, tj);
+    const int64_t i0 = (int64_t)ti * kTile;
+    const int64_t j0 = (int64_t)tj * kTile;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w >> 1, wn = w & 1;
+
+    uint32_t va[kDmaPerOpPair], vb[kDmaPerOpPair];
+#pragma unroll
+    for (int p = 0; p < kDmaPerOpPair; ++p) {
+        va[p] = dma_rcp_off(p, jb.lda, jb.I, i0, w, lane);
+        vb[p] = dma_rcp_off(p, jb.ldb, jb.J, j0, w, lane);
+    }
+    int fo[2][kFrags][2]; // [A/B][block][half]
+#pragma unroll
+    for (int x = 0; x < kFrags; ++x)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            fo[0][x][h] = frag_off_rcp(wm * 128 + x * 16, lane, h);
+            fo[1][x][h] = kBOffset + frag_off_rcp(wn * 128 + x * 16, lane, h);
+        }
+    f32x4_t acc[kFrags][kFrags];
+#pragma unroll
+    for (int x = 0; x < kFrags; ++x)
+#pragma unroll
+        for (int y = 0; y < kFrags; ++y)
+            acc[x][y] = f32x4_t{};
+
+    const int64_t R = jb.R;
+    const int npair = (int)((R + 63) / 64);
+    const int nslab4 = (int)(((R + kBK - 1) / kBK + 3) / 4 * 4); // padded with zero slabs
+    const int P = nslab4 / 2;                                     // pairs, padding included
+    const bool ptail = (R % 64) != 0;                             // last real pair is partial
+    // rotation of the reduction order (see TileJob), in whole pairs
+    const int rotp = ptail || npair == 0 ? 0 : ((jb.rot_i * (ti & 3) + jb.rot_j * (tj & 7)) >> 1) % npair;
+    LDS char *const wdst = smem + w * kDmaPerOpPair * 1024;
+
+    struct PairSrc {
+        __amdgpu_buffer_rsrc_t a, b;
+    };
+    auto pair_src = [&](int q) {
+        PairSrc r;
+        if (q >= npair) { // padding: every lane out of range, reads zero
+            r.a = make_rsrc(jb.a, 0);
+            r.b = make_rsrc(jb.b, 0);
+            return r;
+        }
+        q += rotp;
+        q = q >= npair ? q - npair : q;
+        const int64_t k0 = (int64_t)q * 64;
+        r.a = make_rsrc(jb.a + k0, jb.a_bytes - (uint32_t)(2 * k0));
+        r.b = make_rsrc(jb.b + k0, jb.b_bytes - (uint32_t)(2 * k0));
+        return r;
+    };
+    auto dma = [&](const PairSrc &src, int q, int op, int p, bool tail) {
+        LDS char *st = wdst + (q & 1) * kPairBytes + p * 1024 + op * kBOffset;
+        if (tail) {
+            const int64_t k0 = (int64_t)q * 64;
+            if (op == 0)
+                dma16(make_rsrc(jb.a, jb.a_bytes), st, dma_rcp_off(p, jb.lda, jb.I, i0, w, lane, k0, R));
+            else
+                dma16(make_rsrc(jb.b, jb.b_bytes), st, dma_rcp_off(p, jb.ldb, jb.J, j0, w, lane, k0, R));
+        } else {
+            dma16(op == 0 ? src.a : src.b, st, op == 0 ? va[p] : vb[p]);
+        }
+    };
+    // LDS read j (0..15) of the slab with t % 4 == TM
+    auto read_frag = [&](auto tm, int j, Frags &an, Frags &bn) {
+        constexpr int m = decltype(tm)::value;
+        constexpr int off = ((m >> 1) & 1) * kPairBytes;
+        const int op = j / kFrags, xb = j % kFrags;
+        (op == 0 ? an : bn)[xb] = read_rc<off>(smem + fo[op][xb][m & 1]);
+    };
+    // slab t with t % 4 == TM (compile time); flags as described above
+    auto slab = [&](int t, auto tm, bool dmas, bool tail, bool N, Frags &af, Frags &bf, Frags &an, Frags &bn) {
+        constexpr int m = decltype(tm)::value;
+        constexpr bool odd = m & 1;
+        const int q = (t + 3) / 2;
+        PairSrc src{};
+        if (odd && dmas)
+            src = pair_src(q);
+        if (odd && N) {
+            dma_wait(0);
+            slab_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kFrags * kFrags; ++i) {
+            const int x = i / kFrags, y = i % kFrags;
+            mfma16(acc[x][y], bf[y], af[x]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i % 2 == 0 && i / 2 < kReads)
+                read_frag(std::integral_constant<int, (m + 1) % 4>{}, i / 2, an, bn);
+            if (odd && dmas && i % 2 == 1 && i / 2 < 2 * kDmaPerOpPair) {
+                const int d = i / 2;
+                dma(src, q, d & 1, d >> 1, tail);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        lgkm_wait(an, bn);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    Frags af, bf, an, bn;
+    if (nslab4 > 0) {
+        // prologue: pairs 0 and 1 fill both slots; wait for pair 0 and read slab 0
+        for (int q = 0; q < 2; ++q) {
+            const PairSrc src = pair_src(q);
+            const bool tail = ptail && q == npair - 1;
+#pragma unroll
+            for (int p = 0; p < kDmaPerOpPair; ++p) {
+                dma(src, q, 0, p, tail);
+                dma(src, q, 1, p, tail);
+            }
+        }
+        dma_wait(2 * kDmaPerOpPair);
+        slab_barrier();
+#pragma unroll
+        for (int j = 0; j < kReads; ++j)
+            read_frag(std::integral_constant<int, 0>{}, j, af, bf);
+        lgkm_wait(af, bf);
+
+        using C0 = std::integral_constant<int, 0>;
+        using C1 = std::integral_constant<int, 1>;
+        using C2 = std::integral_constant<int, 2>;
+        using C3 = std::integral_constant<int, 3>;
+        int s = 0;
+        // steady state: the pairs issued (s/2 + 2, s/2 + 3) are full ones
+        for (; s / 2 + 4 < npair; s += 4) {
+            slab(s + 0, C0{}, false, false, false, af, bf, an, bn);
+            slab(s + 1, C1{}, true, false, true, an, bn, af, bf);
+            slab(s + 2, C2{}, false, false, false, af, bf, an, bn);
+            slab(s + 3, C3{}, true, false, true, an, bn, af, bf);
+        }
+        auto odd_flags = [&](int t, bool &dmas, bool &tail, bool &N) {
+            const int q = (t + 3) / 2;
+            dmas = q < P;
+            tail = dmas && ptail && q == npair - 1;
+            N = t + 1 < nslab4;
+        };
+        for (; s < nslab4; s += 4) {
+            bool d1, t1, n1, d3, t3, n3;
+            odd_flags(s + 1, d1, t1, n1);
+            odd_flags(s + 3, d3, t3, n3);
+            slab(s + 0, C0{}, false, false, false, af, bf, an, bn);
+            slab(s + 1, C1{}, d1, t1, n1, an, bn, af, bf);
+            slab(s + 2, C2{}, false, false, false, af, bf, an, bn);
+            slab(s + 3, C3{}, d3, t3, n3, an, bn, af, bf);
+        }
+    }
+    mfma_drain();
+    store_tile<JOB_DX>(acc, jb, i0, j0, wm, wn, lane);
+}
+
 // One 256x256 output tile.  Wave w = 2*wm + wn owns the 128x128 quadrant
 // (wm, wn) as 8x8 blocks of 16x16 (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
 // The reduction runs in slabs of 32 through a 4-slot LDS ring; one slab is one
@@ -491,29 +712,7 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
     }
 
     mfma_drain();
-    // Epilogue: block (x, y) of lane l holds C[i][j..j+3] for
-    // i = 16x + l%16, j = 16y + 4*(l/16) within the wave's quadrant.
-    const int64_t ib = i0 + wm * 128 + (lane & 15);
-    const int64_t jb0 = j0 + wn * 128 + 4 * (lane >> 4);
-#pragma unroll
-    for (int x = 0; x < kFrags; ++x) {
-        const int64_t i = ib + x * 16;
-        if (i >= jb.I)
-            continue;
-#pragma unroll
-        for (int y = 0; y < kFrags; ++y) {
-            const int64_t j = jb0 + y * 16;
-            if (j >= jb.J)
-                continue; // J % 8 == 0: j..j+3 all in range
-            const f32x4_t &a = acc[x][y];
-            if (KIND == JOB_DX) {
-                u32x2_t pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-                *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(jb.c) + i * jb.J + j) = pk;
-            } else {
-                *reinterpret_cast<f32x4_t *>(static_cast<float *>(jb.c) + i * jb.J + j) = a;
-            }
-        }
-    }
+    store_tile<KIND>(acc, jb, i0, j0, wm, wn, lane);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
@@ -526,7 +725,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
         jb = &p.job[1];
     }
     if (jb->kind == JOB_DX)
-        run_tile<JOB_DX>(*jb, b, smem);
+        run_tile_rc(*jb, b, smem);
     else
         run_tile<JOB_DW>(*jb, b, smem);
 }

@@ -70,6 +70,24 @@ def test_bf16_shapes_match_oracle(M, K, N):
     check_full(case, dX, dW)
 
 
+# Reduction lengths around the 32-deep slab, the 64-deep dX slab pair (a
+# partial last pair when R % 64 != 0) and the padding of the slab count to a
+# multiple of four.
+REDUCTIONS = [8, 24, 32, 40, 64, 72, 96, 128, 136, 200, 256, 264, 392]
+
+
+@pytest.mark.parametrize("R", REDUCTIONS)
+def test_short_and_ragged_reductions(R):
+    # dX on the tile path (M > 64): reduction over n = R
+    case = synth.linear_case(96, 72, R, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=R)
+    dX, _ = run(case, need_dw=False)
+    check_full(case, dX, None)
+    # dW: reduction over m = R
+    case = synth.linear_case(R, 72, 80, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=R + 1)
+    _, dW = run(case, need_dx=False)
+    check_full(case, None, dW)
+
+
 @pytest.mark.parametrize("M,K,N", [(64, 64, 64), (33, 100, 70), (130, 264, 96)])
 def test_f32_shapes_match_oracle(M, K, N):
     case = synth.linear_case(M, K, N, "f32", x_std=1.0, w_std=1.0, g_std=1.0, seed=7)
@@ -110,6 +128,10 @@ def test_skip_outputs_and_empty_sums():
     assert bool((dW == 0).all())
     # N = 0: dX is zeros
     e = synth.linear_case(40, 72, 0, "bf16", seed=5)
+    dX, _ = run(e, need_dw=False)
+    assert bool((dX == 0).all())
+    # N = 0 on the tile path (M > 64): a reduction of padding slabs only
+    e = synth.linear_case(100, 72, 0, "bf16", seed=5)
     dX, _ = run(e, need_dw=False)
     assert bool((dX == 0).all())
     # small-M shape with N = 0, and fp32 with M = 0
