@@ -61,30 +61,20 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 // conflicts whether the LDS serves 8 or 16 lanes of a 16-byte read (resp. 16
 // or 32 lanes of an 8-byte read) per cycle.
 //
-//  RC ("reduction contiguous", dX operands dY and W): 128 lines of 128 B;
-//     line k holds the 32 r of output rows k (chunks 0-3) and k + 128
-//     (chunks 4-7), and 16-byte chunk c of line k is stored at chunk
-//     c ^ swz_rc(k).  An MFMA fragment (one ds_read_b128, 8 r values per
-//     lane) reads 16 consecutive lines at each of four chunks; any 16
-//     consecutive lines at one chunk cover all banks under this swizzle.
+//  RC ("reduction contiguous", dX operands dY and W): slab pairs, described
+//     with the dX pipeline below.
 //  OC ("outer contiguous", dW operands X and dY): 32 rows (r) x 256 outer
 //     indices, 512 B per row; chunk c of row r is stored at chunk
 //     c ^ swz_oc(r).  MFMA fragment = two ds_read_b64_tr_b16: within each
 //     16-lane group the instruction reads a 4-row x 16-column block (each
 //     lane addresses 4 columns of one row) and hands lane i column i, so a
 //     lane receives 4 consecutive r of its own outer index.
-static_assert(kBK == 32, "the RC line layout packs two 32-deep rows per 128-byte line");
-__device__ __forceinline__ int swz_rc(int line) { return (line & 7) ^ ((line >> 3) & 7); }
+static_assert(kBK == 32, "an RC slab pair is one 128-byte line per row");
 __device__ __forceinline__ int swz_oc(int row) {
     // 32-byte segment s of row r moves to s ^ ((r & 3) | 4*((r >> 3) & 1)): the
     // rows r..r+3 and r+8..r+11 that one 32-lane read touches land on eight
     // different segments (chunk pairs stay together)
     return 2 * ((row & 3) | (((row >> 3) & 1) << 2));
-}
-// LDS byte offset of 16-byte chunk c (0..3) of output row o (0..255) in an RC slab
-__device__ __forceinline__ int rc_off(int o, int c) {
-    const int line = o & 127;
-    return line * 128 + (((4 * (o >> 7) + c) ^ swz_rc(line)) << 4);
 }
 
 enum JobKind { JOB_DX = 0, JOB_DW = 1 };
@@ -117,49 +107,24 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, LDS char *dst, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void *)dst, 16, (int)off, 0, 0, 0);
 }
 
-// Per-lane DMA source offsets, fixed for a tile.  Instruction p of wave w
-// fills 1 KiB of the operand slab at q = kDmaPerOp*w + p:
-//  RC: LDS line 8q + (lane>>3), physical chunk lane&7, which holds logical
-//      chunk (lane&7) ^ swz_rc(line) = 4*half + c: r-chunk c of output row
-//      line + 128*half.  Offset (o*ld + 8c)*2 relative to the slab's first r.
-//  OC: LDS row 2q + (lane>>5) (an r), physical chunk lane&31 holding outer
-//      chunk (lane&31) ^ swz_oc(row).  Offset (row*ld + o)*2 relative to the
-//      slab's first row.
-// Lanes whose row (RC) or outer chunk (OC) lies outside the operand get kOOB.
-template <int KIND>
-__device__ __forceinline__ uint32_t dma_lane_off(int p, int64_t ld, int64_t O, int64_t o0, int w, int lane) {
+// Per-lane DMA source offsets of an OC slab, fixed for a tile.  Instruction p
+// of wave w fills LDS rows 2q, 2q+1 (r) of the slab, q = kDmaPerOp*w + p: lane
+// l takes physical chunk l&31 of row 2q + l/32, i.e. outer chunk
+// (l&31) ^ swz_oc(row).  Offset (row*ld + o)*2 relative to the slab's first
+// row; outer chunks outside the operand get kOOB.
+__device__ __forceinline__ uint32_t dma_oc_off(int p, int64_t ld, int64_t O, int64_t o0, int w, int lane) {
     const int q = w * kDmaPerOp + p;
-    if (KIND == JOB_DX) {
-        const int line = q * 8 + (lane >> 3);
-        const int lc = (lane & 7) ^ swz_rc(line);
-        const int64_t o = o0 + line + 128 * (lc >> 2);
-        return o < O ? (uint32_t)((o * ld + 8 * (lc & 3)) * 2) : kOOB;
-    } else {
-        const int row = q * 2 + (lane >> 5);
-        const int lc = (lane & 31) ^ swz_oc(row);
-        const int64_t o = o0 + 8 * lc;
-        return o < O ? (uint32_t)((row * ld + o) * 2) : kOOB;
-    }
+    const int row = q * 2 + (lane >> 5);
+    const int lc = (lane & 31) ^ swz_oc(row);
+    const int64_t o = o0 + 8 * lc;
+    return o < O ? (uint32_t)((row * ld + o) * 2) : kOOB;
 }
 
-// The last RC slab when R % kBK != 0: r-chunks past R must read as zero, and
-// (as ld == R) they would otherwise read the next row, so each lane checks r.
-__device__ __forceinline__ uint32_t dma_rc_tail_off(int p, int64_t ld, int64_t O, int64_t R, int64_t o0,
-                                                    int64_t r0, int w, int lane) {
-    const int q = w * kDmaPerOp + p;
-    const int line = q * 8 + (lane >> 3);
-    const int lc = (lane & 7) ^ swz_rc(line);
-    const int64_t o = o0 + line + 128 * (lc >> 2);
-    const int64_t r = r0 + 8 * (lc & 3);
-    return (o < O && r < R) ? (uint32_t)((o * ld + r) * 2) : kOOB;
-}
-
-// Per-lane LDS byte offsets (within an operand slab) of the fragment for the
-// 16 outer indices ob..ob+15, all 32 r of the slab: lane l holds outer index
-// ob + l%16 and r = 8*(l/16) .. +7 (the operand layout of a 16x16x32 MFMA).
-// RC: one ds_read_b128.  OC: two ds_read_b64_tr_b16 (half h = r 4h..4h+3 of
-// each 8): each 16-lane group reads a 4-row x 16-column block.
-__device__ __forceinline__ int frag_off_rc(int ob, int lane) { return rc_off(ob + (lane & 15), lane >> 4); }
+// Per-lane LDS byte offsets (within an OC slab) of the fragment for the 16
+// outer indices ob..ob+15, all 32 r of the slab: lane l holds outer index
+// ob + l%16 and r = 8*(l/16) .. +7 (the operand layout of a 16x16x32 MFMA),
+// read as two ds_read_b64_tr_b16 (half h = r 4h..4h+3 of each 8): each
+// 16-lane group reads a 4-row x 16-column block.
 __device__ __forceinline__ int frag_off_oc(int ob, int lane, int half) {
     const int g = lane >> 4, s = lane & 15;
     const int row = 8 * g + 4 * half + (s >> 2);
@@ -483,15 +448,14 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
     store_tile<JOB_DX>(acc, jb, i0, j0, wm, wn, lane);
 }
 
-// One 256x256 output tile.  Wave w = 2*wm + wn owns the 128x128 quadrant
+// dW tile (OC operands).  Wave w = 2*wm + wn owns the 128x128 quadrant
 // (wm, wn) as 8x8 blocks of 16x16 (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
 // The reduction runs in slabs of 32 through a 4-slot LDS ring; one slab is one
 // k-step of 64 MFMAs per wave.
-template <int KIND>
-__device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS char *smem) {
+__device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS char *smem) {
     static_assert(kDmaPerOp == 4 && kStages == 4, "pipeline below assumes 4 DMAs per operand, 4 stages");
-    constexpr int kRPF = KIND == JOB_DX ? 1 : 2; // LDS reads per fragment
-    constexpr int kReads = 2 * kFrags * kRPF;    // per wave per slab
+    constexpr int kRPF = 2;                   // ds_read_b64_tr_b16 per fragment
+    constexpr int kReads = 2 * kFrags * kRPF; // per wave per slab
     constexpr int kDmaPerSlab = 2 * kDmaPerOp;
     int ti, tj;
     tile_coords(jb, t_index, ti, tj);
@@ -505,21 +469,16 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
     uint32_t va[kDmaPerOp], vb[kDmaPerOp];
 #pragma unroll
     for (int p = 0; p < kDmaPerOp; ++p) {
-        va[p] = dma_lane_off<KIND>(p, jb.lda, jb.I, i0, w, lane);
-        vb[p] = dma_lane_off<KIND>(p, jb.ldb, jb.J, j0, w, lane);
+        va[p] = dma_oc_off(p, jb.lda, jb.I, i0, w, lane);
+        vb[p] = dma_oc_off(p, jb.ldb, jb.J, j0, w, lane);
     }
     int fo[2][kFrags][kRPF]; // [A/B][block][half]
 #pragma unroll
     for (int x = 0; x < kFrags; ++x)
 #pragma unroll
         for (int h = 0; h < kRPF; ++h) {
-            if (KIND == JOB_DX) {
-                fo[0][x][h] = frag_off_rc(wm * 128 + x * 16, lane);
-                fo[1][x][h] = kBOffset + frag_off_rc(wn * 128 + x * 16, lane);
-            } else {
-                fo[0][x][h] = frag_off_oc(wm * 128 + x * 16, lane, h);
-                fo[1][x][h] = kBOffset + frag_off_oc(wn * 128 + x * 16, lane, h);
-            }
+            fo[0][x][h] = frag_off_oc(wm * 128 + x * 16, lane, h);
+            fo[1][x][h] = kBOffset + frag_off_oc(wn * 128 + x * 16, lane, h);
         }
 
     f32x4_t acc[kFrags][kFrags];
@@ -530,20 +489,15 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
             acc[x][y] = f32x4_t{};
 
     const int nslab = (int)((jb.R + kBK - 1) / kBK);
-    const bool rc_tail = KIND == JOB_DX && (jb.R % kBK) != 0;
-    // Tiles that run together on one XCD start the reduction at different
-    // slabs.  With RC operands whose rows are a large power of two of bytes
-    // apart, all rows of every concurrent tile otherwise share their low
-    // address bits and crowd into a few L2 sets.  (The sum is the same set of
-    // slab products taken in a rotated order.)
-    const int rot = rc_tail || nslab == 0 ? 0 : (jb.rot_i * (ti & 3) + jb.rot_j * (tj & 7)) % nslab;
+    // optional rotation of the reduction order (see TileJob)
+    const int rot = nslab == 0 ? 0 : (jb.rot_i * (ti & 3) + jb.rot_j * (tj & 7)) % nslab;
     // per-slab source advance (elements) of each operand
-    const int64_t step_a = KIND == JOB_DX ? kBK : (int64_t)kBK * jb.lda;
-    const int64_t step_b = KIND == JOB_DX ? kBK : (int64_t)kBK * jb.ldb;
+    const int64_t step_a = (int64_t)kBK * jb.lda;
+    const int64_t step_b = (int64_t)kBK * jb.ldb;
     LDS char *const wdst = smem + w * kDmaPerOp * 1024; // this wave's DMA destinations
 
     // Buffer descriptors for slab s: the base advances to the slab (scalar work
-    // only); for OC the size shrinks to the rows left, so rows past R read zero.
+    // only) and the size shrinks to the rows left, so rows past R read zero.
     struct SlabSrc {
         __amdgpu_buffer_rsrc_t a, b;
     };
@@ -557,27 +511,14 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
         s += rot;
         s = s >= nslab ? s - nslab : s;
         const int64_t r0 = (int64_t)s * kBK;
-        if (KIND == JOB_DX) {
-            r.a = make_rsrc(jb.a + s * step_a, jb.a_bytes - (uint32_t)(2 * r0));
-            r.b = make_rsrc(jb.b + s * step_b, jb.b_bytes - (uint32_t)(2 * r0));
-        } else {
-            r.a = make_rsrc(jb.a + s * step_a, (uint32_t)(2 * (jb.R - r0) * jb.lda));
-            r.b = make_rsrc(jb.b + s * step_b, (uint32_t)(2 * (jb.R - r0) * jb.ldb));
-        }
+        r.a = make_rsrc(jb.a + s * step_a, (uint32_t)(2 * (jb.R - r0) * jb.lda));
+        r.b = make_rsrc(jb.b + s * step_b, (uint32_t)(2 * (jb.R - r0) * jb.ldb));
         return r;
     };
-    // DMA instruction p of operand op for slab s (TAIL: the partial last RC slab)
-    auto dma = [&](const SlabSrc &src, int s, int op, int p, bool tail) {
+    // DMA instruction p of operand op for slab s
+    auto dma = [&](const SlabSrc &src, int s, int op, int p) {
         LDS char *st = wdst + (s % kStages) * kOperandBytes + p * 1024 + op * kBOffset;
-        if (tail) {
-            const int64_t r0 = (int64_t)s * kBK;
-            if (op == 0)
-                dma16(make_rsrc(jb.a, jb.a_bytes), st, dma_rc_tail_off(p, jb.lda, jb.I, jb.R, i0, r0, w, lane));
-            else
-                dma16(make_rsrc(jb.b, jb.b_bytes), st, dma_rc_tail_off(p, jb.ldb, jb.J, jb.R, j0, r0, w, lane));
-        } else {
-            dma16(op == 0 ? src.a : src.b, st, op == 0 ? va[p] : vb[p]);
-        }
+        dma16(op == 0 ? src.a : src.b, st, op == 0 ? va[p] : vb[p]);
     };
     // Read LDS read number j (0 .. kReads-1) of a slab held in ring slot `stage`
     // (an int, or a compile-time constant that becomes the immediate offset).
@@ -585,32 +526,21 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
         const int op = j / (kFrags * kRPF), xb = (j % (kFrags * kRPF)) / kRPF, h = j % kRPF;
         const LDS char *base = smem + fo[op][xb][h];
         if constexpr (std::is_integral_v<decltype(stage)>) {
-            base += stage * kOperandBytes;
-            if (KIND == JOB_DX)
-                (op == 0 ? an : bn)[xb] = read_rc<0>(base);
-            else
-                tr[op][xb][h] = read_tr<0>(base);
+            tr[op][xb][h] = read_tr<0>(base + stage * kOperandBytes);
         } else {
             constexpr int off = decltype(stage)::value * kOperandBytes;
-            if (KIND == JOB_DX)
-                (op == 0 ? an : bn)[xb] = read_rc<off>(base);
-            else
-                tr[op][xb][h] = read_tr<off>(base);
+            tr[op][xb][h] = read_tr<off>(base);
         }
     };
-    // wait for the slab's reads, then (OC) join the two transposed halves
+    // wait for the slab's reads, then join the two transposed halves
     auto finish_reads = [&](Frags &an, Frags &bn, TrHalves (&tr)[2]) {
-        if (KIND == JOB_DX) {
-            lgkm_wait(an, bn);
-        } else {
-            lgkm_wait_tr(tr[0]);
-            lgkm_wait_tr(tr[1]);
-            __builtin_amdgcn_sched_barrier(0);
+        lgkm_wait_tr(tr[0]);
+        lgkm_wait_tr(tr[1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int xb = 0; xb < kFrags; ++xb) {
-                an[xb] = __builtin_shufflevector(tr[0][xb][0], tr[0][xb][1], 0, 1, 2, 3, 4, 5, 6, 7);
-                bn[xb] = __builtin_shufflevector(tr[1][xb][0], tr[1][xb][1], 0, 1, 2, 3, 4, 5, 6, 7);
-            }
+        for (int xb = 0; xb < kFrags; ++xb) {
+            an[xb] = __builtin_shufflevector(tr[0][xb][0], tr[0][xb][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            bn[xb] = __builtin_shufflevector(tr[1][xb][0], tr[1][xb][1], 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
 
@@ -635,10 +565,10 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
         else
             return std::integral_constant<int, (decltype(st)::value + 1) % kStages>{};
     };
-    constexpr int kReadSlot = KIND == JOB_DX ? 2 : 1; // MFMA slots per LDS read
-    constexpr int kDmaSlot0 = 36;                      // DMA j after MFMA kDmaSlot0 + 2j
-    auto slab = [&](int s, auto stage, bool dmas, bool tail, bool N, int wait_n, Frags &af, Frags &bf,
-                    Frags &an, Frags &bn) {
+    constexpr int kReadSlot = 1; // MFMA slots per LDS read
+    constexpr int kDmaSlot0 = 36; // DMA j after MFMA kDmaSlot0 + 2j
+    auto slab = [&](int s, auto stage, bool dmas, bool N, int wait_n, Frags &af, Frags &bf, Frags &an,
+                    Frags &bn) {
         const SlabSrc src = dmas ? slab_src(s + kStages) : SlabSrc{};
         if (N) {
             dma_wait(wait_n);
@@ -655,7 +585,7 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
                 read_frag(next_stage(stage), i / kReadSlot, an, bn, tr);
             if (dmas && i >= kDmaSlot0 && i < kDmaSlot0 + 2 * kDmaPerSlab && (i - kDmaSlot0) % 2 == 0) {
                 const int d = (i - kDmaSlot0) / 2;
-                dma(src, s + kStages, d & 1, d >> 1, tail);
+                dma(src, s + kStages, d & 1, d >> 1);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -671,11 +601,10 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
         // prologue: slabs 0..3 fill the ring; wait for slab 0 and read it
         for (int s = 0; s < kStages; ++s) {
             const SlabSrc src = slab_src(s);
-            const bool tail = rc_tail && s == nslab - 1;
 #pragma unroll
             for (int p = 0; p < kDmaPerOp; ++p) {
-                dma(src, s, 0, p, tail);
-                dma(src, s, 1, p, tail);
+                dma(src, s, 0, p);
+                dma(src, s, 1, p);
             }
         }
         dma_wait(kDmaPerSlab * (kStages - 1));
@@ -691,16 +620,15 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
         constexpr int kW = 2 * kDmaPerSlab; // slabs s+2 and s+3 may be in flight
         int s = 0;
         for (; s + 2 * kStages < nslab; s += kStages) {
-            slab(s + 0, std::integral_constant<int, 0>{}, true, false, true, kW, af, bf, an, bn);
-            slab(s + 1, std::integral_constant<int, 1>{}, true, false, true, kW, an, bn, af, bf);
-            slab(s + 2, std::integral_constant<int, 2>{}, true, false, true, kW, af, bf, an, bn);
-            slab(s + 3, std::integral_constant<int, 3>{}, true, false, true, kW, an, bn, af, bf);
+            slab(s + 0, std::integral_constant<int, 0>{}, true, true, kW, af, bf, an, bn);
+            slab(s + 1, std::integral_constant<int, 1>{}, true, true, kW, an, bn, af, bf);
+            slab(s + 2, std::integral_constant<int, 2>{}, true, true, kW, af, bf, an, bn);
+            slab(s + 3, std::integral_constant<int, 3>{}, true, true, kW, an, bn, af, bf);
         }
-        // the rest (last DMAs, possibly the partial RC slab, then draining), with
-        // run-time flags that only gate DMA issue and barriers
+        // the rest (last DMAs, then draining), with run-time flags that only gate
+        // DMA issue and barriers
         auto slab_rt = [&](int t, auto stage, Frags &a, Frags &b, Frags &a2, Frags &b2) {
-            const bool dmas = t + kStages < nslab4;
-            slab(t, stage, dmas, dmas && rc_tail && t + kStages == nslab - 1, t + 1 < nslab4,
+            slab(t, stage, t + kStages < nslab4, t + 1 < nslab4,
                  kDmaPerSlab * ((t + 2 < nslab4) + (t + 3 < nslab4)), a, b, a2, b2);
         };
         for (; s < nslab4; s += kStages) {
@@ -712,7 +640,7 @@ __device__ __forceinline__ void run_tile(const TileJob &jb, int t_index, LDS cha
     }
 
     mfma_drain();
-    store_tile<KIND>(acc, jb, i0, j0, wm, wn, lane);
+    store_tile<JOB_DW>(acc, jb, i0, j0, wm, wn, lane);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
@@ -727,7 +655,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
     if (jb->kind == JOB_DX)
         run_tile_rc(*jb, b, smem);
     else
-        run_tile<JOB_DW>(*jb, b, smem);
+        run_tile_oc(*jb, b, smem);
 }
 
 // ------------------------------------------------------------------------
