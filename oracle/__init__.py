@@ -74,6 +74,15 @@ def _load():
     lib.oracle_adamw.argtypes = [vp, vp, i32, vp, vp, i64,
                                  f32, f32, f32, f32, f32, i32, f32]
     lib.oracle_adamw.restype = i32
+    lib.oracle_adamw_ex.argtypes = [vp, vp, i32, vp, vp, i64, f32, f32, f32, f32, f32, i32, f32,
+                                    vp, i32, vp, i32]
+    lib.oracle_adamw_ex.restype = i32
+    lib.oracle_f32_to_bf16.argtypes = [f32]
+    lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_f32_to_f16.argtypes = [f32]
+    lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+    lib.oracle_round16.argtypes = [vp, i64, i32, vp]
+    lib.oracle_round16.restype = None
     _lib = lib
     return lib
 
@@ -178,3 +187,35 @@ def adamw(W, g, m, v, gtype: str, lr, b1, b2, eps, wd, step, inv_scale):
         raise ValueError("adamw: invalid hyper-parameters (step=%r, b1=%r, b2=%r)"
                          % (step, b1, b2))
     return W, m, v
+
+
+def round16(a, dtype: str) -> np.ndarray:
+    """fp32 values rounded to nearest even as 'bf16' or 'f16' bit patterns (uint16)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().oracle_round16(_ptr(a), a.size, _DTYPES[dtype], _ptr(out))
+    return out
+
+
+def adamw_ex(W, g, m, v, gtype: str, lr, b1, b2, eps, wd, step, inv_scale,
+             clip=None, skip=False, w16=None):
+    """The AdamW step with the loop's optional parts: clip (float or None) multiplies
+    the unscaled gradient, skip leaves everything unchanged, w16 ('bf16' / 'f16' /
+    None) also returns the updated W rounded to 16 bits.  Returns (W, m, v, W16)."""
+    W = np.array(W, dtype=np.float32, copy=True)
+    m = np.array(m, dtype=np.float32, copy=True)
+    v = np.array(v, dtype=np.float32, copy=True)
+    g = _as_input(g, gtype)
+    if not (W.shape == m.shape == v.shape and g.size == W.size):
+        raise ValueError("W, g, m, v must have the same number of elements")
+    W16 = np.zeros(W.shape, dtype=np.uint16) if w16 is not None else None
+    c = np.array([clip], dtype=np.float32) if clip is not None else None
+    rc = _load().oracle_adamw_ex(_ptr(W), _ptr(g), _DTYPES[gtype], _ptr(m), _ptr(v), W.size,
+                                 lr, b1, b2, eps, wd, int(step), inv_scale,
+                                 _ptr(c) if c is not None else None, int(bool(skip)),
+                                 _ptr(W16) if W16 is not None else None,
+                                 _DTYPES[w16] if w16 is not None else 0)
+    if rc != 0:
+        raise ValueError("adamw_ex: invalid arguments (step=%r, b1=%r, b2=%r, w16=%r)"
+                         % (step, b1, b2, w16))
+    return W, m, v, W16

@@ -35,6 +35,18 @@
  *    Algorithm" (the same update written as θ − η·m̂/(√v̂+ε) − η·λ·θ).
  *    The oracle is a scalar fp32 loop.  The bias corrections are evaluated
  *    once per call in double and rounded to float once.
+ *
+ *  - The training step's optional parts around that update, in the order of
+ *    the pages' complete loop ("GPU 优化实战 Part 2", section "完整训练循环
+ *    （整合一切）": unscale to fp32, optional clipping of the gradient by a
+ *    factor, the AdamW step on the fp32 master weights, then a 16-bit copy of
+ *    the updated weights for the next forward pass; section "混合精度训练
+ *    （FP16 / BF16）" for the 16-bit forward weights):
+ *        g  = (float(g_in) * inv_scale) * clip          (clip given: two roundings)
+ *        ... the AdamW update above ...
+ *        W16 = round_to_nearest_even(W) as fp16 or bf16
+ *    and a skip flag that leaves every array untouched.  The 16-bit roundings
+ *    are written from the IEEE definitions below.
  */
 #include <math.h>
 #include <stdint.h>
@@ -177,6 +189,56 @@ static float grad_f32(const void *g, int gtype, int64_t i)
  * (step < 1, or a beta outside [0,1) which makes a bias correction zero or
  * meaningless).
  */
+/* ---- 16-bit roundings of an fp32 value (IEEE round to nearest, ties to even) ---- */
+
+/* bf16 keeps the upper 16 bits of the binary32 pattern: add half of the
+ * dropped part, plus one when the kept part is odd (ties to even), then
+ * truncate; a carry into the exponent is the correct rounding, including to
+ * infinity.  NaN stays NaN (quiet bit set, sign kept). */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t b;
+    memcpy(&b, &f, sizeof b);
+    if ((b & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((b >> 16) | 0x0040u);
+    const uint32_t lsb = (b >> 16) & 1u;
+    return (uint16_t)((b + 0x7fffu + lsb) >> 16);
+}
+
+/* binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits; normal values
+ * 2^-14 <= |x| <= 65504, subnormals k*2^-24.  Computed on the exact value in
+ * double with nearbyint (round to nearest even in the default mode). */
+uint16_t oracle_f32_to_f16(float f)
+{
+    const uint16_t sign = signbit(f) ? 0x8000u : 0u;
+    if (isnan(f))
+        return (uint16_t)(sign | 0x7e00u);
+    const double a = fabs((double)f);
+    if (isinf(f))
+        return (uint16_t)(sign | 0x7c00u);
+    if (a < ldexp(1.0, -14)) {                 /* subnormal range: k * 2^-24 */
+        const double k = nearbyint(ldexp(a, 24)); /* exact scaling; k <= 1024 */
+        return (uint16_t)(sign | (uint16_t)k); /* k == 1024 is the smallest normal */
+    }
+    int e;
+    (void)frexp(a, &e);                        /* a = fr * 2^e, 0.5 <= fr < 1 */
+    e -= 1;                                    /* 2^e <= a < 2^(e+1) */
+    double q = nearbyint(ldexp(a, 10 - e));    /* 1024 <= q <= 2048 */
+    if (q >= 2048.0) {
+        q = 1024.0;
+        e += 1;
+    }
+    if (e > 15)
+        return (uint16_t)(sign | 0x7c00u);     /* rounds past 65504: infinity */
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(q - 1024.0));
+}
+
+void oracle_round16(const float *in, int64_t n, int type, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = type == ORACLE_BF16 ? oracle_f32_to_bf16(in[i]) : oracle_f32_to_f16(in[i]);
+}
+
 int oracle_adamw(float *W, const void *g, int gtype, float *m, float *v, int64_t n,
                  float lr, float b1, float b2, float eps, float wd, int step,
                  float inv_scale)
@@ -193,6 +255,37 @@ int oracle_adamw(float *W, const void *g, int gtype, float *m, float *v, int64_t
         float mh = m[i] / bc1;
         float vh = v[i] / bc2;
         W[i] = W[i] - lr * (mh / (sqrtf(vh) + eps) + wd * W[i]);
+    }
+    return 0;
+}
+
+/* The update with the loop's optional parts: clip (NULL: none) multiplies the
+ * unscaled gradient, skip != 0 leaves W, m, v and W16 untouched, W16 (NULL:
+ * none) receives the updated W rounded to w16type (ORACLE_BF16 / ORACLE_F16). */
+int oracle_adamw_ex(float *W, const void *g, int gtype, float *m, float *v, int64_t n,
+                    float lr, float b1, float b2, float eps, float wd, int step,
+                    float inv_scale, const float *clip, int skip, uint16_t *W16, int w16type)
+{
+    if (step < 1 || !(b1 >= 0.0f && b1 < 1.0f) || !(b2 >= 0.0f && b2 < 1.0f) || n < 0)
+        return -1;
+    if (W16 && w16type != ORACLE_BF16 && w16type != ORACLE_F16)
+        return -1;
+    if (skip)
+        return 0;
+    const float bc1 = (float)(1.0 - pow((double)b1, (double)step));
+    const float bc2 = (float)(1.0 - pow((double)b2, (double)step));
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float gi = grad_f32(g, gtype, i) * inv_scale;
+        if (clip)
+            gi = gi * *clip;
+        m[i] = b1 * m[i] + (1.0f - b1) * gi;
+        v[i] = b2 * v[i] + (1.0f - b2) * gi * gi;
+        float mh = m[i] / bc1;
+        float vh = v[i] / bc2;
+        W[i] = W[i] - lr * (mh / (sqrtf(vh) + eps) + wd * W[i]);
+        if (W16)
+            W16[i] = w16type == ORACLE_BF16 ? oracle_f32_to_bf16(W[i]) : oracle_f32_to_f16(W[i]);
     }
     return 0;
 }
