@@ -32,6 +32,7 @@ extern "C" {
 /* element type of X, W, dY and dX in lin_bwd() */
 #define LB_F32 0  /* IEEE binary32 */
 #define LB_BF16 1 /* bfloat16 (upper half of a binary32) */
+#define LB_F16 2  /* IEEE binary16 (gradients and 16-bit weight copies only) */
 
 /* return codes */
 #define LB_OK 0
@@ -106,6 +107,36 @@ int adamw_step_f16(float *W, const uint16_t *grad, float *m, float *v, int64_t n
 int adamw_step_bf16(float *W, const uint16_t *grad, float *m, float *v, int64_t n,
                     float lr, float b1, float b2, float eps, float wd, int step,
                     float inv_scale);
+
+/*
+ * adamw_step_ex -- the AdamW pass with the optional parts of the training
+ * step around it, in the order of the pages' complete loop ("GPU 优化实战
+ * Part 2", section "完整训练循环（整合一切）": unscale, clip, AdamW on the fp32
+ * master weights, 16-bit copy of the updated weights for the next forward
+ * pass; section "混合精度训练（FP16 / BF16）" for the 16-bit forward weights).
+ * Per parameter:
+ *   g   = (float(grad) * inv_scale) * clip        clip = *d_clip, or 1 if NULL
+ *   ... the AdamW update of adamw_step ...
+ *   W16 = W rounded to nearest even, as w16_dtype  (if W16 is not NULL)
+ * and nothing at all is written when d_skip is not NULL and *d_skip != 0.
+ *
+ *   W, m, v, grad, n, lr .. inv_scale   as for adamw_step
+ *   grad_dtype  LB_F32, LB_F16 or LB_BF16 (element type of grad)
+ *   d_clip      device pointer to one float, read by the kernel (so a factor
+ *               computed on the device needs no host round trip), or NULL
+ *   d_skip      device pointer to one int32, read by the kernel, or NULL
+ *   W16         [n] 16-bit copy of the updated W (written), or NULL
+ *   w16_dtype   LB_BF16 or LB_F16; ignored when W16 is NULL
+ *
+ * All pointers are device memory owned by the caller; W16 must not alias the
+ * other buffers.  Any alignment is accepted (16-byte aligned buffers take the
+ * vector path).  Asynchronous on the thread's stream, like adamw_step.
+ * Errors: those of adamw_step; LB_EDTYPE for another grad_dtype, or a W16
+ * with a w16_dtype other than LB_BF16 / LB_F16.
+ */
+int adamw_step_ex(float *W, const void *grad, int grad_dtype, float *m, float *v, int64_t n,
+                  float lr, float b1, float b2, float eps, float wd, int step, float inv_scale,
+                  const float *d_clip, const int32_t *d_skip, void *W16, int w16_dtype);
 
 /*
  * lb_set_stream -- the HIP stream (a hipStream_t, passed as void*) on which

@@ -15,7 +15,7 @@ __all__ = ["lin_bwd", "adamw_step", "adamw_step_f16", "adamw_step_bf16", "lb_set
            "lb_last_error", "lb_version", "library", "LIB_PATH", "LB_F32", "LB_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinbwd.so")
-LB_F32, LB_BF16 = 0, 1
+LB_F32, LB_BF16, LB_F16 = 0, 1, 2
 LB_OK, LB_EINVAL, LB_EDTYPE, LB_EHIP = 0, -1, -2, -4
 
 _lib = None
@@ -37,6 +37,9 @@ def library() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, i64, f32, f32, f32, f32, f32, i32, f32]
         fn.restype = i32
+    lib.adamw_step_ex.argtypes = [vp, vp, i32, vp, vp, i64, f32, f32, f32, f32, f32, i32, f32,
+                                  vp, vp, vp, i32]
+    lib.adamw_step_ex.restype = i32
     lib.lb_set_stream.argtypes = [vp]
     lib.lb_set_stream.restype = i32
     lib.lb_last_error.argtypes = []
@@ -163,3 +166,41 @@ def adamw_step_bf16(W, grad, m, v, lr, b1, b2, eps, wd, step, inv_scale=1.0) -> 
     if grad.dtype != torch.bfloat16:
         raise TypeError("grad must be bfloat16")
     _adamw("adamw_step_bf16", W, grad, m, v, lr, b1, b2, eps, wd, step, inv_scale)
+
+
+def adamw_step_ex(W, grad, m, v, lr, b1, b2, eps, wd, step, inv_scale=1.0, clip=None, skip=None,
+                  w16=None) -> None:
+    """The AdamW step with the training loop's optional parts (C: adamw_step_ex).
+
+    grad: float32, float16 or bfloat16.  clip: a one-element float32 GPU tensor whose
+    value multiplies the unscaled gradient, or None.  skip: a one-element int32 GPU
+    tensor; when nonzero the step writes nothing.  w16: a bfloat16 or float16 tensor
+    receiving the updated W rounded to nearest even, or None.  The kernel reads clip and
+    skip itself, so factors computed on the GPU need no synchronisation.
+    """
+    import torch
+    gd = {torch.float32: LB_F32, torch.float16: LB_F16, torch.bfloat16: LB_BF16}.get(grad.dtype)
+    if gd is None:
+        raise TypeError("grad must be float32, float16 or bfloat16")
+    for t, nm in ((W, "W"), (m, "m"), (v, "v")):
+        if t.dtype != torch.float32:
+            raise TypeError("%s must be float32" % nm)
+    n = W.numel()
+    if m.numel() != n or v.numel() != n or grad.numel() != n:
+        raise ValueError("W, grad, m, v must have the same number of elements")
+    if clip is not None and (clip.dtype != torch.float32 or clip.numel() != 1):
+        raise TypeError("clip must be a one-element float32 tensor")
+    if skip is not None and (skip.dtype != torch.int32 or skip.numel() != 1):
+        raise TypeError("skip must be a one-element int32 tensor")
+    wd16 = 0
+    if w16 is not None:
+        wd16 = {torch.bfloat16: LB_BF16, torch.float16: LB_F16}.get(w16.dtype)
+        if wd16 is None:
+            raise TypeError("w16 must be bfloat16 or float16")
+        if w16.numel() != n:
+            raise ValueError("w16 must have n elements")
+    dev = _device_of([W, grad, m, v, clip, skip, w16])
+    _use_current_stream(dev)
+    rc = library().adamw_step_ex(_ptr(W), _ptr(grad), gd, _ptr(m), _ptr(v), n, lr, b1, b2, eps, wd,
+                                 int(step), inv_scale, _ptr(clip), _ptr(skip), _ptr(w16), wd16)
+    _check(rc, "adamw_step_ex")

@@ -29,9 +29,10 @@ int hip_fail(const char *what, hipError_t e) {
 
 bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; } // false for NaN
 
-template <lb::GradType GT>
-int adamw_impl(const char *name, float *W, const void *g, float *m, float *v, int64_t n, float lr,
-               float b1, float b2, float eps, float wd, int step, float inv_scale) {
+int adamw_impl(const char *name, lb::GradType gt, float *W, const void *g, float *m, float *v, int64_t n,
+               float lr, float b1, float b2, float eps, float wd, int step, float inv_scale,
+               const float *clip = nullptr, const int32_t *skip = nullptr, void *W16 = nullptr,
+               lb::ShadowType shadow = lb::SHADOW_NONE) {
     tl_error.clear();
     if (n < 0)
         return fail(LB_EINVAL, "%s: n = %lld is negative", name, (long long)n);
@@ -43,6 +44,8 @@ int adamw_impl(const char *name, float *W, const void *g, float *m, float *v, in
         return LB_OK;
     if (!W || !g || !m || !v)
         return fail(LB_EINVAL, "%s: NULL buffer with n = %lld", name, (long long)n);
+    if (W16 && (W16 == (void *)W || W16 == g || W16 == (void *)m || W16 == (void *)v))
+        return fail(LB_EINVAL, "%s: the 16-bit copy must not alias W, grad, m or v", name);
     lb::AdamWArgs a;
     a.W = W;
     a.g = g;
@@ -59,7 +62,10 @@ int adamw_impl(const char *name, float *W, const void *g, float *m, float *v, in
     a.bc1 = (float)(1.0 - std::pow((double)b1, (double)step));
     a.bc2 = (float)(1.0 - std::pow((double)b2, (double)step));
     a.inv_scale = inv_scale;
-    hipError_t e = lb::launch_adamw(a, GT, tl_stream);
+    a.clip = clip;
+    a.skip = skip;
+    a.W16 = static_cast<uint16_t *>(W16);
+    hipError_t e = lb::launch_adamw(a, gt, W16 ? shadow : lb::SHADOW_NONE, tl_stream);
     if (e != hipSuccess)
         return hip_fail(name, e);
     return LB_OK;
@@ -104,20 +110,44 @@ int lin_bwd(const void *X, const void *W, const void *dY, void *dX, float *dW, i
 
 int adamw_step(float *W, const float *grad, float *m, float *v, int64_t n, float lr, float b1, float b2,
                float eps, float wd, int step, float inv_scale) {
-    return adamw_impl<lb::GRAD_F32>("adamw_step", W, grad, m, v, n, lr, b1, b2, eps, wd, step,
-                                    inv_scale);
+    return adamw_impl("adamw_step", lb::GRAD_F32, W, grad, m, v, n, lr, b1, b2, eps, wd, step, inv_scale);
 }
 
 int adamw_step_f16(float *W, const uint16_t *grad, float *m, float *v, int64_t n, float lr, float b1,
                    float b2, float eps, float wd, int step, float inv_scale) {
-    return adamw_impl<lb::GRAD_F16>("adamw_step_f16", W, grad, m, v, n, lr, b1, b2, eps, wd, step,
-                                    inv_scale);
+    return adamw_impl("adamw_step_f16", lb::GRAD_F16, W, grad, m, v, n, lr, b1, b2, eps, wd, step,
+                      inv_scale);
 }
 
 int adamw_step_bf16(float *W, const uint16_t *grad, float *m, float *v, int64_t n, float lr, float b1,
                     float b2, float eps, float wd, int step, float inv_scale) {
-    return adamw_impl<lb::GRAD_BF16>("adamw_step_bf16", W, grad, m, v, n, lr, b1, b2, eps, wd, step,
-                                     inv_scale);
+    return adamw_impl("adamw_step_bf16", lb::GRAD_BF16, W, grad, m, v, n, lr, b1, b2, eps, wd, step,
+                      inv_scale);
+}
+
+int adamw_step_ex(float *W, const void *grad, int grad_dtype, float *m, float *v, int64_t n, float lr,
+                  float b1, float b2, float eps, float wd, int step, float inv_scale, const float *d_clip,
+                  const int32_t *d_skip, void *W16, int w16_dtype) {
+    tl_error.clear();
+    lb::GradType gt;
+    switch (grad_dtype) {
+    case LB_F32: gt = lb::GRAD_F32; break;
+    case LB_F16: gt = lb::GRAD_F16; break;
+    case LB_BF16: gt = lb::GRAD_BF16; break;
+    default:
+        return fail(LB_EDTYPE, "adamw_step_ex: grad_dtype %d is not LB_F32, LB_F16 or LB_BF16", grad_dtype);
+    }
+    lb::ShadowType sh = lb::SHADOW_NONE;
+    if (W16) {
+        if (w16_dtype == LB_BF16)
+            sh = lb::SHADOW_BF16;
+        else if (w16_dtype == LB_F16)
+            sh = lb::SHADOW_F16;
+        else
+            return fail(LB_EDTYPE, "adamw_step_ex: w16_dtype %d is not LB_BF16 or LB_F16", w16_dtype);
+    }
+    return adamw_impl("adamw_step_ex", gt, W, grad, m, v, n, lr, b1, b2, eps, wd, step, inv_scale, d_clip,
+                      d_skip, W16, sh);
 }
 
 int lb_set_stream(void *hip_stream) {

@@ -9,6 +9,8 @@ namespace lb {
 // ---- fused unscale + AdamW ---------------------------------------------
 enum GradType { GRAD_F32 = 0, GRAD_F16 = 1, GRAD_BF16 = 2 };
 
+enum ShadowType { SHADOW_NONE = 0, SHADOW_BF16 = 1, SHADOW_F16 = 2 };
+
 struct AdamWArgs {
     float *W;
     const void *g;
@@ -19,9 +21,12 @@ struct AdamWArgs {
     float one_minus_b1, one_minus_b2; // 1 - b, rounded to float
     float bc1, bc2;                   // 1 - b^t, computed in double, rounded once
     float inv_scale;
+    const float *clip;   // device scalar multiplying the unscaled gradient, or null
+    const int32_t *skip; // device flag: nonzero -> write nothing, or null
+    uint16_t *W16;       // 16-bit copy of the updated W, or null (then shadow = NONE)
 };
 
-hipError_t launch_adamw(const AdamWArgs &a, GradType gt, hipStream_t s);
+hipError_t launch_adamw(const AdamWArgs &a, GradType gt, ShadowType shadow, hipStream_t s);
 
 // ---- Linear backward ----------------------------------------------------
 struct LinBwdArgs {

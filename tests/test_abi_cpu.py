@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("lin_bwd", "adamw_step", "adamw_step_f16", "adamw_step_bf16",
+    for want in ("lin_bwd", "adamw_step", "adamw_step_f16", "adamw_step_bf16", "adamw_step_ex",
                  "lb_set_stream", "lb_last_error", "lb_version"):
         assert want in names
 
@@ -108,3 +108,32 @@ def test_python_binding_rejects_cpu_tensors():
     w = torch.zeros(8)
     with pytest.raises(TypeError):
         lb.adamw_step(w, w.to(torch.int32), w, w, 1e-3, 0.9, 0.99, 1e-8, 0.0, 1)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(gd=3), -2), (dict(gd=-1), -2),                           # unknown gradient dtype
+    (dict(w16=16, wd16=0), -2), (dict(w16=16, wd16=7), -2),        # 16-bit copy must be bf16/f16
+    (dict(step=0), -1), (dict(b2=1.0), -1), (dict(n=-2), -1),
+    (dict(n=10), -1),                                              # NULL buffers with n > 0
+    (dict(n=0), 0), (dict(n=0, w16=16, wd16=1), 0),                # empty: no-op
+])
+def test_adamw_ex_rejects_on_host(over, code):
+    a = dict(n=0, gd=1, step=1, b1=0.9, b2=0.999, w16=NULL, wd16=0)
+    a.update(over)
+    rc = lb.library().adamw_step_ex(NULL, NULL, a["gd"], NULL, NULL, a["n"], 1e-3, a["b1"], a["b2"],
+                                    1e-8, 0.01, a["step"], 1.0, NULL, NULL, a["w16"], a["wd16"])
+    assert rc == code
+    assert (lb.lb_last_error() != "") == (code != 0)
+
+
+def test_adamw_ex_binding_checks_types():
+    import torch
+    w = torch.zeros(8)
+    with pytest.raises(TypeError):
+        lb.adamw_step_ex(w, w.to(torch.int32), w, w, 1e-3, 0.9, 0.99, 1e-8, 0.0, 1)
+    with pytest.raises(TypeError):
+        lb.adamw_step_ex(w, w, w, w, 1e-3, 0.9, 0.99, 1e-8, 0.0, 1, w16=torch.zeros(8))
+    with pytest.raises(TypeError):
+        lb.adamw_step_ex(w, w, w, w, 1e-3, 0.9, 0.99, 1e-8, 0.0, 1, clip=torch.zeros(2))
+    with pytest.raises(TypeError):
+        lb.adamw_step_ex(w, w, w, w, 1e-3, 0.9, 0.99, 1e-8, 0.0, 1, skip=torch.zeros(1))

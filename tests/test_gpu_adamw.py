@@ -149,3 +149,121 @@ def test_run_twice_is_bitwise():
     b = gpu_steps(case, [1, 2])
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+# ---- adamw_step_ex: clip factor, skip flag, 16-bit copy of the updated W ----
+
+W16T = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _ex_gpu(case, step, clip=None, skip=None, w16=None, offset=0, w16_fill=0x1234):
+    def place(t, dt=None):
+        t = t.to(DEV)
+        buf = torch.empty(t.numel() + offset, dtype=t.dtype, device=DEV)
+        view = buf[offset:]
+        view.copy_(t)
+        return view
+    W, m, v, g = (place(t) for t in (case.W, case.m, case.v, case.g))
+    h = None
+    if w16 is not None:
+        hb = torch.full((W.numel() + offset,), w16_fill, dtype=torch.int16, device=DEV)
+        h = hb[offset:].view(W16T[w16])
+    c = torch.tensor([clip], dtype=torch.float32, device=DEV) if clip is not None else None
+    s = torch.tensor([skip], dtype=torch.int32, device=DEV) if skip is not None else None
+    lb.adamw_step_ex(W, g, m, v, case.lr, case.b1, case.b2, case.eps, case.wd, step,
+                     case.inv_scale, clip=c, skip=s, w16=h)
+    torch.cuda.synchronize()
+    return (W.cpu().numpy(), m.cpu().numpy(), v.cpu().numpy(),
+            None if h is None else bits(h))
+
+
+def _ex_ref(case, step, clip=None, skip=False, w16=None):
+    return oracle.adamw_ex(case.W.numpy(), synth.bits(case.g), case.m.numpy(), case.v.numpy(),
+                           case.gdtype, case.lr, case.b1, case.b2, case.eps, case.wd, step,
+                           case.inv_scale, clip=clip, skip=skip, w16=w16)
+
+
+def _check_shadow(W_gpu, h_gpu, w16):
+    """The 16-bit copy is the GPU's own updated W rounded to nearest even."""
+    ref = oracle.round16(W_gpu, w16)
+    nan = np.isnan(W_gpu)
+    assert np.array_equal(h_gpu[~nan], ref[~nan])
+    expm = 0x7F80 if w16 == "bf16" else 0x7C00
+    assert ((h_gpu[nan].astype(np.int64) & expm) == expm).all()
+
+
+@pytest.mark.parametrize("w16", [None, "bf16", "f16"])
+@pytest.mark.parametrize("gdtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("clip", [None, 0.37, 1.0])
+def test_ex_matches_oracle(gdtype, w16, clip):
+    n = 100003
+    case = synth.adamw_case(n, gdtype, g_scale=1.0 if gdtype == "f32" else 1024.0, seed=21)
+    got = _ex_gpu(case, 4, clip=clip, skip=0 if clip == 1.0 else None, w16=w16)
+    ref = _ex_ref(case, 4, clip=clip, w16=w16)
+    compare(got[:3], ref[:3])
+    if w16 is not None:
+        _check_shadow(got[0], got[3], w16)
+        assert np.array_equal(got[3], ref[3])  # GPU and oracle W agree bit for bit here
+
+
+def test_ex_clip_one_equals_plain_step():
+    case = synth.adamw_case(65539, "bf16", seed=22)
+    a = _ex_gpu(case, 2, clip=1.0)
+    b = gpu_steps(case, [2])
+    for x, y in zip(a[:3], b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("w16", [None, "bf16"])
+def test_ex_skip_writes_nothing(w16):
+    case = synth.adamw_case(70001, "f16", seed=23)
+    got = _ex_gpu(case, 3, clip=0.5, skip=1, w16=w16, w16_fill=0x5A5A)
+    assert np.array_equal(got[0], case.W.numpy())
+    assert np.array_equal(got[1], case.m.numpy())
+    assert np.array_equal(got[2], case.v.numpy())
+    if w16 is not None:
+        assert (got[3] == 0x5A5A).all()
+
+
+@pytest.mark.parametrize("w16", ["bf16", "f16"])
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 4099])
+def test_ex_ragged_and_misaligned(w16, n):
+    case = synth.adamw_case(n, "bf16", seed=24 + n)
+    for offset in (0, 1):
+        got = _ex_gpu(case, 1, clip=0.8, w16=w16, offset=offset)
+        ref = _ex_ref(case, 1, clip=0.8, w16=w16)
+        compare(got[:3], ref[:3])
+        _check_shadow(got[0], got[3], w16)
+
+
+def test_ex_shadow_overflow_and_nan():
+    case = synth.adamw_case(64, "f32", g_scale=1.0, seed=25)
+    case.W[0] = 70000.0      # beyond fp16: the copy is inf
+    case.W[1] = 65504.0
+    case.g[2] = float("nan")
+    got = _ex_gpu(case, 1, w16="f16")
+    ref = _ex_ref(case, 1, w16="f16")
+    compare(got[:3], ref[:3])
+    _check_shadow(got[0], got[3], "f16")
+    assert got[3][0] == 0x7C00
+
+
+def test_ex_large_sampled():
+    """2^26 params, fp16 gradients x1024, clip 0.61, bf16 copy; oracle on a sample."""
+    n = 1 << 26
+    case = synth.adamw_2p28(seed=1, n=n, device=DEV)
+    rng = np.random.default_rng(3)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 1 << 18), np.arange(n - 100, n)]))
+    tidx = torch.from_numpy(idx).to(DEV)
+    before = tuple(t[tidx].cpu() for t in (case.W, case.m, case.v, case.g))
+    h = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    c = torch.tensor([0.61], dtype=torch.float32, device=DEV)
+    lb.adamw_step_ex(case.W, case.g, case.m, case.v, case.lr, case.b1, case.b2, case.eps, case.wd,
+                     5, case.inv_scale, clip=c, w16=h)
+    torch.cuda.synchronize()
+    ref = oracle.adamw_ex(before[0].numpy(), synth.bits(before[3]), before[1].numpy(),
+                          before[2].numpy(), case.gdtype, case.lr, case.b1, case.b2, case.eps,
+                          case.wd, 5, case.inv_scale, clip=0.61, w16="bf16")
+    got = tuple(t[tidx].cpu().numpy() for t in (case.W, case.m, case.v))
+    compare(got, ref[:3])
+    _check_shadow(got[0], bits(h[tidx]), "bf16")
