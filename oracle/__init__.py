@@ -81,6 +81,8 @@ def _load():
     lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
     lib.oracle_f32_to_f16.argtypes = [f32]
     lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+    lib.oracle_grad_norm.argtypes = [vp, i32, i64, f32, f32, vp, vp]
+    lib.oracle_grad_norm.restype = None
     lib.oracle_round16.argtypes = [vp, i64, i32, vp]
     lib.oracle_round16.restype = None
     _lib = lib
@@ -219,3 +221,13 @@ def adamw_ex(W, g, m, v, gtype: str, lr, b1, b2, eps, wd, step, inv_scale,
         raise ValueError("adamw_ex: invalid arguments (step=%r, b1=%r, b2=%r, w16=%r)"
                          % (step, b1, b2, w16))
     return W, m, v, W16
+
+
+def grad_norm(g, gtype: str, inv_scale=1.0, max_norm=0.0):
+    """(norm, clip factor, found_inf) of the unscaled gradient float(g)*inv_scale."""
+    g = _as_input(g, gtype)
+    out = np.zeros(2, dtype=np.float32)
+    bad = np.zeros(1, dtype=np.int32)
+    _load().oracle_grad_norm(_ptr(g), _DTYPES[gtype], g.size, inv_scale, max_norm, _ptr(out),
+                             _ptr(bad))
+    return float(out[0]), float(out[1]), bool(bad[0])

@@ -47,6 +47,14 @@
  *        W16 = round_to_nearest_even(W) as fp16 or bf16
  *    and a skip flag that leaves every array untouched.  The 16-bit roundings
  *    are written from the IEEE definitions below.
+ *
+ *  - The loop's gradient clipping (same section, its step 7: the L2 norm of
+ *    the unscaled fp32 gradient; when it exceeds max_norm the gradient is
+ *    scaled by max_norm / norm):
+ *        g32  = float(g_in) * inv_scale                       (fp32, as above)
+ *        norm = sqrt( sum g32^2 )     squares and sum in fp64, rounded to fp32 once
+ *        clip = norm > max_norm ? max_norm / norm : 1         (fp32; max_norm <= 0: 1)
+ *        found_inf = some g32 is inf or NaN
  */
 #include <math.h>
 #include <stdint.h>
@@ -257,6 +265,26 @@ int oracle_adamw(float *W, const void *g, int gtype, float *m, float *v, int64_t
         W[i] = W[i] - lr * (mh / (sqrtf(vh) + eps) + wd * W[i]);
     }
     return 0;
+}
+
+/* Global L2 norm of the unscaled gradient, its clip factor and an inf/NaN
+ * flag: out[0] = norm, out[1] = clip factor, *found_inf = 0 or 1.  A plain
+ * sequential fp64 sum of the exact squares of the fp32 values. */
+void oracle_grad_norm(const void *g, int gtype, int64_t n, float inv_scale, float max_norm,
+                      float *out, int *found_inf)
+{
+    double sum = 0.0;
+    int bad = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const float x = grad_f32(g, gtype, i) * inv_scale;
+        if (!isfinite(x))
+            bad = 1;
+        sum += (double)x * (double)x;
+    }
+    const float norm = (float)sqrt(sum);
+    out[0] = norm;
+    out[1] = (max_norm > 0.0f && norm > max_norm) ? max_norm / norm : 1.0f;
+    *found_inf = bad;
 }
 
 /* The update with the loop's optional parts: clip (NULL: none) multiplies the
