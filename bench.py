@@ -33,6 +33,8 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 ADAMW_BYTES_16BIT_GRAD = 26   # read g(2) W m v (12), write W m v (12)
 ADAMW_BYTES_F32_GRAD = 28
+ADAMW_EX_BYTES_16BIT_GRAD_BF16_COPY = 28   # the 26 above + the bf16 copy of W (2)
+GRAD_NORM_BYTES_16BIT = 2                  # reads the gradient once
 
 
 def ideal_intensity(M, K, N, bytes_per_elem=2):
@@ -249,6 +251,49 @@ def bench_adamw(n, steps, warmup, seed):
             "gparams_per_s": round(n / (ms * 1e-3) / 1e9, 2)}
 
 
+def bench_clipped_step(n, steps, warmup, seed):
+    """grad_norm then adamw_step_ex (clip factor and skip flag from the norm, bf16 copy of W)."""
+    import torch
+
+    import linear_layer_backward_bwd_amd as lb
+    import synth
+    case = synth.adamw_2p28(seed=seed, n=n, device="cuda")
+    w16 = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(2, dtype=torch.float32, device="cuda")
+    found = torch.empty(1, dtype=torch.int32, device="cuda")
+    norm = lambda: lb.grad_norm(case.g, case.inv_scale, 1.0, out=out, found_inf=found)
+    upd = lambda t: lb.adamw_step_ex(case.W, case.g, case.m, case.v, case.lr, case.b1, case.b2,
+                                     case.eps, case.wd, t, case.inv_scale, clip=out[1:2],
+                                     skip=found, w16=w16)
+    for i in range(warmup):
+        norm()
+        upd(1 + i % 10)
+    # each kernel back to back (its own rate), then the pair as one step; the
+    # norm's launches are shorter than the binding's host time, so they are
+    # timed as one batch between two events (the queue never drains)
+    timer = Timer(["norm", "adamw_ex", "step"])
+    timer.run("norm", lambda: [norm() for _ in range(steps)])
+    for i in range(steps):
+        timer.run("adamw_ex", lambda: upd(1 + i % 10))
+    for i in range(steps):
+        timer.run("step", lambda: (norm(), upd(1 + i % 10)))
+    timer.collect()
+    norm_ms = timer.ms["norm"] / steps
+    upd_ms = timer.ms["adamw_ex"] / steps
+    step_ms = timer.ms["step"] / steps
+    norm_gbps = GRAD_NORM_BYTES_16BIT * n / (norm_ms * 1e-3) / 1e9
+    upd_gbps = ADAMW_EX_BYTES_16BIT_GRAD_BF16_COPY * n / (upd_ms * 1e-3) / 1e9
+    return {"n": n, "grad": "f16", "copy": "bf16",
+            "grad_norm": {"ms": round(norm_ms, 4), "gbps": round(norm_gbps, 1),
+                          "frac_of_hbm_peak": round(norm_gbps / PEAK_HBM_GBPS, 4),
+                          "bytes_per_param": GRAD_NORM_BYTES_16BIT},
+            "adamw_step_ex": {"ms": round(upd_ms, 4), "gbps": round(upd_gbps, 1),
+                              "frac_of_hbm_peak": round(upd_gbps / PEAK_HBM_GBPS, 4),
+                              "bytes_per_param": ADAMW_EX_BYTES_16BIT_GRAD_BF16_COPY},
+            "step_ms": round(step_ms, 4),
+            "gparams_per_s": round(n / (step_ms * 1e-3) / 1e9, 2)}
+
+
 def cpu_baseline(cases, opt, target_s=12.0):
     """The CPU oracle on a bounded sample of the block workload, extrapolated to one step."""
     import numpy as np
@@ -303,7 +348,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the M=32 / M=2048 / 2^28-param AdamW figures")
-    ap.add_argument("--only", choices=["block", "m32", "m2048", "adamw", "copycal"], default=None,
+    ap.add_argument("--only", choices=["block", "m32", "m2048", "adamw", "clipped", "copycal"],
+                    default=None,
                     help="time one workload only (for profiling); copycal = 1 GiB copies for "
                          "scaling HBM byte counters")
     args = ap.parse_args(argv)
@@ -324,6 +370,9 @@ def main(argv=None):
         return 0
     if args.only == "adamw":
         print(json.dumps(bench_adamw(1 << 28, args.steps, args.warmup, args.seed)), flush=True)
+        return 0
+    if args.only == "clipped":
+        print(json.dumps(bench_clipped_step(1 << 28, args.steps, args.warmup, args.seed)), flush=True)
         return 0
     if args.only == "copycal":
         print(json.dumps(copy_calibration(args.steps)), flush=True)
@@ -351,6 +400,7 @@ def main(argv=None):
             "lin_bwd_M32_K4096_N4096": bench_linear(32, 4096, 4096, 50, 5, args.seed),
             "lin_bwd_M2048_K4096_N4096": bench_linear(2048, 4096, 4096, 50, 5, args.seed),
             "adamw_2p28_f16": bench_adamw(1 << 28, 10, 2, args.seed),
+            "grad_norm_adamw_ex_2p28_f16": bench_clipped_step(1 << 28, 10, 2, args.seed),
         }
     print(json.dumps(out), flush=True)
     return 0

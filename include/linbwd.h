@@ -139,6 +139,33 @@ int adamw_step_ex(float *W, const void *grad, int grad_dtype, float *m, float *v
                   const float *d_clip, const int32_t *d_skip, void *W16, int w16_dtype);
 
 /*
+ * grad_norm -- the L2 norm of the unscaled gradient and the clip factor of the
+ * pages' complete loop ("GPU 优化实战 Part 2", section "完整训练循环（整合
+ * 一切）": the norm of the fp32 gradient, and a scale of max_norm / norm when it
+ * exceeds max_norm), with an inf/NaN flag, written to device memory so that
+ * adamw_step_ex can consume them without a host round trip:
+ *   g32 = float(grad[i]) * inv_scale                  (fp32)
+ *   d_out[0] = sqrt(sum g32^2)      exact squares summed in fp64, rounded once
+ *   d_out[1] = d_out[0] > max_norm ? max_norm / d_out[0] : 1    (max_norm <= 0: 1)
+ *   *d_found_inf = 1 if some g32 is inf or NaN, else 0         (if not NULL)
+ * Pass d_out + 1 as adamw_step_ex's d_clip and d_found_inf as its d_skip.
+ *
+ *   grad         [n] device, read only; grad_dtype LB_F32, LB_F16 or LB_BF16
+ *   d_out        device float[2], written
+ *   d_found_inf  device int32, written, or NULL
+ *
+ * The summation order is fixed for a given n and 16-byte alignment of grad
+ * (the result is reproducible).
+ * Uses a small library-owned workspace (192 KiB per device, allocated on first
+ * use and kept until the process ends); calls that overlap on one device race.
+ * Asynchronous on the thread's stream.  Errors: LB_EDTYPE for another
+ * grad_dtype; LB_EINVAL for n < 0, NULL d_out, or NULL grad with n > 0;
+ * LB_EHIP when the workspace cannot be allocated or a launch fails.
+ */
+int grad_norm(const void *grad, int grad_dtype, int64_t n, float inv_scale, float max_norm,
+              float *d_out, int32_t *d_found_inf);
+
+/*
  * lb_set_stream -- the HIP stream (a hipStream_t, passed as void*) on which
  * the calling thread's later calls enqueue their kernels; NULL selects the
  * null stream.  The setting is per thread.  Returns LB_OK.

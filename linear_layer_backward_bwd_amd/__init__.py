@@ -40,6 +40,8 @@ def library() -> ctypes.CDLL:
     lib.adamw_step_ex.argtypes = [vp, vp, i32, vp, vp, i64, f32, f32, f32, f32, f32, i32, f32,
                                   vp, vp, vp, i32]
     lib.adamw_step_ex.restype = i32
+    lib.grad_norm.argtypes = [vp, i32, i64, f32, f32, vp, vp]
+    lib.grad_norm.restype = i32
     lib.lb_set_stream.argtypes = [vp]
     lib.lb_set_stream.restype = i32
     lib.lb_last_error.argtypes = []
@@ -204,3 +206,30 @@ def adamw_step_ex(W, grad, m, v, lr, b1, b2, eps, wd, step, inv_scale=1.0, clip=
     rc = library().adamw_step_ex(_ptr(W), _ptr(grad), gd, _ptr(m), _ptr(v), n, lr, b1, b2, eps, wd,
                                  int(step), inv_scale, _ptr(clip), _ptr(skip), _ptr(w16), wd16)
     _check(rc, "adamw_step_ex")
+
+
+def grad_norm(grad, inv_scale=1.0, max_norm=0.0, out=None, found_inf=None):
+    """Norm of the unscaled gradient, clip factor and inf/NaN flag, on the GPU (C: grad_norm).
+
+    Returns (out, found_inf): out a float32 tensor [norm, clip factor], found_inf an
+    int32 tensor [flag]; both stay on the device (pass out[1:] as adamw_step_ex's clip and
+    found_inf as its skip).  Tensors may be given to reuse them.
+    """
+    import torch
+    gd = {torch.float32: LB_F32, torch.float16: LB_F16, torch.bfloat16: LB_BF16}.get(grad.dtype)
+    if gd is None:
+        raise TypeError("grad must be float32, float16 or bfloat16")
+    if out is None:
+        out = torch.empty(2, dtype=torch.float32, device=grad.device)
+    if found_inf is None:
+        found_inf = torch.empty(1, dtype=torch.int32, device=grad.device)
+    if out.dtype != torch.float32 or out.numel() != 2:
+        raise TypeError("out must be a two-element float32 tensor")
+    if found_inf.dtype != torch.int32 or found_inf.numel() != 1:
+        raise TypeError("found_inf must be a one-element int32 tensor")
+    dev = _device_of([grad, out, found_inf])
+    _use_current_stream(dev)
+    rc = library().grad_norm(_ptr(grad), gd, grad.numel(), inv_scale, max_norm, _ptr(out),
+                             _ptr(found_inf))
+    _check(rc, "grad_norm")
+    return out, found_inf

@@ -3,7 +3,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
+#include <unordered_map>
 
 #include "../../include/linbwd.h"
 #include "kernels.h"
@@ -28,6 +30,37 @@ int hip_fail(const char *what, hipError_t e) {
 }
 
 bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; } // false for NaN
+
+// Library-owned workspace of grad_norm: the per-block partial sums and flags,
+// allocated on first use on each device and kept until the process ends.
+// Calls that overlap on one device share it (and would race).
+struct NormWorkspace {
+    double *partial = nullptr;
+    int *flag = nullptr;
+};
+std::mutex ws_mutex;
+std::unordered_map<int, NormWorkspace> ws_by_device;
+
+hipError_t norm_workspace(NormWorkspace &out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    std::lock_guard<std::mutex> lock(ws_mutex);
+    auto it = ws_by_device.find(dev);
+    if (it == ws_by_device.end()) {
+        void *p = nullptr;
+        e = hipMalloc(&p, lb::kNormMaxBlocks * (sizeof(double) + sizeof(int)));
+        if (e != hipSuccess)
+            return e;
+        NormWorkspace w;
+        w.partial = static_cast<double *>(p);
+        w.flag = reinterpret_cast<int *>(w.partial + lb::kNormMaxBlocks);
+        it = ws_by_device.emplace(dev, w).first;
+    }
+    out = it->second;
+    return hipSuccess;
+}
 
 int adamw_impl(const char *name, lb::GradType gt, float *W, const void *g, float *m, float *v, int64_t n,
                float lr, float b1, float b2, float eps, float wd, int step, float inv_scale,
@@ -148,6 +181,41 @@ int adamw_step_ex(float *W, const void *grad, int grad_dtype, float *m, float *v
     }
     return adamw_impl("adamw_step_ex", gt, W, grad, m, v, n, lr, b1, b2, eps, wd, step, inv_scale, d_clip,
                       d_skip, W16, sh);
+}
+
+int grad_norm(const void *grad, int grad_dtype, int64_t n, float inv_scale, float max_norm, float *d_out,
+              int32_t *d_found_inf) {
+    tl_error.clear();
+    lb::GradType gt;
+    switch (grad_dtype) {
+    case LB_F32: gt = lb::GRAD_F32; break;
+    case LB_F16: gt = lb::GRAD_F16; break;
+    case LB_BF16: gt = lb::GRAD_BF16; break;
+    default: return fail(LB_EDTYPE, "grad_norm: grad_dtype %d is not LB_F32, LB_F16 or LB_BF16", grad_dtype);
+    }
+    if (n < 0)
+        return fail(LB_EINVAL, "grad_norm: n = %lld is negative", (long long)n);
+    if (!d_out)
+        return fail(LB_EINVAL, "grad_norm: d_out is NULL");
+    if (n > 0 && !grad)
+        return fail(LB_EINVAL, "grad_norm: grad is NULL with n = %lld", (long long)n);
+    NormWorkspace ws;
+    hipError_t e = norm_workspace(ws);
+    if (e != hipSuccess)
+        return hip_fail("grad_norm (workspace)", e);
+    lb::NormArgs a;
+    a.g = grad;
+    a.n = n;
+    a.inv_scale = inv_scale;
+    a.max_norm = max_norm;
+    a.partial = ws.partial;
+    a.flag = ws.flag;
+    a.out = d_out;
+    a.found_inf = d_found_inf;
+    e = lb::launch_grad_norm(a, gt, tl_stream);
+    if (e != hipSuccess)
+        return hip_fail("grad_norm", e);
+    return LB_OK;
 }
 
 int lb_set_stream(void *hip_stream) {

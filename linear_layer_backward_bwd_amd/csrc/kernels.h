@@ -28,6 +28,21 @@ struct AdamWArgs {
 
 hipError_t launch_adamw(const AdamWArgs &a, GradType gt, ShadowType shadow, hipStream_t s);
 
+// ---- gradient norm ------------------------------------------------------
+constexpr int kNormMaxBlocks = 16384; // workspace: this many fp64 partials and int flags
+
+struct NormArgs {
+    const void *g;
+    int64_t n;
+    float inv_scale, max_norm;
+    double *partial; // workspace, kNormMaxBlocks entries
+    int *flag;       // workspace, kNormMaxBlocks entries
+    float *out;      // [0] norm, [1] clip factor
+    int32_t *found_inf; // or null
+};
+
+hipError_t launch_grad_norm(const NormArgs &a, GradType gt, hipStream_t s);
+
 // ---- Linear backward ----------------------------------------------------
 struct LinBwdArgs {
     const void *X, *W, *dY;

@@ -24,6 +24,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("lin_bwd", "adamw_step", "adamw_step_f16", "adamw_step_bf16", "adamw_step_ex",
+                 "grad_norm",
                  "lb_set_stream", "lb_last_error", "lb_version"):
         assert want in names
 
@@ -137,3 +138,31 @@ def test_adamw_ex_binding_checks_types():
         lb.adamw_step_ex(w, w, w, w, 1e-3, 0.9, 0.99, 1e-8, 0.0, 1, clip=torch.zeros(2))
     with pytest.raises(TypeError):
         lb.adamw_step_ex(w, w, w, w, 1e-3, 0.9, 0.99, 1e-8, 0.0, 1, skip=torch.zeros(1))
+
+
+FAKE = ctypes.c_void_p(256)   # never dereferenced: every case below is rejected on the host
+
+
+@pytest.mark.parametrize("gd,n,grad,out,code", [
+    (3, 0, NULL, FAKE, -2), (-1, 4, FAKE, FAKE, -2),   # unknown gradient dtype
+    (1, -1, FAKE, FAKE, -1),                           # negative size
+    (0, 0, NULL, NULL, -1), (2, 8, FAKE, NULL, -1),    # NULL d_out
+    (1, 8, NULL, FAKE, -1),                            # NULL grad with n > 0
+])
+def test_grad_norm_rejects_on_host(gd, n, grad, out, code):
+    rc = lb.library().grad_norm(grad, gd, n, 1.0, 1.0, out, NULL)
+    assert rc == code
+    assert lb.lb_last_error() != ""
+
+
+def test_grad_norm_binding_checks_types():
+    import torch
+    g = torch.zeros(8)
+    with pytest.raises(TypeError):
+        lb.grad_norm(g.to(torch.int32))
+    with pytest.raises(TypeError):
+        lb.grad_norm(g, out=torch.zeros(3))
+    with pytest.raises(TypeError):
+        lb.grad_norm(g, out=torch.zeros(2, dtype=torch.float64))
+    with pytest.raises(TypeError):
+        lb.grad_norm(g, found_inf=torch.zeros(1))
