@@ -74,3 +74,16 @@ def test_fp64_accumulation_against_fsum():
     for v in g32[:1 << 16]:
         f32_running = np.float32(f32_running + v * v)   # what the oracle must not do
     assert f32_running != np.float32(math.fsum(float(v) * float(v) for v in g32[:1 << 16]))
+
+
+@pytest.mark.parametrize("x", [1e30, -1e30, 1e-30])
+def test_squares_outside_fp32_range(x):
+    """fp32 squares of 1e30 overflow and of 1e-30 underflow; the fp64 sum of four
+    exact squares is 4x², whose root 2|x| is exact in fp32."""
+    g = np.full(4, x, F)
+    norm, clip, bad = oracle.grad_norm(g, "f32")
+    assert norm == 2 * abs(float(np.float32(x)))
+    assert not bad
+    with np.errstate(over="ignore", under="ignore"):
+        naive = np.sqrt(np.sum(g * g, dtype=np.float32))
+    assert naive != np.float32(norm)
