@@ -12,6 +12,8 @@ Definitions followed (cited by page title and section):
   section "反向传播——Linear 层的梯度"; "GPU 如何训练模型：从算子到 Kernel",
   section "一个线性层，前向和反向到底在算什么".  Evaluated in fp64 on the exact
   decoded inputs.
+* db = sum of G over rows for the bias of Y = X·W + b -- "GPU 优化实战 Part 2",
+  section "反向传播——Linear 层的梯度" (the forward with a bias).  fp64.
 * unscale + AdamW with decoupled weight decay -- "GPU 优化实战 Part 2", sections
   "AdamW 优化器——融合内核" and "混合精度训练（FP16 / BF16）"; "Mastering LLM
   Training with CUDA and ROCm", section "AdamW Algorithm".  Scalar fp32 loop.
@@ -82,6 +84,8 @@ def _load():
     lib.oracle_f32_to_f16.argtypes = [f32]
     lib.oracle_f32_to_f16.restype = ctypes.c_uint16
     lib.oracle_grad_norm.argtypes = [vp, i32, i64, f32, f32, vp, vp]
+    lib.oracle_db.argtypes = [vp, i32, i64, i64, vp]
+    lib.oracle_db.restype = None
     lib.oracle_grad_norm.restype = None
     lib.oracle_round16.argtypes = [vp, i64, i32, vp]
     lib.oracle_round16.restype = None
@@ -141,6 +145,17 @@ def lin_bwd(X, W, G, dtype: str, need_dx: bool = True, need_dw: bool = True):
         dW = np.empty((K, N), dtype=np.float64)
         lib.oracle_dw(_ptr(X), _ptr(G), _DTYPES[dtype], M, K, N, _ptr(dW))
     return dX, dW
+
+
+def bias_grad(G, dtype: str) -> np.ndarray:
+    """db[n] = sum over rows m of G[m, n], in float64, for G[M,N]."""
+    G = _as_input(G, dtype)
+    if G.ndim != 2:
+        raise ValueError("G must be 2-D")
+    M, N = G.shape
+    db = np.empty(N, dtype=np.float64)
+    _load().oracle_db(_ptr(G), _DTYPES[dtype], M, N, _ptr(db))
+    return db
 
 
 def dx_at(G, W, dtype: str, rows, cols) -> np.ndarray:

@@ -14,6 +14,7 @@
  *    into M) and upstream gradient G = dL/dY [M,N]:
  *        dX = G·Wᵀ      dX[m,k] = Σ_n G[m,n]·W[k,n]
  *        dW = Xᵀ·G      dW[k,n] = Σ_m X[m,k]·G[m,n]
+ *        db = 1ᵀ·G      db[n]   = Σ_m G[m,n]       (bias b added to every row)
  *    Pages: "GPU 优化实战 Part 2", section "反向传播——Linear 层的梯度"
  *    (the two backward products of a Linear layer); "GPU 如何训练模型：从算子
  *    到 Kernel", section "一个线性层，前向和反向到底在算什么" (shapes with batch
@@ -178,6 +179,23 @@ void oracle_dw_at(const void *X, const void *G, int dtype,
         for (int64_t m = 0; m < M; ++m)
             s += elt(X, dtype, m * K + k) * elt(G, dtype, m * N + n);
         out[i] = s;
+    }
+}
+
+/* ---- bias gradient, fp64 -------------------------------------------------- */
+
+/* db[n] = Σ_m G[m,n]: the gradient of the bias b in Y = X·W + b, where b is
+ * added to every one of the M rows ("GPU 优化实战 Part 2", section
+ * "反向传播——Linear 层的梯度", which writes the forward with a bias; the
+ * section "AdamW 优化器——融合内核" then speaks of dW and db). */
+void oracle_db(const void *G, int dtype, int64_t M, int64_t N, double *db)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double s = 0.0;
+        for (int64_t m = 0; m < M; ++m)
+            s += elt(G, dtype, m * N + n);
+        db[n] = s;
     }
 }
 
