@@ -294,6 +294,30 @@ def bench_clipped_step(n, steps, warmup, seed):
             "gparams_per_s": round(n / (step_ms * 1e-3) / 1e9, 2)}
 
 
+def bench_bias(steps, warmup, seed):
+    """db = column sums of dY for the block's four projections (lin_bwd_ex with db only)."""
+    import torch
+
+    import linear_layer_backward_bwd_amd as lb
+    import synth
+    gens = [synth._gen(seed + 1 + i, "cuda") for i in range(len(synth.BLOCK_PROJECTIONS))]
+    Gs = [synth.to_storage(synth.normal((synth.BLOCK_TOKENS, n), 1e-4, g), "bf16")
+          for g, (_, _, n) in zip(gens, synth.BLOCK_PROJECTIONS)]
+    dbs = [torch.empty(G.shape[1], device="cuda") for G in Gs]
+    run = lambda: [lb.lin_bwd_ex(None, None, G, db=db) for G, db in zip(Gs, dbs)]
+    for _ in range(warmup):
+        run()
+    timer = Timer(["bias"])
+    timer.run("bias", lambda: [run() for _ in range(steps)])
+    timer.collect()
+    ms = timer.ms["bias"] / steps
+    nbytes = sum(G.numel() * 2 + G.shape[1] * 4 for G in Gs)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "block dY, M=16384, N=12288/4096/16384/4096, bf16", "ms": round(ms, 4),
+            "gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+            "bytes": nbytes}
+
+
 def cpu_baseline(cases, opt, target_s=12.0):
     """The CPU oracle on a bounded sample of the block workload, extrapolated to one step."""
     import numpy as np
@@ -348,7 +372,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the M=32 / M=2048 / 2^28-param AdamW figures")
-    ap.add_argument("--only", choices=["block", "m32", "m2048", "adamw", "clipped", "copycal"],
+    ap.add_argument("--only", choices=["block", "m32", "m2048", "adamw", "clipped", "bias", "copycal"],
                     default=None,
                     help="time one workload only (for profiling); copycal = 1 GiB copies for "
                          "scaling HBM byte counters")
@@ -373,6 +397,9 @@ def main(argv=None):
         return 0
     if args.only == "clipped":
         print(json.dumps(bench_clipped_step(1 << 28, args.steps, args.warmup, args.seed)), flush=True)
+        return 0
+    if args.only == "bias":
+        print(json.dumps(bench_bias(args.steps, args.warmup, args.seed)), flush=True)
         return 0
     if args.only == "copycal":
         print(json.dumps(copy_calibration(args.steps)), flush=True)
@@ -401,6 +428,7 @@ def main(argv=None):
             "lin_bwd_M2048_K4096_N4096": bench_linear(2048, 4096, 4096, 50, 5, args.seed),
             "adamw_2p28_f16": bench_adamw(1 << 28, 10, 2, args.seed),
             "grad_norm_adamw_ex_2p28_f16": bench_clipped_step(1 << 28, 10, 2, args.seed),
+            "bias_grad_block": bench_bias(20, 3, args.seed),
         }
     print(json.dumps(out), flush=True)
     return 0

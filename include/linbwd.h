@@ -70,6 +70,25 @@ int lin_bwd(const void *X, const void *W, const void *dY, void *dX, float *dW,
             int64_t M, int64_t K, int64_t N, int dtype);
 
 /*
+ * lin_bwd_ex -- lin_bwd plus the bias gradient of Y = X·W + b, where b [N] is
+ * added to every row ("GPU 优化实战 Part 2", section "反向传播——Linear 层的
+ * 梯度", which writes the forward with a bias; its AdamW section then updates
+ * with dW and db):
+ *     db[n] = Σ_m dY[m,n]                                    [N]
+ *
+ *   db  [N]  fp32 always  written (overwritten); NULL makes this call lin_bwd
+ * Every other argument, size rule and error is lin_bwd's.  db is summed in
+ * fp32 per row range and the partials in fp64, in a fixed order (results
+ * repeat bit for bit); M = 0 fills db with zeros.  X and W may be NULL when
+ * only db is requested.  Additional error: LB_EINVAL for a NULL dY with db
+ * requested and M, N > 0.  Uses the library-owned workspace (about 4.2 MiB
+ * per device, allocated on first use, kept until the process ends); calls that
+ * request db and overlap on one device race.
+ */
+int lin_bwd_ex(const void *X, const void *W, const void *dY, void *dX, float *dW, float *db,
+               int64_t M, int64_t K, int64_t N, int dtype);
+
+/*
  * adamw_step -- one fused pass over n parameters that unscales the gradient
  * and applies AdamW with decoupled weight decay to the fp32 master weights:
  *     g  = float(grad[i]) · inv_scale
@@ -156,8 +175,8 @@ int adamw_step_ex(float *W, const void *grad, int grad_dtype, float *m, float *v
  *
  * The summation order is fixed for a given n and 16-byte alignment of grad
  * (the result is reproducible).
- * Uses a small library-owned workspace (192 KiB per device, allocated on first
- * use and kept until the process ends); calls that overlap on one device race.
+ * Uses the library-owned workspace (about 4.2 MiB per device, allocated on
+ * first use, kept until the process ends); calls that overlap on one device race.
  * Asynchronous on the thread's stream.  Errors: LB_EDTYPE for another
  * grad_dtype; LB_EINVAL for n < 0, NULL d_out, or NULL grad with n > 0;
  * LB_EHIP when the workspace cannot be allocated or a launch fails.

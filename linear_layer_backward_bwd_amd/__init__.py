@@ -33,6 +33,8 @@ def library() -> ctypes.CDLL:
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     lib.lin_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32]
     lib.lin_bwd.restype = i32
+    lib.lin_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32]
+    lib.lin_bwd_ex.restype = i32
     for name in ("adamw_step", "adamw_step_f16", "adamw_step_bf16"):
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, i64, f32, f32, f32, f32, f32, i32, f32]
@@ -125,6 +127,42 @@ def lin_bwd(X, W, dY, dX=None, dW=None) -> None:
     rc = library().lin_bwd(_ptr(X), _ptr(W), _ptr(dY), _ptr(dX), _ptr(dW), M, K, N,
                            LB_BF16 if dtype == torch.bfloat16 else LB_F32)
     _check(rc, "lin_bwd")
+
+
+def lin_bwd_ex(X, W, dY, dX=None, dW=None, db=None) -> None:
+    """lin_bwd plus the bias gradient db[n] = Σ_m dY[m,n] (into db, float32 [N]).
+
+    X and W may be None when dX and dW are None (db only).
+    """
+    import torch
+    if dY is None or dY.dim() != 2:
+        raise ValueError("dY must be a 2-D tensor")
+    dtype = dY.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("dY must be bfloat16 or float32")
+    M, N = dY.shape
+    if dX is not None or dW is not None or X is not None or W is not None:
+        if X is None or W is None:
+            raise ValueError("X and W are required with dX or dW")
+        if X.dtype != dtype or W.dtype != dtype:
+            raise TypeError("X, W, dY must all be bfloat16 or all float32")
+        if X.dim() != 2 or W.dim() != 2 or X.shape[0] != M or W.shape[1] != N or W.shape[0] != X.shape[1]:
+            raise ValueError("shape mismatch: X%s W%s dY%s" % (tuple(X.shape), tuple(W.shape),
+                                                               tuple(dY.shape)))
+        K = X.shape[1]
+    else:
+        K = 0
+    if dX is not None and (dX.dtype != dtype or tuple(dX.shape) != (M, K)):
+        raise ValueError("dX must be %s of shape (%d, %d)" % (dtype, M, K))
+    if dW is not None and (dW.dtype != torch.float32 or tuple(dW.shape) != (K, N)):
+        raise ValueError("dW must be float32 of shape (%d, %d)" % (K, N))
+    if db is not None and (db.dtype != torch.float32 or db.numel() != N):
+        raise ValueError("db must be float32 with %d elements" % N)
+    dev = _device_of([X, W, dY, dX, dW, db])
+    _use_current_stream(dev)
+    rc = library().lin_bwd_ex(_ptr(X), _ptr(W), _ptr(dY), _ptr(dX), _ptr(dW), _ptr(db), M, K, N,
+                              LB_BF16 if dtype == torch.bfloat16 else LB_F32)
+    _check(rc, "lin_bwd_ex")
 
 
 def _adamw(name, W, grad, m, v, lr, b1, b2, eps, wd, step, inv_scale):

@@ -31,17 +31,19 @@ int hip_fail(const char *what, hipError_t e) {
 
 bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; } // false for NaN
 
-// Library-owned workspace of grad_norm: the per-block partial sums and flags,
-// allocated on first use on each device and kept until the process ends.
-// Calls that overlap on one device share it (and would race).
-struct NormWorkspace {
-    double *partial = nullptr;
-    int *flag = nullptr;
+// Library-owned workspace, allocated on first use on each device and kept
+// until the process ends: grad_norm's per-block partial sums and flags and
+// lin_bwd_ex's per-split bias partials, in separate regions.  Calls of one
+// entry point that overlap on one device share its region (and would race).
+struct Workspace {
+    double *norm_partial = nullptr;
+    int *norm_flag = nullptr;
+    float *bias_partial = nullptr;
 };
 std::mutex ws_mutex;
-std::unordered_map<int, NormWorkspace> ws_by_device;
+std::unordered_map<int, Workspace> ws_by_device;
 
-hipError_t norm_workspace(NormWorkspace &out) {
+hipError_t workspace(Workspace &out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -49,13 +51,16 @@ hipError_t norm_workspace(NormWorkspace &out) {
     std::lock_guard<std::mutex> lock(ws_mutex);
     auto it = ws_by_device.find(dev);
     if (it == ws_by_device.end()) {
+        const size_t norm_bytes = lb::kNormMaxBlocks * (sizeof(double) + sizeof(int));
+        const size_t bias_bytes = lb::kBiasWorkspaceFloats * sizeof(float);
         void *p = nullptr;
-        e = hipMalloc(&p, lb::kNormMaxBlocks * (sizeof(double) + sizeof(int)));
+        e = hipMalloc(&p, norm_bytes + bias_bytes);
         if (e != hipSuccess)
             return e;
-        NormWorkspace w;
-        w.partial = static_cast<double *>(p);
-        w.flag = reinterpret_cast<int *>(w.partial + lb::kNormMaxBlocks);
+        Workspace w;
+        w.norm_partial = static_cast<double *>(p);
+        w.norm_flag = reinterpret_cast<int *>(w.norm_partial + lb::kNormMaxBlocks);
+        w.bias_partial = reinterpret_cast<float *>(static_cast<char *>(p) + norm_bytes);
         it = ws_by_device.emplace(dev, w).first;
     }
     out = it->second;
@@ -108,23 +113,33 @@ int adamw_impl(const char *name, lb::GradType gt, float *W, const void *g, float
 
 extern "C" {
 
-int lin_bwd(const void *X, const void *W, const void *dY, void *dX, float *dW, int64_t M, int64_t K,
-            int64_t N, int dtype) {
+int lin_bwd_ex(const void *X, const void *W, const void *dY, void *dX, float *dW, float *db, int64_t M,
+               int64_t K, int64_t N, int dtype) {
+    const char *name = db ? "lin_bwd_ex" : "lin_bwd";
     tl_error.clear();
     if (dtype != LB_F32 && dtype != LB_BF16)
-        return fail(LB_EDTYPE, "lin_bwd: dtype %d is not LB_F32 (0) or LB_BF16 (1)", dtype);
+        return fail(LB_EDTYPE, "%s: dtype %d is not LB_F32 (0) or LB_BF16 (1)", name, dtype);
     if (M < 0 || K < 0 || N < 0)
-        return fail(LB_EINVAL, "lin_bwd: negative size M=%lld K=%lld N=%lld", (long long)M,
-                    (long long)K, (long long)N);
+        return fail(LB_EINVAL, "%s: negative size M=%lld K=%lld N=%lld", name, (long long)M, (long long)K,
+                    (long long)N);
     const int64_t lim = (int64_t)1 << 31;
     if (M >= lim || K >= lim || N >= lim)
-        return fail(LB_EINVAL, "lin_bwd: sizes must be below 2^31 (M=%lld K=%lld N=%lld)",
-                    (long long)M, (long long)K, (long long)N);
-    // dX has M*K entries and sums over N; dW has K*N entries and sums over M.
+        return fail(LB_EINVAL, "%s: sizes must be below 2^31 (M=%lld K=%lld N=%lld)", name, (long long)M,
+                    (long long)K, (long long)N);
+    // dX has M*K entries and sums over N; dW has K*N entries and sums over M;
+    // db has N entries and sums over M.
     if (dX && M > 0 && K > 0 && N > 0 && (!dY || !W))
-        return fail(LB_EINVAL, "lin_bwd: dX requested but dY or W is NULL");
+        return fail(LB_EINVAL, "%s: dX requested but dY or W is NULL", name);
     if (dW && K > 0 && N > 0 && M > 0 && (!X || !dY))
-        return fail(LB_EINVAL, "lin_bwd: dW requested but X or dY is NULL");
+        return fail(LB_EINVAL, "%s: dW requested but X or dY is NULL", name);
+    if (db && N > 0 && M > 0 && !dY)
+        return fail(LB_EINVAL, "%s: db requested but dY is NULL", name);
+    Workspace ws;
+    if (db && N > 0) {
+        hipError_t e = workspace(ws);
+        if (e != hipSuccess)
+            return hip_fail("lin_bwd_ex (workspace)", e);
+    }
     lb::LinBwdArgs a;
     a.X = X;
     a.W = W;
@@ -137,8 +152,25 @@ int lin_bwd(const void *X, const void *W, const void *dY, void *dX, float *dW, i
     a.bf16 = dtype == LB_BF16;
     hipError_t e = lb::launch_lin_bwd(a, tl_stream);
     if (e != hipSuccess)
-        return hip_fail("lin_bwd", e);
+        return hip_fail(name, e);
+    if (db) {
+        lb::BiasArgs b;
+        b.dY = dY;
+        b.db = db;
+        b.M = M;
+        b.N = N;
+        b.bf16 = dtype == LB_BF16;
+        b.partial = ws.bias_partial;
+        e = lb::launch_bias_grad(b, tl_stream);
+        if (e != hipSuccess)
+            return hip_fail("lin_bwd_ex (bias)", e);
+    }
     return LB_OK;
+}
+
+int lin_bwd(const void *X, const void *W, const void *dY, void *dX, float *dW, int64_t M, int64_t K,
+            int64_t N, int dtype) {
+    return lin_bwd_ex(X, W, dY, dX, dW, nullptr, M, K, N, dtype);
 }
 
 int adamw_step(float *W, const float *grad, float *m, float *v, int64_t n, float lr, float b1, float b2,
@@ -199,8 +231,8 @@ int grad_norm(const void *grad, int grad_dtype, int64_t n, float inv_scale, floa
         return fail(LB_EINVAL, "grad_norm: d_out is NULL");
     if (n > 0 && !grad)
         return fail(LB_EINVAL, "grad_norm: grad is NULL with n = %lld", (long long)n);
-    NormWorkspace ws;
-    hipError_t e = norm_workspace(ws);
+    Workspace ws;
+    hipError_t e = workspace(ws);
     if (e != hipSuccess)
         return hip_fail("grad_norm (workspace)", e);
     lb::NormArgs a;
@@ -208,8 +240,8 @@ int grad_norm(const void *grad, int grad_dtype, int64_t n, float inv_scale, floa
     a.n = n;
     a.inv_scale = inv_scale;
     a.max_norm = max_norm;
-    a.partial = ws.partial;
-    a.flag = ws.flag;
+    a.partial = ws.norm_partial;
+    a.flag = ws.norm_flag;
     a.out = d_out;
     a.found_inf = d_found_inf;
     e = lb::launch_grad_norm(a, gt, tl_stream);

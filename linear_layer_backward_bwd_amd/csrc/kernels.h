@@ -55,4 +55,19 @@ struct LinBwdArgs {
 // Chooses kernels by dtype, alignment and M; enqueues 1-2 launches.
 hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s);
 
+// ---- bias gradient ------------------------------------------------------
+constexpr int kBiasMaxSplits = 256;              // row splits per launch
+constexpr int64_t kBiasWorkspaceFloats = 1 << 20; // workspace: splits * N fp32 partials
+
+struct BiasArgs {
+    const void *dY; // [M,N] bf16 or fp32
+    float *db;      // [N] fp32
+    int64_t M, N;
+    bool bf16;
+    float *partial; // workspace, kBiasWorkspaceFloats entries
+};
+
+// db[n] = sum_m dY[m,n]; one or two launches; N = 0 launches nothing.
+hipError_t launch_bias_grad(const BiasArgs &a, hipStream_t s);
+
 } // namespace lb

@@ -16,6 +16,8 @@ F32_OUT_RELF = 1e-5   # fp32 dX (fp32 operands) vs fp64
 ADAMW_ABS = 2e-6      # |gpu - oracle| <= ADAMW_ABS * max(1, |oracle|) for W, m, v
 NORM_ULP = 1          # gradient norm: fp32 ulps from the oracle (same exact squares, fp64 sums)
 CLIP_ULP = 2          # clip factor: fp32 ulps from the oracle's
+DB_RELF = 1e-5        # fp32 bias gradient vs fp64: relative Frobenius error
+DB_ABS = 1e-5         # ... and per column |error| <= DB_ABS * sum_m |dY[m,n]|
 
 
 class Guarded:

@@ -24,7 +24,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("lin_bwd", "adamw_step", "adamw_step_f16", "adamw_step_bf16", "adamw_step_ex",
-                 "grad_norm",
+                 "grad_norm", "lin_bwd_ex",
                  "lb_set_stream", "lb_last_error", "lb_version"):
         assert want in names
 
@@ -166,3 +166,32 @@ def test_grad_norm_binding_checks_types():
         lb.grad_norm(g, out=torch.zeros(2, dtype=torch.float64))
     with pytest.raises(TypeError):
         lb.grad_norm(g, found_inf=torch.zeros(1))
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(dtype=2), -2), (dict(dtype=-1), -2),                  # unknown dtype
+    (dict(M=-1), -1), (dict(N=-5), -1), (dict(K=1 << 31), -1),  # bad sizes
+    (dict(db=FAKE), -1),                                        # db requested, dY NULL
+    (dict(db=FAKE, N=0), 0),                                    # N = 0: nothing to write
+    (dict(), 0),                                                # nothing requested
+])
+def test_lin_bwd_ex_rejects_on_host(args, code):
+    a = dict(M=8, K=8, N=8, dtype=1, db=NULL)
+    a.update(args)
+    rc = lb.library().lin_bwd_ex(NULL, NULL, NULL, NULL, NULL, a["db"], a["M"], a["K"], a["N"],
+                                 a["dtype"])
+    assert rc == code
+    assert (lb.lb_last_error() != "") == (code != 0)
+
+
+def test_lin_bwd_ex_binding_checks():
+    import torch
+    g = torch.zeros(4, 6, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        lb.lin_bwd_ex(None, None, g, db=torch.zeros(5))
+    with pytest.raises(ValueError):
+        lb.lin_bwd_ex(None, None, g, db=torch.zeros(6, dtype=torch.float64))
+    with pytest.raises(ValueError):
+        lb.lin_bwd_ex(torch.zeros(4, 3, dtype=torch.bfloat16), None, g, db=torch.zeros(6))
+    with pytest.raises(TypeError):
+        lb.lin_bwd_ex(None, None, g.to(torch.float16), db=torch.zeros(6))
