@@ -14,6 +14,8 @@ Definitions followed (cited by page title and section):
   decoded inputs.
 * db = sum of G over rows for the bias of Y = X·W + b -- "GPU 优化实战 Part 2",
   section "反向传播——Linear 层的梯度" (the forward with a bias).  fp64.
+* softmax backward dX = P·(dY − Σ P·dY) per row -- "GPU 优化实战 Part 2", section
+  "Softmax 和 LayerNorm 的梯度（自定义内核）".  fp64.
 * unscale + AdamW with decoupled weight decay -- "GPU 优化实战 Part 2", sections
   "AdamW 优化器——融合内核" and "混合精度训练（FP16 / BF16）"; "Mastering LLM
   Training with CUDA and ROCm", section "AdamW Algorithm".  Scalar fp32 loop.
@@ -86,6 +88,8 @@ def _load():
     lib.oracle_grad_norm.argtypes = [vp, i32, i64, f32, f32, vp, vp]
     lib.oracle_db.argtypes = [vp, i32, i64, i64, vp]
     lib.oracle_db.restype = None
+    lib.oracle_softmax_bwd.argtypes = [vp, vp, i32, i64, i64, vp]
+    lib.oracle_softmax_bwd.restype = None
     lib.oracle_grad_norm.restype = None
     lib.oracle_round16.argtypes = [vp, i64, i32, vp]
     lib.oracle_round16.restype = None
@@ -156,6 +160,17 @@ def bias_grad(G, dtype: str) -> np.ndarray:
     db = np.empty(N, dtype=np.float64)
     _load().oracle_db(_ptr(G), _DTYPES[dtype], M, N, _ptr(db))
     return db
+
+
+def softmax_bwd(P, dY, dtype: str) -> np.ndarray:
+    """dX = P * (dY - rowsum(P * dY)) in float64 for row-major P, dY [rows, cols]."""
+    P, dY = _as_input(P, dtype), _as_input(dY, dtype)
+    if P.ndim != 2 or P.shape != dY.shape:
+        raise ValueError("P and dY must be 2-D of one shape")
+    rows, cols = P.shape
+    dX = np.empty((rows, cols), dtype=np.float64)
+    _load().oracle_softmax_bwd(_ptr(P), _ptr(dY), _DTYPES[dtype], rows, cols, _ptr(dX))
+    return dX
 
 
 def dx_at(G, W, dtype: str, rows, cols) -> np.ndarray:

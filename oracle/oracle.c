@@ -15,6 +15,7 @@
  *        dX = G·Wᵀ      dX[m,k] = Σ_n G[m,n]·W[k,n]
  *        dW = Xᵀ·G      dW[k,n] = Σ_m X[m,k]·G[m,n]
  *        db = 1ᵀ·G      db[n]   = Σ_m G[m,n]       (bias b added to every row)
+ *  - Softmax backward over rows: dX = P ⊙ (dY − rowsum(P ⊙ dY)).
  *    Pages: "GPU 优化实战 Part 2", section "反向传播——Linear 层的梯度"
  *    (the two backward products of a Linear layer); "GPU 如何训练模型：从算子
  *    到 Kernel", section "一个线性层，前向和反向到底在算什么" (shapes with batch
@@ -196,6 +197,25 @@ void oracle_db(const void *G, int dtype, int64_t M, int64_t N, double *db)
         for (int64_t m = 0; m < M; ++m)
             s += elt(G, dtype, m * N + n);
         db[n] = s;
+    }
+}
+
+/* ---- softmax backward, fp64 ---------------------------------------------- */
+
+/* Rows of P = softmax(z) (probabilities, row-major [rows, cols]) and of the
+ * upstream gradient dY: dX[r,i] = P[r,i]·(dY[r,i] − Σ_j P[r,j]·dY[r,j]), the
+ * gradient with respect to the logits z ("GPU 优化实战 Part 2", section
+ * "Softmax 和 LayerNorm 的梯度（自定义内核）", softmax backward). */
+void oracle_softmax_bwd(const void *P, const void *dY, int dtype, int64_t rows, int64_t cols,
+                        double *dX)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double dot = 0.0;
+        for (int64_t j = 0; j < cols; ++j)
+            dot += elt(P, dtype, r * cols + j) * elt(dY, dtype, r * cols + j);
+        for (int64_t i = 0; i < cols; ++i)
+            dX[r * cols + i] = elt(P, dtype, r * cols + i) * (elt(dY, dtype, r * cols + i) - dot);
     }
 }
 

@@ -169,3 +169,21 @@ def block_case(seed=0, tokens=BLOCK_TOKENS, projections=BLOCK_PROJECTIONS, devic
                      lr=3e-4, b1=0.9, b2=0.95, eps=1e-8, wd=0.1, steps=[100], seed=seed,
                      W=masters, device=device)
     return cases, opt
+
+
+# ---- softmax backward --------------------------------------------------------
+
+#: attention probabilities of one block: batch 8 x 32 heads x 2048 query rows, 2048 keys
+SOFTMAX_ROWS = 8 * 32 * 2048
+SOFTMAX_COLS = 2048
+
+
+def softmax_case(rows, cols, dtype="bf16", z_std=1.0, dy_std=1.0, seed=0, device="cpu"):
+    """(P, dY): P = row softmax of logits z ~ N(0, z_std) computed in fp32, dY ~ N(0, dy_std),
+    both rounded to dtype.  Draw order: z, dY.  (No causal mask: every row is dense.)"""
+    gen = _gen(seed, device)
+    z = normal((rows, cols), z_std, gen)
+    P = to_storage(torch.softmax(z, dim=1), dtype)
+    del z
+    dY = to_storage(normal((rows, cols), dy_std, gen), dtype)
+    return P, dY
