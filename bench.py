@@ -318,6 +318,29 @@ def bench_bias(steps, warmup, seed):
             "bytes": nbytes}
 
 
+def bench_softmax(steps, warmup, seed):
+    """softmax_bwd over the attention probabilities of one block (bf16, rows of 2048)."""
+    import torch
+
+    import linear_layer_backward_bwd_amd as lb
+    import synth
+    rows, cols = synth.SOFTMAX_ROWS, synth.SOFTMAX_COLS
+    P, dY = synth.softmax_case(rows, cols, "bf16", seed=seed, device="cuda")
+    dX = torch.empty_like(P)
+    for _ in range(warmup):
+        lb.softmax_bwd(P, dY, dX)
+    timer = Timer(["softmax"])
+    for _ in range(steps):
+        timer.run("softmax", lambda: lb.softmax_bwd(P, dY, dX))
+    timer.collect()
+    ms = timer.ms["softmax"] / steps
+    nbytes = 3 * 2 * rows * cols
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "softmax_bwd rows=%d (8x32x2048) cols=%d bf16" % (rows, cols),
+            "ms": round(ms, 4), "gbps": round(gbps, 1),
+            "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "bytes_per_elem": 6}
+
+
 def cpu_baseline(cases, opt, target_s=12.0):
     """The CPU oracle on a bounded sample of the block workload, extrapolated to one step."""
     import numpy as np
@@ -372,7 +395,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the M=32 / M=2048 / 2^28-param AdamW figures")
-    ap.add_argument("--only", choices=["block", "m32", "m2048", "adamw", "clipped", "bias", "copycal"],
+    ap.add_argument("--only", choices=["block", "m32", "m2048", "adamw", "clipped", "bias", "softmax",
+                                       "copycal"],
                     default=None,
                     help="time one workload only (for profiling); copycal = 1 GiB copies for "
                          "scaling HBM byte counters")
@@ -400,6 +424,9 @@ def main(argv=None):
         return 0
     if args.only == "bias":
         print(json.dumps(bench_bias(args.steps, args.warmup, args.seed)), flush=True)
+        return 0
+    if args.only == "softmax":
+        print(json.dumps(bench_softmax(args.steps, args.warmup, args.seed)), flush=True)
         return 0
     if args.only == "copycal":
         print(json.dumps(copy_calibration(args.steps)), flush=True)
@@ -429,6 +456,7 @@ def main(argv=None):
             "adamw_2p28_f16": bench_adamw(1 << 28, 10, 2, args.seed),
             "grad_norm_adamw_ex_2p28_f16": bench_clipped_step(1 << 28, 10, 2, args.seed),
             "bias_grad_block": bench_bias(20, 3, args.seed),
+            "softmax_bwd_attention": bench_softmax(10, 2, args.seed),
         }
     print(json.dumps(out), flush=True)
     return 0

@@ -185,6 +185,29 @@ int grad_norm(const void *grad, int grad_dtype, int64_t n, float inv_scale, floa
               float *d_out, int32_t *d_found_inf);
 
 /*
+ * softmax_bwd -- backward of a row softmax P = softmax(z), with respect to the
+ * logits z ("GPU 优化实战 Part 2", section "Softmax 和 LayerNorm 的梯度（自定义
+ * 内核）", softmax backward):
+ *     dX[r,i] = P[r,i] * (dY[r,i] - Σ_j P[r,j]*dY[r,j])
+ *
+ *   P   [rows, cols]  dtype  read only (the forward's output)
+ *   dY  [rows, cols]  dtype  read only
+ *   dX  [rows, cols]  dtype  written; may be the same buffer as P or dY (in
+ *                            place), must not overlap them otherwise
+ *   dtype  LB_F32, or LB_BF16 (bf16 in and out, fp32 arithmetic, dX rounded
+ *          to nearest even)
+ *
+ * Row-major, contiguous.  Each row's dot product is summed in fp32 in a fixed
+ * order (results repeat bit for bit).  Any sizes and alignment; rows of up to
+ * 4096 columns are held in registers (one read of P and dY), longer rows are
+ * read twice.  rows = 0 or cols = 0 writes nothing.  Asynchronous on the
+ * thread's stream.  Errors: LB_EDTYPE for another dtype; LB_EINVAL for a
+ * negative size, a size of 2^40 or more, or a NULL buffer with rows, cols > 0;
+ * LB_EHIP when a launch fails.
+ */
+int softmax_bwd(const void *P, const void *dY, void *dX, int64_t rows, int64_t cols, int dtype);
+
+/*
  * lb_set_stream -- the HIP stream (a hipStream_t, passed as void*) on which
  * the calling thread's later calls enqueue their kernels; NULL selects the
  * null stream.  The setting is per thread.  Returns LB_OK.

@@ -35,6 +35,8 @@ def library() -> ctypes.CDLL:
     lib.lin_bwd.restype = i32
     lib.lin_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32]
     lib.lin_bwd_ex.restype = i32
+    lib.softmax_bwd.argtypes = [vp, vp, vp, i64, i64, i32]
+    lib.softmax_bwd.restype = i32
     for name in ("adamw_step", "adamw_step_f16", "adamw_step_bf16"):
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, i64, f32, f32, f32, f32, f32, i32, f32]
@@ -271,3 +273,32 @@ def grad_norm(grad, inv_scale=1.0, max_norm=0.0, out=None, found_inf=None):
                              _ptr(found_inf))
     _check(rc, "grad_norm")
     return out, found_inf
+
+
+def softmax_bwd(P, dY, dX=None):
+    """dX = P * (dY - rowsum(P * dY)) over the last dimension (C: softmax_bwd).
+
+    P, dY: one shape, both bfloat16 or both float32, contiguous, on one GPU; rows are
+    all leading dimensions flattened.  dX (same shape and dtype) may be given, also as
+    P or dY itself (in place); returns dX.
+    """
+    import torch
+    if P.dtype != dY.dtype or P.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("P and dY must both be bfloat16 or both float32")
+    if P.shape != dY.shape or P.dim() < 1:
+        raise ValueError("P and dY must have one shape")
+    if dX is None:
+        dX = torch.empty_like(P)
+    if dX.dtype != P.dtype or dX.shape != P.shape:
+        raise ValueError("dX must match P in shape and dtype")
+    for t, nm in ((P, "P"), (dY, "dY"), (dX, "dX")):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % nm)
+    cols = P.shape[-1]
+    rows = P.numel() // cols if cols else 0
+    dev = _device_of([P, dY, dX])
+    _use_current_stream(dev)
+    rc = library().softmax_bwd(_ptr(P), _ptr(dY), _ptr(dX), rows, cols,
+                               LB_BF16 if P.dtype == torch.bfloat16 else LB_F32)
+    _check(rc, "softmax_bwd")
+    return dX

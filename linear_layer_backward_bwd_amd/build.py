@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "liblinbwd.so")
-SOURCES = ["api.hip", "lin_bwd.hip", "adamw.hip", "grad_norm.hip", "bias_grad.hip"]
+SOURCES = ["api.hip", "lin_bwd.hip", "adamw.hip", "grad_norm.hip", "bias_grad.hip", "softmax_bwd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

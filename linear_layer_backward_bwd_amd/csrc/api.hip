@@ -250,6 +250,32 @@ int grad_norm(const void *grad, int grad_dtype, int64_t n, float inv_scale, floa
     return LB_OK;
 }
 
+int softmax_bwd(const void *P, const void *dY, void *dX, int64_t rows, int64_t cols, int dtype) {
+    tl_error.clear();
+    if (dtype != LB_F32 && dtype != LB_BF16)
+        return fail(LB_EDTYPE, "softmax_bwd: dtype %d is not LB_F32 (0) or LB_BF16 (1)", dtype);
+    if (rows < 0 || cols < 0)
+        return fail(LB_EINVAL, "softmax_bwd: negative size rows=%lld cols=%lld", (long long)rows,
+                    (long long)cols);
+    if (rows >= ((int64_t)1 << 40) || cols >= ((int64_t)1 << 40))
+        return fail(LB_EINVAL, "softmax_bwd: sizes must be below 2^40 (rows=%lld cols=%lld)", (long long)rows,
+                    (long long)cols);
+    if (rows > 0 && cols > 0 && (!P || !dY || !dX))
+        return fail(LB_EINVAL, "softmax_bwd: NULL P, dY or dX with rows=%lld cols=%lld", (long long)rows,
+                    (long long)cols);
+    lb::SoftmaxArgs a;
+    a.P = P;
+    a.dY = dY;
+    a.dX = dX;
+    a.rows = rows;
+    a.cols = cols;
+    a.bf16 = dtype == LB_BF16;
+    hipError_t e = lb::launch_softmax_bwd(a, tl_stream);
+    if (e != hipSuccess)
+        return hip_fail("softmax_bwd", e);
+    return LB_OK;
+}
+
 int lb_set_stream(void *hip_stream) {
     tl_stream = static_cast<hipStream_t>(hip_stream);
     return LB_OK;

@@ -70,4 +70,16 @@ struct BiasArgs {
 // db[n] = sum_m dY[m,n]; one or two launches; N = 0 launches nothing.
 hipError_t launch_bias_grad(const BiasArgs &a, hipStream_t s);
 
+// ---- softmax backward ---------------------------------------------------
+constexpr int64_t kSoftmaxWaveMaxCols = 4096; // longest row one wave holds in registers
+
+struct SoftmaxArgs {
+    const void *P, *dY; // [rows, cols] bf16 or fp32
+    void *dX;           // [rows, cols], same type; may be P or dY
+    int64_t rows, cols;
+    bool bf16;
+};
+
+hipError_t launch_softmax_bwd(const SoftmaxArgs &a, hipStream_t s);
+
 } // namespace lb

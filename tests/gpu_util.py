@@ -18,6 +18,24 @@ NORM_ULP = 1          # gradient norm: fp32 ulps from the oracle (same exact squ
 CLIP_ULP = 2          # clip factor: fp32 ulps from the oracle's
 DB_RELF = 1e-5        # fp32 bias gradient vs fp64: relative Frobenius error
 DB_ABS = 1e-5         # ... and per column |error| <= DB_ABS * sum_m |dY[m,n]|
+SM_RELF = {"f32": 1e-5, "bf16": 4e-3}   # softmax backward vs fp64: relative Frobenius error
+
+
+def softmax_bound(P, dY, cols, dtype):
+    """Per-element error bound of an fp32 softmax backward: the row's dot product summed
+    in chains of at most cols/64 + 64 terms (relative error of the dot at most
+    2^-24 * that length * sum_j |P_j dY_j|), one rounding each for the difference and the
+    product, and the final rounding to bf16 (half an ulp, 2^-9) when dtype is bf16."""
+    u = 2.0 ** -24
+    P = np.abs(np.asarray(P, np.float64))
+    g = np.abs(np.asarray(dY, np.float64))
+    S = np.sum(P * g, axis=1, keepdims=True)
+    gamma = u * (cols / 64.0 + 64.0)
+    ref_mag = P * (g + S)
+    b = P * (gamma * S + 2 * u * (g + S)) + 2 * u * ref_mag
+    if dtype == "bf16":
+        b = b + 2.0 ** -8 * ref_mag
+    return b
 
 
 class Guarded:

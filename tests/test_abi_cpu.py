@@ -24,7 +24,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("lin_bwd", "adamw_step", "adamw_step_f16", "adamw_step_bf16", "adamw_step_ex",
-                 "grad_norm", "lin_bwd_ex",
+                 "grad_norm", "lin_bwd_ex", "softmax_bwd",
                  "lb_set_stream", "lb_last_error", "lb_version"):
         assert want in names
 
@@ -195,3 +195,32 @@ def test_lin_bwd_ex_binding_checks():
         lb.lin_bwd_ex(torch.zeros(4, 3, dtype=torch.bfloat16), None, g, db=torch.zeros(6))
     with pytest.raises(TypeError):
         lb.lin_bwd_ex(None, None, g.to(torch.float16), db=torch.zeros(6))
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(dtype=2), -2), (dict(dtype=9), -2),
+    (dict(rows=-1), -1), (dict(cols=-3), -1), (dict(rows=1 << 40), -1),
+    (dict(), -1),                                   # NULL buffers with rows, cols > 0
+    (dict(rows=0), 0), (dict(cols=0), 0),           # nothing to write
+])
+def test_softmax_bwd_rejects_on_host(args, code):
+    a = dict(rows=4, cols=8, dtype=1)
+    a.update(args)
+    rc = lb.library().softmax_bwd(NULL, NULL, NULL, a["rows"], a["cols"], a["dtype"])
+    assert rc == code
+    assert (lb.lb_last_error() != "") == (code != 0)
+
+
+def test_softmax_bwd_binding_checks():
+    import torch
+    p = torch.zeros(4, 8)
+    with pytest.raises(TypeError):
+        lb.softmax_bwd(p, p.to(torch.bfloat16))
+    with pytest.raises(TypeError):
+        lb.softmax_bwd(p.double(), p.double())
+    with pytest.raises(ValueError):
+        lb.softmax_bwd(p, torch.zeros(4, 9))
+    with pytest.raises(ValueError):
+        lb.softmax_bwd(p, p, torch.zeros(4, 8, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        lb.softmax_bwd(p.t(), p.t())
