@@ -227,29 +227,65 @@ __device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, i
     tj = in_group / rows;
 }
 
-// Epilogue: block (x, y) of lane l holds C[i][j..j+3] for i = 16x + l%16,
-// j = 16y + 4*(l/16) within the wave's quadrant; bf16 (dX) or fp32 (dW) out.
+// Epilogue.  Block (x, y) of lane l holds C[i][j..j+3] for i = 16x + l%16,
+// j = 16y + 4*(l/16) within the wave's 128x128 quadrant, so a direct store
+// instruction would write 16 rows x 32 or 64 bytes: partial-line requests,
+// which, issued by every CU at the end of its tile at once, made the epilogue
+// cost as much as several k-steps.  Instead each wave first writes its
+// quadrant to its own 32 KiB of LDS (the operand ring is free once every wave
+// is past its last slab: one barrier), row-major with 16-byte chunk c of row r
+// at chunk c ^ (r % 16) (16 consecutive rows of one chunk hit distinct banks),
+// then reads it back a row segment per lane group and stores whole 128-byte
+// lines: dX (bf16) as 32 stores of 4 rows x 256 B, dW (fp32) in two halves of
+// 64 rows, each 32 stores of 2 rows x 512 B.
 template <int KIND>
 __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[kFrags][kFrags], const TileJob &jb, int64_t i0,
-                                           int64_t j0, int wm, int wn, int lane) {
-    const int64_t ib = i0 + wm * 128 + (lane & 15);
-    const int64_t jb0 = j0 + wn * 128 + 4 * (lane >> 4);
+                                           int64_t j0, int w, int wm, int wn, int lane, LDS char *smem) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // no operand DMA still landing in the ring
+    slab_barrier();
+    LDS char *const reg = smem + w * 32768;
+    const int64_t ib = i0 + wm * 128;
+    const int64_t jb0 = j0 + wn * 128;
+    if constexpr (KIND == JOB_DX) {
 #pragma unroll
-    for (int x = 0; x < kFrags; ++x) {
-        const int64_t i = ib + x * 16;
-        if (i >= jb.I)
-            continue;
+        for (int x = 0; x < kFrags; ++x)
 #pragma unroll
-        for (int y = 0; y < kFrags; ++y) {
-            const int64_t j = jb0 + y * 16;
-            if (j >= jb.J)
-                continue; // J % 8 == 0: j..j+3 all in range
-            const f32x4_t &a = acc[x][y];
-            if (KIND == JOB_DX) {
-                u32x2_t pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-                *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(jb.c) + i * jb.J + j) = pk;
-            } else {
-                *reinterpret_cast<f32x4_t *>(static_cast<float *>(jb.c) + i * jb.J + j) = a;
+            for (int y = 0; y < kFrags; ++y) {
+                const int r = 16 * x + (lane & 15);
+                const int c = 16 * y + 4 * (lane >> 4); // bf16 column, 4 per lane
+                const f32x4_t &a = acc[x][y];
+                const u32x2_t pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+                *reinterpret_cast<LDS u32x2_t *>(reg + r * 256 + (((c >> 3) ^ (r & 15)) << 4) + (c & 4) * 2) = pk;
+            }
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            const int r = 4 * q + (lane >> 4);
+            const int k = lane & 15; // 8 bf16 columns
+            const u32x4_t v = *reinterpret_cast<const LDS u32x4_t *>(reg + r * 256 + ((k ^ (r & 15)) << 4));
+            const int64_t i = ib + r, j = jb0 + 8 * k;
+            if (i < jb.I && j < jb.J) // J % 8 == 0: j..j+7 all in range
+                *reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(jb.c) + i * jb.J + j) = v;
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int x = 0; x < kFrags / 2; ++x)
+#pragma unroll
+                for (int y = 0; y < kFrags; ++y) {
+                    const int r = 16 * x + (lane & 15);
+                    const int c = 16 * y + 4 * (lane >> 4); // fp32 column, 4 per lane
+                    *reinterpret_cast<LDS f32x4_t *>(reg + r * 512 + (((c >> 2) ^ (r & 15)) << 4)) =
+                        acc[h * (kFrags / 2) + x][y];
+                }
+#pragma unroll
+            for (int q = 0; q < 32; ++q) {
+                const int r = 2 * q + (lane >> 5);
+                const int k = lane & 31; // 4 fp32 columns
+                const f32x4_t v = *reinterpret_cast<const LDS f32x4_t *>(reg + r * 512 + ((k ^ (r & 15)) << 4));
+                const int64_t i = ib + 64 * h + r, j = jb0 + 4 * k;
+                if (i < jb.I && j < jb.J)
+                    *reinterpret_cast<f32x4_t *>(static_cast<float *>(jb.c) + i * jb.J + j) = v;
             }
         }
     }
@@ -445,7 +481,7 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
         }
     }
     mfma_drain();
-    store_tile<JOB_DX>(acc, jb, i0, j0, wm, wn, lane);
+    store_tile<JOB_DX>(acc, jb, i0, j0, w, wm, wn, lane, smem);
 }
 
 // dW tile (OC operands).  Wave w = 2*wm + wn owns the 128x128 quadrant
@@ -640,7 +676,7 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
     }
 
     mfma_drain();
-    store_tile<JOB_DW>(acc, jb, i0, j0, wm, wn, lane);
+    store_tile<JOB_DW>(acc, jb, i0, j0, w, wm, wn, lane, smem);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
