@@ -231,59 +231,60 @@ __device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, i
 // j = 16y + 4*(l/16) within the wave's 128x128 quadrant, so a direct store
 // instruction would write 16 rows x 32 or 64 bytes: partial-line requests,
 // which, issued by every CU at the end of its tile at once, made the epilogue
-// cost as much as several k-steps.  Instead each wave first writes its
-// quadrant to its own 32 KiB of LDS (the operand ring is free once every wave
-// is past its last slab: one barrier), row-major with 16-byte chunk c of row r
-// at chunk c ^ (r % 16) (16 consecutive rows of one chunk hit distinct banks),
-// then reads it back a row segment per lane group and stores whole 128-byte
-// lines: dX (bf16) as 32 stores of 4 rows x 256 B, dW (fp32) in two halves of
-// 64 rows, each 32 stores of 2 rows x 512 B.
+// cost as much as several k-steps.  Instead each wave passes its quadrant
+// through its own 8 KiB of LDS beyond the operand ring (no barrier: nothing
+// else touches it) in rounds of 32 rows (dX, bf16: 4 rounds) or 16 rows (dW,
+// fp32: 8 rounds), row-major with 16-byte chunk c of row r at chunk c ^ (r % 16)
+// (16 consecutive rows of one chunk hit distinct banks), reads each round
+// back a row segment per lane group and stores whole 128-byte lines.
+constexpr int kEpiBytes = 8192; // per wave
 template <int KIND>
 __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[kFrags][kFrags], const TileJob &jb, int64_t i0,
                                            int64_t j0, int w, int wm, int wn, int lane, LDS char *smem) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // no operand DMA still landing in the ring
-    slab_barrier();
-    LDS char *const reg = smem + w * 32768;
+    LDS char *const reg = smem + kLdsBytes + w * kEpiBytes;
     const int64_t ib = i0 + wm * 128;
     const int64_t jb0 = j0 + wn * 128;
     if constexpr (KIND == JOB_DX) {
+        // round h: fragment rows x = 2h, 2h+1 (quadrant rows 32h .. 32h+31), 256 B each
 #pragma unroll
-        for (int x = 0; x < kFrags; ++x)
+        for (int h = 0; h < kFrags / 2; ++h) {
 #pragma unroll
-            for (int y = 0; y < kFrags; ++y) {
-                const int r = 16 * x + (lane & 15);
-                const int c = 16 * y + 4 * (lane >> 4); // bf16 column, 4 per lane
-                const f32x4_t &a = acc[x][y];
-                const u32x2_t pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-                *reinterpret_cast<LDS u32x2_t *>(reg + r * 256 + (((c >> 3) ^ (r & 15)) << 4) + (c & 4) * 2) = pk;
-            }
-#pragma unroll
-        for (int q = 0; q < 32; ++q) {
-            const int r = 4 * q + (lane >> 4);
-            const int k = lane & 15; // 8 bf16 columns
-            const u32x4_t v = *reinterpret_cast<const LDS u32x4_t *>(reg + r * 256 + ((k ^ (r & 15)) << 4));
-            const int64_t i = ib + r, j = jb0 + 8 * k;
-            if (i < jb.I && j < jb.J) // J % 8 == 0: j..j+7 all in range
-                *reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(jb.c) + i * jb.J + j) = v;
-        }
-    } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int x = 0; x < kFrags / 2; ++x)
+            for (int xx = 0; xx < 2; ++xx)
 #pragma unroll
                 for (int y = 0; y < kFrags; ++y) {
-                    const int r = 16 * x + (lane & 15);
-                    const int c = 16 * y + 4 * (lane >> 4); // fp32 column, 4 per lane
-                    *reinterpret_cast<LDS f32x4_t *>(reg + r * 512 + (((c >> 2) ^ (r & 15)) << 4)) =
-                        acc[h * (kFrags / 2) + x][y];
+                    const int r = 16 * xx + (lane & 15);
+                    const int c = 16 * y + 4 * (lane >> 4); // bf16 column, 4 per lane
+                    const f32x4_t &a = acc[2 * h + xx][y];
+                    const u32x2_t pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+                    *reinterpret_cast<LDS u32x2_t *>(reg + r * 256 + (((c >> 3) ^ (r & 15)) << 4) + (c & 4) * 2) =
+                        pk;
                 }
 #pragma unroll
-            for (int q = 0; q < 32; ++q) {
+            for (int q = 0; q < 8; ++q) {
+                const int r = 4 * q + (lane >> 4);
+                const int k = lane & 15; // 8 bf16 columns
+                const u32x4_t v = *reinterpret_cast<const LDS u32x4_t *>(reg + r * 256 + ((k ^ (r & 15)) << 4));
+                const int64_t i = ib + 32 * h + r, j = jb0 + 8 * k;
+                if (i < jb.I && j < jb.J) // J % 8 == 0: j..j+7 all in range
+                    *reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(jb.c) + i * jb.J + j) = v;
+            }
+        }
+    } else {
+        // round x: fragment row x (quadrant rows 16x .. 16x+15), 512 B each
+#pragma unroll
+        for (int x = 0; x < kFrags; ++x) {
+#pragma unroll
+            for (int y = 0; y < kFrags; ++y) {
+                const int r = lane & 15;
+                const int c = 16 * y + 4 * (lane >> 4); // fp32 column, 4 per lane
+                *reinterpret_cast<LDS f32x4_t *>(reg + r * 512 + (((c >> 2) ^ r) << 4)) = acc[x][y];
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
                 const int r = 2 * q + (lane >> 5);
                 const int k = lane & 31; // 4 fp32 columns
-                const f32x4_t v = *reinterpret_cast<const LDS f32x4_t *>(reg + r * 512 + ((k ^ (r & 15)) << 4));
-                const int64_t i = ib + 64 * h + r, j = jb0 + 4 * k;
+                const f32x4_t v = *reinterpret_cast<const LDS f32x4_t *>(reg + r * 512 + ((k ^ r) << 4));
+                const int64_t i = ib + 16 * x + r, j = jb0 + 4 * k;
                 if (i < jb.I && j < jb.J)
                     *reinterpret_cast<f32x4_t *>(static_cast<float *>(jb.c) + i * jb.J + j) = v;
             }
@@ -680,7 +681,7 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes + 4 * kEpiBytes];
     LDS char *smem = (LDS char *)smem_raw;
     int b = blockIdx.x;
     const TileJob *jb = &p.job[0];
