@@ -297,11 +297,13 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[kFrags][kFrags],
 // (r 0..63 of the pair), so each 8-lane group of a DMA instruction fetches one
 // whole 128-byte line: half-line requests would double the L1->L2 request
 // count.  The 128 KiB hold two such pairs per operand.  16-byte chunk c of row
-// o is stored at chunk c ^ swz_rcp(o), which keeps any 8 (or any 16, on two
-// 128-byte rows per bank sweep) consecutive rows of one chunk on distinct banks.
+// o is stored at chunk c ^ (o % 8), so the 8 rows of one chunk that a fragment
+// read serves together sit on distinct banks (measured with the LDS conflict
+// counter: 0 conflict cycles; also folding bit 3 of the row into the XOR, as
+// an earlier layout did, gave conflicts in a quarter of the active cycles).
 constexpr int kPairBytes = 2 * kOperandBytes; // 32 KiB per operand
 constexpr int kDmaPerOpPair = 8;              // DMA instructions per wave per operand per pair
-__device__ __forceinline__ int swz_rcp(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz_rcp(int row) { return row & 7; }
 __device__ __forceinline__ int rcp_off(int o, int c) { return o * 128 + ((c ^ swz_rcp(o)) << 4); }
 // fragment of outer block ob (16 wide) for slab half h of a pair
 __device__ __forceinline__ int frag_off_rcp(int ob, int lane, int h) {
