@@ -57,9 +57,9 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 // global->LDS DMA (buffer_load_dwordx4 ... lds: lane l of a wave
 // instruction writes 16 bytes at M0 + 16*l, so one instruction fills 1 KiB).
 // The XOR swizzles are applied by choosing which global chunk each lane
-// fetches; the LDS side is always contiguous.  Both swizzles are free of bank
-// conflicts whether the LDS serves 8 or 16 lanes of a 16-byte read (resp. 16
-// or 32 lanes of an 8-byte read) per cycle.
+// fetches; the LDS side is always contiguous.  Both are free of bank
+// conflicts for the fragment reads, as measured with the LDS bank-conflict
+// counter on in-bounds probes of the exact read patterns.
 //
 //  RC ("reduction contiguous", dX operands dY and W): slab pairs, described
 //     with the dX pipeline below.
