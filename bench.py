@@ -58,7 +58,10 @@ def _sync():
 
 
 KERNEL_SOURCES = {"k_lin_bwd_mfma": "linear_layer_backward_bwd_amd/csrc/lin_bwd.hip",
-                  "k_adamw": "linear_layer_backward_bwd_amd/csrc/adamw.hip"}
+                  "k_adamw": "linear_layer_backward_bwd_amd/csrc/adamw.hip",
+                  "k_norm_partial": "linear_layer_backward_bwd_amd/csrc/grad_norm.hip",
+                  "k_bias_partial": "linear_layer_backward_bwd_amd/csrc/bias_grad.hip",
+                  "k_softmax_bwd_wave": "linear_layer_backward_bwd_amd/csrc/softmax_bwd.hip"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -248,7 +251,8 @@ def bench_adamw(n, steps, warmup, seed):
     gbps = ADAMW_BYTES_16BIT_GRAD * n / (ms * 1e-3) / 1e9
     return {"n": n, "grad": "f16", "ms": round(ms, 4), "gbps": round(gbps, 1),
             "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
-            "gparams_per_s": round(n / (ms * 1e-3) / 1e9, 2)}
+            "gparams_per_s": round(n / (ms * 1e-3) / 1e9, 2),
+            "traffic": recorded_traffic("k_adamw", "adamw_2p28_f16")}
 
 
 def bench_clipped_step(n, steps, warmup, seed):
@@ -286,10 +290,12 @@ def bench_clipped_step(n, steps, warmup, seed):
     return {"n": n, "grad": "f16", "copy": "bf16",
             "grad_norm": {"ms": round(norm_ms, 4), "gbps": round(norm_gbps, 1),
                           "frac_of_hbm_peak": round(norm_gbps / PEAK_HBM_GBPS, 4),
-                          "bytes_per_param": GRAD_NORM_BYTES_16BIT},
+                          "bytes_per_param": GRAD_NORM_BYTES_16BIT,
+                          "traffic": recorded_traffic("k_norm_partial", "grad_norm_2p28_f16")},
             "adamw_step_ex": {"ms": round(upd_ms, 4), "gbps": round(upd_gbps, 1),
                               "frac_of_hbm_peak": round(upd_gbps / PEAK_HBM_GBPS, 4),
-                              "bytes_per_param": ADAMW_EX_BYTES_16BIT_GRAD_BF16_COPY},
+                              "bytes_per_param": ADAMW_EX_BYTES_16BIT_GRAD_BF16_COPY,
+                              "traffic": recorded_traffic("k_adamw", "adamw_ex_2p28_f16_bf16_copy")},
             "step_ms": round(step_ms, 4),
             "gparams_per_s": round(n / (step_ms * 1e-3) / 1e9, 2)}
 
@@ -315,7 +321,8 @@ def bench_bias(steps, warmup, seed):
     gbps = nbytes / (ms * 1e-3) / 1e9
     return {"workload": "block dY, M=16384, N=12288/4096/16384/4096, bf16", "ms": round(ms, 4),
             "gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
-            "bytes": nbytes}
+            "bytes": nbytes,
+            "traffic_per_launch": recorded_traffic("k_bias_partial", "bias_grad_block_M16384")}
 
 
 def bench_softmax(steps, warmup, seed):
@@ -338,7 +345,8 @@ def bench_softmax(steps, warmup, seed):
     gbps = nbytes / (ms * 1e-3) / 1e9
     return {"workload": "softmax_bwd rows=%d (8x32x2048) cols=%d bf16" % (rows, cols),
             "ms": round(ms, 4), "gbps": round(gbps, 1),
-            "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "bytes_per_elem": 6}
+            "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "bytes_per_elem": 6,
+            "traffic": recorded_traffic("k_softmax_bwd_wave", "softmax_bwd_524288x2048_bf16")}
 
 
 def cpu_baseline(cases, opt, target_s=12.0):
