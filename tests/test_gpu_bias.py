@@ -83,7 +83,7 @@ def test_empty_sum_writes_zeros():
 @pytest.mark.parametrize("M,N", [(3, (1 << 20) + 8), (400, 200000)])
 def test_wide_outputs(M, N):
     """Past 2^20 columns one row split remains and the first pass writes db itself;
-    at 200000 columns the workspace caps the splits below the target (5 instead of 6)."""
+    200000 columns: 391 strips of 512 columns, 3 row splits (the most partials a launch writes)."""
     G = synth.to_storage(synth.normal((M, N), 1.0, synth._gen(9)), "bf16")
     check(gpu_db(G), G, "bf16")
 
