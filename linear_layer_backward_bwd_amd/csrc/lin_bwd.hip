@@ -327,11 +327,12 @@ __device__ __forceinline__ uint32_t dma_rcp_off(int p, int64_t ld, int64_t O, in
 // slab t the MFMAs use slab t's fragments (in registers) while slab t+1's are
 // read; an odd slab t first waits for pair (t+1)/2 and barriers (after which
 // the slot of pair (t-1)/2, whose fragments are all in registers, is free),
-// then issues the first half of the DMA of pair (t+3)/2 into that slot, and
-// the even slab after it the second half: a pair is fetched one to two slabs
-// ahead of its first use, with one barrier per pair.  (All 16 DMA instructions
-// of a pair in one slab kept the CU's address path busy for that whole slab;
-// the waves then stalled unevenly and the barrier paid for the skew.)
+// then issues the DMA of pair (t+3)/2 into that slot, one instruction every
+// fourth MFMA: a pair is fetched one to two slabs ahead of its first use, with
+// one barrier per pair.  The spacing keeps the CU's address path at its rate
+// (the four waves' 64 instructions of 1 KiB over 64 MFMAs); issued every
+// second MFMA, or half of them in the next slab, the address FIFO filled, the
+// waves stalled unevenly and the barrier paid for the skew (block 1.8% slower).
 __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS char *smem) {
     static_assert(kStages * kOperandBytes == 2 * kPairBytes, "two pairs per operand");
     constexpr int kReads = 2 * kFrags; // ds_read_b128 per wave per slab
@@ -409,16 +410,14 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
         const int op = j / kFrags, xb = j % kFrags;
         (op == 0 ? an : bn)[xb] = read_rc<off>(smem + fo[op][xb][m & 1]);
     };
-    // slab t with t % 4 == TM (compile time); flags as described above.  Its
-    // DMAs: an odd slab issues instructions 0..7 of pair (t+3)/2, an even slab
-    // instructions 8..15 of pair (t+2)/2 (the same pair, one slab later).
+    // slab t with t % 4 == TM (compile time); flags as described above (only
+    // odd slabs issue DMAs: the 16 instructions of pair (t+3)/2)
     auto slab = [&](int t, auto tm, bool dmas, bool tail, bool N, Frags &af, Frags &bf, Frags &an, Frags &bn) {
         constexpr int m = decltype(tm)::value;
         constexpr bool odd = m & 1;
-        constexpr int d0 = odd ? 0 : kDmaPerOpPair;
-        const int q = odd ? (t + 3) / 2 : (t + 2) / 2;
+        const int q = (t + 3) / 2;
         PairSrc src{};
-        if (dmas)
+        if (odd && dmas)
             src = pair_src(q);
         if (odd && N) {
             dma_wait(0);
@@ -432,8 +431,8 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
             __builtin_amdgcn_sched_barrier(0);
             if (i % 2 == 0 && i / 2 < kReads)
                 read_frag(std::integral_constant<int, (m + 1) % 4>{}, i / 2, an, bn);
-            if (dmas && i % 2 == 1 && i / 2 < kDmaPerOpPair) {
-                const int d = d0 + i / 2;
+            if (odd && dmas && i % 4 == 1) { // MFMAs 1, 5, ..., 61
+                const int d = i / 4;
                 dma(src, q, d & 1, d >> 1, tail);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -444,16 +443,15 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
 
     Frags af, bf, an, bn;
     if (nslab4 > 0) {
-        // prologue: pair 0 and the first half of pair 1 (slab 0 issues the
-        // second); wait for pair 0 and read slab 0
+        // prologue: pairs 0 and 1 fill both slots; wait for pair 0 and read slab 0
         for (int q = 0; q < 2; ++q) {
             const PairSrc src = pair_src(q);
             const bool tail = ptail && q == npair - 1;
 #pragma unroll
-            for (int d = 0; d < (q == 0 ? 2 : 1) * kDmaPerOpPair; ++d)
+            for (int d = 0; d < 2 * kDmaPerOpPair; ++d)
                 dma(src, q, d & 1, d >> 1, tail);
         }
-        dma_wait(kDmaPerOpPair);
+        dma_wait(2 * kDmaPerOpPair);
         slab_barrier();
 #pragma unroll
         for (int j = 0; j < kReads; ++j)
@@ -465,7 +463,7 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
         using C2 = std::integral_constant<int, 2>;
         using C3 = std::integral_constant<int, 3>;
         int s = 0;
-        // steady state: the pairs issued (s/2 + 1 .. s/2 + 3) are full ones
+        // steady state: the pairs issued (s/2 + 2, s/2 + 3) are full ones
         for (; s / 2 + 4 < npair; s += 4) {
             slab(s + 0, C0{}, true, false, false, af, bf, an, bn);
             slab(s + 1, C1{}, true, false, true, an, bn, af, bf);
@@ -474,8 +472,8 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
         }
         auto flags = [&](int t, bool &dmas, bool &tail, bool &N) {
             const bool odd = t & 1;
-            const int q = odd ? (t + 3) / 2 : (t + 2) / 2;
-            dmas = q < P;
+            const int q = (t + 3) / 2;
+            dmas = odd && q < P;
             tail = dmas && ptail && q == npair - 1;
             N = odd && t + 1 < nslab4;
         };
