@@ -88,9 +88,9 @@ struct TileJob {
     uint32_t a_bytes, b_bytes; // operand sizes (each < 2 GiB on this path)
     int tiles_i, tiles_j, ntiles;
     int kind;          // JOB_DX: RC operands, bf16 out; JOB_DW: OC operands, fp32 out
-    // k rotation: the tile at (ti, tj) walks the slabs starting at
-    // (rot_i*(ti%4) + rot_j*(tj%8)) mod nslab (0 for a ragged RC reduction)
-    int rot_i, rot_j;
+    // k rotation (slabs): the tile at (ti, tj) walks the slabs starting at
+    // rot * ((tj / 2) % 4) mod nslab (0 for a ragged RC reduction)
+    int rot;
 };
 
 struct MfmaParams {
@@ -371,7 +371,7 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
     const int P = nslab4 / 2;                                     // pairs, padding included
     const bool ptail = (R % 64) != 0;                             // last real pair is partial
     // rotation of the reduction order (see TileJob), in whole pairs
-    const int rotp = ptail || npair == 0 ? 0 : ((jb.rot_i * (ti & 3) + jb.rot_j * (tj & 7)) >> 1) % npair;
+    const int rotp = ptail || npair == 0 ? 0 : ((jb.rot * ((tj >> 1) & 3)) >> 1) % npair;
     LDS char *const wdst = smem + w * kDmaPerOpPair * 1024;
 
     struct PairSrc {
@@ -535,7 +535,7 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
 
     const int nslab = (int)((jb.R + kBK - 1) / kBK);
     // optional rotation of the reduction order (see TileJob)
-    const int rot = nslab == 0 ? 0 : (jb.rot_i * (ti & 3) + jb.rot_j * (tj & 7)) % nslab;
+    const int rot = nslab == 0 ? 0 : (jb.rot * ((tj >> 1) & 3)) % nslab;
     // per-slab source advance (elements) of each operand
     const int64_t step_a = (int64_t)kBK * jb.lda;
     const int64_t step_b = (int64_t)kBK * jb.ldb;
@@ -873,8 +873,7 @@ TileJob make_tile_job(int kind, const void *a, const void *b, void *c, int64_t I
     j.tiles_j = ceil_div(J, kTile);
     j.ntiles = j.tiles_i * j.tiles_j;
     j.kind = kind;
-    j.rot_i = 0;
-    j.rot_j = 0;
+    j.rot = 0;
     return j;
 }
 
@@ -935,15 +934,17 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
     if (need_dx && !small_dx) {
         jx = make_tile_job(JOB_DX, a.dY, a.W, a.dX, a.M, a.K, a.N, a.N, a.N);
         // Rows of both RC operands are 2N bytes apart.  When that is a multiple
-        // of 32 KiB, the same k of every row maps to one small group of L2 sets
-        // and the tiles running together on an XCD evict each other's lines;
-        // giving each of them its own starting slab spreads them out (measured
-        // on 16384x4096x16384: 860 -> 1090 TFLOP/s for dX).  Other strides are
-        // left alone: there the lockstep order shares lines in L2 best.
-        if ((2 * a.N) % 32768 == 0) {
-            jx.rot_i = 4;
-            jx.rot_j = 16;
-        }
+        // of 32 KiB, the same k of every row maps to one small group of L2 sets:
+        // the 32 tiles running together on an XCD (4 tile rows x 8 tile columns)
+        // touch about 3072 such lines per slab pair, the sets hold about 2048,
+        // and the tiles evict each other's lines.  Four groups of tiles (by tile
+        // column) start 32 slabs apart: each group's lines fit and are shared
+        // within the group (measured on 16384x4096x16384: dX 860 -> 1090 TFLOP/s
+        // for a distinct start per tile, 1289 -> 1327 for the four groups over
+        // that).  Other strides are left alone: there the lockstep order shares
+        // lines in L2 best.
+        if ((2 * a.N) % 32768 == 0)
+            jx.rot = 32;
         have_x = true;
     }
     if (need_dw) {
