@@ -32,13 +32,15 @@ int hip_fail(const char *what, hipError_t e) {
 bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; } // false for NaN
 
 // Library-owned workspace, allocated on first use on each device and kept
-// until the process ends: grad_norm's per-block partial sums and flags and
-// lin_bwd_ex's per-split bias partials, in separate regions.  Calls of one
-// entry point that overlap on one device share its region (and would race).
+// until the process ends: grad_norm's per-block partial sums and flags,
+// lin_bwd_ex's per-split bias partials and the fp32 dX partials of lin_bwd's
+// M <= 64 path, in separate regions.  Calls of one entry point that overlap on
+// one device share its region (and would race).
 struct Workspace {
     double *norm_partial = nullptr;
     int *norm_flag = nullptr;
     float *bias_partial = nullptr;
+    float *dx_partial = nullptr;
 };
 std::mutex ws_mutex;
 std::unordered_map<int, Workspace> ws_by_device;
@@ -53,14 +55,16 @@ hipError_t workspace(Workspace &out) {
     if (it == ws_by_device.end()) {
         const size_t norm_bytes = lb::kNormMaxBlocks * (sizeof(double) + sizeof(int));
         const size_t bias_bytes = lb::kBiasWorkspaceFloats * sizeof(float);
+        const size_t dx_bytes = lb::kDxPartialFloats * sizeof(float);
         void *p = nullptr;
-        e = hipMalloc(&p, norm_bytes + bias_bytes);
+        e = hipMalloc(&p, norm_bytes + bias_bytes + dx_bytes);
         if (e != hipSuccess)
             return e;
         Workspace w;
         w.norm_partial = static_cast<double *>(p);
         w.norm_flag = reinterpret_cast<int *>(w.norm_partial + lb::kNormMaxBlocks);
         w.bias_partial = reinterpret_cast<float *>(static_cast<char *>(p) + norm_bytes);
+        w.dx_partial = reinterpret_cast<float *>(static_cast<char *>(p) + norm_bytes + bias_bytes);
         it = ws_by_device.emplace(dev, w).first;
     }
     out = it->second;
@@ -135,7 +139,8 @@ int lin_bwd_ex(const void *X, const void *W, const void *dY, void *dX, float *dW
     if (db && N > 0 && M > 0 && !dY)
         return fail(LB_EINVAL, "%s: db requested but dY is NULL", name);
     Workspace ws;
-    if (db && N > 0) {
+    const bool small_dx = dX && dtype == LB_BF16 && M > 0 && M <= 64 && K > 0 && N > 0;
+    if ((db && N > 0) || small_dx) {
         hipError_t e = workspace(ws);
         if (e != hipSuccess)
             return hip_fail("lin_bwd_ex (workspace)", e);
@@ -150,6 +155,8 @@ int lin_bwd_ex(const void *X, const void *W, const void *dY, void *dX, float *dW
     a.K = K;
     a.N = N;
     a.bf16 = dtype == LB_BF16;
+    a.dx_partial = ws.dx_partial;
+    a.dx_partial_floats = ws.dx_partial ? lb::kDxPartialFloats : 0;
     hipError_t e = lb::launch_lin_bwd(a, tl_stream);
     if (e != hipSuccess)
         return hip_fail(name, e);

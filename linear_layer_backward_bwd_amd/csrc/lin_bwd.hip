@@ -22,9 +22,12 @@
 //                    One launch runs the tiles of both products; blocks are ordered
 //                    longest reduction first and mapped so that each XCD works on a
 //                    compact group of tiles.
-//   k_dx_smallm      dX for M <= 64 (decode-like): bound by streaming W once, so the
-//                    reduction over n is split across the waves of a block and
-//                    operands go straight from global memory into MFMA registers.
+//   k_dx_smallm      dX for M <= 64 (decode-like): streams W once, the reduction
+//                    over n split across blocks; the fp32 partials are added in
+//                    split order by the first blocks of k_dw_smallm (or by
+//                    k_dx_smallm_reduce when dW is not requested).
+//   k_dw_smallm      dW for M <= 64: bound by writing the fp32 output; small tiles,
+//                    several per CU, so stores overlap other tiles' loads.
 //   k_lin_bwd_simt   any dtype / alignment / shape: fp32 path and ragged bf16 shapes.
 #include "device.h"
 #include "kernels.h"
@@ -709,77 +712,263 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
 }
 
 // ------------------------------------------------------------------------
-// small-M dX: dX[m,k] = Σ_n dY[m,n]·W[k,n] for M <= 64
+// small M (M <= 64, decode-like): both products are bound by HBM, not MFMA:
+// dX streams W (2KN bytes), dW writes the fp32 output (4KN bytes).  They run
+// as two launches.  (One launch holding the blocks of both was slower where it
+// mattered: the dX blocks took every CU first, the dW blocks then ran at the
+// merged kernel's lower occupancy, and at N = 16384 the mixed read and write
+// streams made it 40% slower than the two launches in turn.)
 // ------------------------------------------------------------------------
-constexpr int kSmallWaves = 8;
-constexpr int kSmallUnroll = 8;
 constexpr int kSmallMaxM = 64;
 
-// Block: 16 output columns k (one 16x16x32 MFMA column block), all M rows
-// (up to 4 blocks of 16).  Wave w reduces n over its own contiguous range;
-// the per-wave partials are summed in LDS in a fixed order.
-__global__ __launch_bounds__(kSmallWaves * 64) void k_dx_smallm(const uint16_t *__restrict__ G,
-                                                                 const uint16_t *__restrict__ W,
-                                                                 uint16_t *__restrict__ dX,
-                                                                 int64_t M, int64_t K, int64_t N) {
-    __shared__ f32x4_t red[kSmallWaves][4][64];
+struct SmallParams {
+    const uint16_t *X, *W, *G; // X[M,K], W[K,N], dY[M,N]
+    uint16_t *dX;              // [M,K] bf16, or null
+    float *dW;                 // [K,N] fp32, or null
+    float *part;               // split partials [splits][M][K] (splits > 1)
+    int64_t M, K, N;
+    int64_t split_len;         // reduction elements per dX split (a multiple of 512)
+    int splits;                // dX splits per column group; dX block b = (split, group) (b % splits, b / splits)
+    int dw_tiles_n;            // dW block b = (n tile, k tile) (b % dw_tiles_n, b / dw_tiles_n)
+    int reduce_blocks;         // dW blocks that also add up dX partials
+};
+
+// dW[k,n] = Σ_m X[m,k]·dY[m,n] with M <= 32*NS: a rank-M product whose cost is
+// writing the output.  Small 64x256 tiles (several resident per CU) let one
+// tile's stores overlap other tiles' loads and MFMAs; a 256x256 tile of the
+// main kernel holds a CU for its whole tile and every CU then stores at once.
+// Per block: dY[0:M, n0:n0+256] goes to LDS by DMA as OC slabs (the main
+// kernel's layout and fragment reads), X[0:M, k0:k0+64] by plain loads as
+// 32-row slabs of 128-byte rows; wave w owns dW rows k0+16w .. +15 (16 blocks
+// of 16x16, one MFMA per block and slab), then passes them through 4 KiB of
+// LDS per wave in rounds of 64 columns so that each store instruction writes
+// 4 rows x 256 contiguous bytes.
+constexpr int kDwsBK = 64;                 // dW rows per block (16 per wave)
+constexpr int kDwsBN = kTile;              // dW columns per block (one OC slab row)
+constexpr int kDwsXSlab = 32 * kDwsBK * 2; // X slab in LDS: 32 rows x 128 B
+constexpr int kDwsStage = 4096;            // per-wave epilogue staging: 16 rows x 256 B
+template <int NS>
+constexpr int dw_small_lds() { return NS * (kOperandBytes + kDwsXSlab) + 4 * kDwsStage; }
+
+__device__ __forceinline__ bf16x8_t join4(bf16x4_t lo, bf16x4_t hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x4_t lds_tr(const LDS char *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4_t *)p);
+}
+
+template <int NS>
+__device__ __forceinline__ void dw_small_block(const SmallParams &p, int b, LDS char *smem) {
+    const int64_t M = p.M, K = p.K, N = p.N;
+    LDS char *const gs = smem;                      // NS OC slabs of dY (32 r x 256 n)
+    LDS char *const xs = smem + NS * kOperandBytes; // NS slabs of X (32 r x 64 k)
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    LDS char *const stage = xs + NS * kDwsXSlab + w * kDwsStage;
+    const int64_t n0 = (int64_t)(b % p.dw_tiles_n) * kDwsBN;
+    const int64_t k0 = (int64_t)(b / p.dw_tiles_n) * kDwsBK;
+
+    // dY slabs: rows past M (and columns past N) read zero through the buffer
+    // descriptor's size / an out-of-range offset
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int64_t r0 = 32 * s;
+        const uint32_t bytes = r0 < M ? (uint32_t)(2 * (M - r0) * N) : 0u;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.G + (r0 < M ? r0 * N : 0), bytes);
+#pragma unroll
+        for (int q = 0; q < kDmaPerOp; ++q)
+            dma16(rs, gs + s * kOperandBytes + (w * kDmaPerOp + q) * 1024, dma_oc_off(q, N, N, n0, w, lane));
+    }
+    // X slabs: thread t loads 16 bytes of row t/8 (chunk t%8)
+    {
+        const int row = threadIdx.x >> 3, ch = threadIdx.x & 7;
+        const int64_t k = k0 + 8 * ch;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int64_t m = 32 * s + row;
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (m < M && k < K) // K % 8 == 0: the chunk is all in or all out
+                v = *reinterpret_cast<const u32x4_t *>(p.X + m * K + k);
+            *reinterpret_cast<LDS u32x4_t *>(xs + s * kDwsXSlab + row * 128 + ch * 16) = v;
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // fragments: lane l holds outer index ob + l%16 and r = 8(l/16) .. +7,
+    // read as two transposing halves (r 4h .. 4h+3 of each 8)
+    f32x4_t acc[16];
+#pragma unroll
+    for (int y = 0; y < 16; ++y)
+        acc[y] = f32x4_t{};
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const LDS char *xb = xs + s * kDwsXSlab;
+        const int xcol = 16 * w + 4 * (sl & 3);
+        const bf16x8_t xf = join4(lds_tr(xb + (8 * g + (sl >> 2)) * 128 + xcol * 2),
+                                  lds_tr(xb + (8 * g + 4 + (sl >> 2)) * 128 + xcol * 2));
+        const LDS char *gb = gs + s * kOperandBytes;
+#pragma unroll
+        for (int y = 0; y < 16; ++y) {
+            const bf16x8_t gf = join4(lds_tr(gb + frag_off_oc(16 * y, lane, 0)),
+                                      lds_tr(gb + frag_off_oc(16 * y, lane, 1)));
+            // lane l: dW[k0 + 16w + l%16][n0 + 16y + 4(l/16) .. +3]
+            acc[y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf, xf, acc[y], 0, 0, 0);
+        }
+    }
+
+    // epilogue: round q covers columns 64q .. 64q+63 of the wave's 16 rows;
+    // 16-byte chunk c of staging row r sits at chunk c ^ r
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int yy = 0; yy < 4; ++yy) {
+            const int r = sl, c = 4 * yy + g;
+            *reinterpret_cast<LDS f32x4_t *>(stage + r * 256 + ((c ^ r) << 4)) = acc[4 * q + yy];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int r = 4 * t + g, c = sl;
+            const f32x4_t v = *reinterpret_cast<const LDS f32x4_t *>(stage + r * 256 + ((c ^ r) << 4));
+            const int64_t k = k0 + 16 * w + r, n = n0 + 64 * q + 4 * c;
+            if (k < K && n < N) // N % 8 == 0: n .. n+3 all in range
+                *reinterpret_cast<f32x4_t *>(p.dW + k * N + n) = v;
+        }
+    }
+}
+
+// dX[m,k] = Σ_n dY[m,n]·W[k,n] with M <= 16*MB: bound by streaming W once.
+// Block (s, grp): dX columns k0 = 64grp .. +63 (wave w: 16 of them, the rows
+// of W it streams) over the reduction range of split s, in chunks of 512 n.
+// Per chunk every lane issues all 16 of its W loads (16 bytes each, one per
+// 32-deep MFMA step) before waiting, and the block stages dY[0:M, chunk] in
+// LDS once for its four waves (16-byte chunk c of row m at chunk c ^ (m % 16):
+// the 16 rows one fragment read serves sit on distinct banks).  With one split
+// the block stores dX in bf16.  With several, each block stores its fp32
+// partial sums part[s][m][k] and k_dx_smallm_reduce adds them in split order.
+// (A last-block-reduces variant, counting finished splits with a device-scope
+// atomic, needs a device-scope release and acquire per block; on this part
+// those write back and invalidate the XCD's L2, and dX took 5x longer.)
+constexpr int kDxsBK = 64;     // dX columns per block
+constexpr int kDxsChunk = 512; // reduction elements per chunk (16 MFMA steps)
+template <int MB>
+constexpr int dx_small_lds() { return MB * 16 * kDxsChunk * 2; }
+
+template <int MB>
+__device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS char *gs) {
+    const int64_t M = p.M, K = p.K, N = p.N;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int64_t k0 = (int64_t)blockIdx.x * 16;
-    const int mb_count = (int)((M + 15) / 16);
-
-    // wave's reduction range, in units of 32
-    const int64_t steps = (N + 31) / 32;
-    const int64_t per_wave = (steps + kSmallWaves - 1) / kSmallWaves;
-    const int64_t s_beg = w * per_wave;
-    const int64_t s_end = min(steps, s_beg + per_wave);
-
-    const int64_t krow = k0 + (lane & 15);
+    const int s = b % p.splits, grp = b / p.splits;
+    const int64_t k0 = (int64_t)grp * kDxsBK;
+    const int64_t n_beg = (int64_t)s * p.split_len;
+    const int64_t n_end = min(N, n_beg + p.split_len);
+    const int64_t krow = k0 + 16 * w + (lane & 15);
     const bool kok = krow < K;
-    const int sub = 8 * (lane >> 4); // this lane's 8 reduction elements within a step of 32
-    const uint16_t *wrow = W + krow * N + sub;
+    const int sub = 8 * (lane >> 4);
 
-    f32x4_t acc[4] = {f32x4_t{}, f32x4_t{}, f32x4_t{}, f32x4_t{}};
-    for (int64_t s = s_beg; s < s_end; s += kSmallUnroll) {
-        bf16x8_t wf[kSmallUnroll];
-        bf16x8_t gf[kSmallUnroll][4];
+    f32x4_t acc[MB];
 #pragma unroll
-        for (int u = 0; u < kSmallUnroll; ++u) {
-            const int64_t n = (s + u) * 32 + sub;
-            const bool nok = (s + u) < s_end && n < N; // N % 8 == 0
-            wf[u] = (nok && kok) ? *reinterpret_cast<const bf16x8_t *>(wrow + (s + u) * 32)
-                                 : bf16x8_t{};
+    for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = f32x4_t{};
+    for (int64_t c0 = n_beg; c0 < n_end; c0 += kDxsChunk) {
+        constexpr int kGLoads = MB * 16 * 64 / 256; // 16-byte dY chunks per thread
+        u32x4_t gv[kGLoads];
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const int64_t m = mb * 16 + (lane & 15);
-                gf[u][mb] = (mb < mb_count && nok && m < M)
-                                ? *reinterpret_cast<const bf16x8_t *>(G + m * N + n)
-                                : bf16x8_t{};
+        for (int j = 0; j < kGLoads; ++j) {
+            const int e = 256 * j + threadIdx.x;
+            const int m = e >> 6, ch = e & 63;
+            const int64_t n = c0 + 8 * ch;
+            gv[j] = u32x4_t{0u, 0u, 0u, 0u};
+            if (m < M && n < n_end) // N % 8 == 0, split_len % 8 == 0
+                gv[j] = *reinterpret_cast<const u32x4_t *>(p.G + m * N + n);
+        }
+        bf16x8_t wf[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int64_t n = c0 + 32 * u + sub;
+            wf[u] = (kok && n < n_end) ? *reinterpret_cast<const bf16x8_t *>(p.W + krow * N + n) : bf16x8_t{};
+        }
+#pragma unroll
+        for (int j = 0; j < kGLoads; ++j) {
+            const int e = 256 * j + threadIdx.x;
+            const int m = e >> 6, ch = e & 63;
+            *reinterpret_cast<LDS u32x4_t *>(gs + m * 1024 + ((ch ^ (m & 15)) << 4)) = gv[j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int m = 16 * mb + (lane & 15), ch = 4 * u + (lane >> 4);
+                const bf16x8_t gf = *reinterpret_cast<const LDS bf16x8_t *>(gs + m * 1024 + ((ch ^ (m & 15)) << 4));
+                // lane l: dX[16mb + l%16][k0 + 16w + 4(l/16) .. +3]
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], gf, acc[mb], 0, 0, 0);
+            }
+        __syncthreads();
+    }
+    const int64_t k = k0 + 16 * w + 4 * (lane >> 4);
+    if (p.splits == 1) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int64_t m = 16 * mb + (lane & 15);
+            if (m < M && k < K) { // K % 8 == 0: k .. k+3 all in range
+                const u32x2_t pk = {pack_bf16x2(acc[mb][0], acc[mb][1]), pack_bf16x2(acc[mb][2], acc[mb][3])};
+                *reinterpret_cast<u32x2_t *>(p.dX + m * K + k) = pk;
             }
         }
-#pragma unroll
-        for (int u = 0; u < kSmallUnroll; ++u)
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-                if (mb < mb_count)
-                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], gf[u][mb], acc[mb], 0, 0, 0);
+        return;
     }
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-        red[w][mb][lane] = acc[mb];
-    __syncthreads();
-    // wave mb sums the partials of m-block mb; lane holds dX[m][k..k+3]
-    if (w < mb_count) {
-        f32x4_t s = red[0][w][lane];
-        for (int ww = 1; ww < kSmallWaves; ++ww)
-            s += red[ww][w][lane];
-        const int64_t m = w * 16 + (lane & 15);
-        const int64_t k = k0 + 4 * (lane >> 4);
-        if (m < M && k < K) { // K % 8 == 0: k..k+3 in range
-            u32x2_t pk = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
-            *reinterpret_cast<u32x2_t *>(dX + m * K + k) = pk;
-        }
+    for (int mb = 0; mb < MB; ++mb) {
+        const int64_t m = 16 * mb + (lane & 15);
+        if (m < M && k < K)
+            *reinterpret_cast<f32x4_t *>(p.part + ((int64_t)s * M + m) * K + k) = acc[mb];
     }
+}
+
+// dX = bf16(Σ_s part[s]) over the splits in order (splits <= kDxsMaxSplits)
+// for entries 4i .. 4i+3 (M*K % 8 == 0), all loads issued at once.  Run by the
+// first blocks of the dW kernel that follows the dX kernel on the stream (its
+// write stream hides the reads), or, without dW, by a kernel of its own.
+constexpr int kDxsMaxSplits = 16;
+__device__ __forceinline__ void dx_reduce_quad(const SmallParams &p, int64_t q) {
+    const int64_t MK = p.M * p.K;
+    const int64_t i = 4 * q;
+    if (i >= MK)
+        return;
+    f32x4_t v[kDxsMaxSplits];
+#pragma unroll
+    for (int t = 0; t < kDxsMaxSplits; ++t)
+        v[t] = t < p.splits ? *reinterpret_cast<const f32x4_t *>(p.part + t * MK + i) : f32x4_t{};
+    f32x4_t a = v[0];
+#pragma unroll
+    for (int t = 1; t < kDxsMaxSplits; ++t)
+        if (t < p.splits)
+            a += v[t];
+    const u32x2_t pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+    *reinterpret_cast<u32x2_t *>(p.dX + i) = pk;
+}
+
+__global__ __launch_bounds__(256) void k_dx_smallm_reduce(SmallParams p) {
+    dx_reduce_quad(p, (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+template <int MB>
+__global__ __launch_bounds__(256) void k_dx_smallm(SmallParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem_raw[dx_small_lds<MB>()];
+    dx_small_block<MB>(p, blockIdx.x, (LDS char *)smem_raw);
+}
+
+// dW blocks; with reduce_blocks > 0 the first reduce_blocks blocks also finish
+// the preceding dX launch's split reduction, 1024 entries each.
+template <int NS>
+__global__ __launch_bounds__(256) void k_dw_smallm(SmallParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem_raw[dw_small_lds<NS>()];
+    if ((int)blockIdx.x < p.reduce_blocks)
+        dx_reduce_quad(p, (int64_t)blockIdx.x * 256 + threadIdx.x);
+    dw_small_block<NS>(p, blockIdx.x, (LDS char *)smem_raw);
 }
 
 // ------------------------------------------------------------------------
@@ -927,6 +1116,7 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
         return launch_simt(a, need_dx, need_dw, s);
 
     const bool small_dx = need_dx && a.M <= kSmallMaxM && a.N > 0;
+    const bool small_dw = need_dw && a.M > 0 && a.M <= kSmallMaxM;
     MfmaParams p{};
     int nj = 0;
     TileJob jx{}, jw{};
@@ -947,7 +1137,7 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
             jx.rot = 32;
         have_x = true;
     }
-    if (need_dw) {
+    if (need_dw && !small_dw) {
         jw = make_tile_job(JOB_DW, a.X, a.dY, a.dW, a.K, a.N, a.M, a.K, a.N);
         have_w = true;
     }
@@ -975,11 +1165,73 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
         if (e != hipSuccess)
             return e;
     }
-    if (small_dx) {
-        hipLaunchKernelGGL(k_dx_smallm, dim3((unsigned)ceil_div(a.K, 16)), dim3(kSmallWaves * 64), 0, s,
-                           static_cast<const uint16_t *>(a.dY), static_cast<const uint16_t *>(a.W),
-                           static_cast<uint16_t *>(a.dX), a.M, a.K, a.N);
-        return hipGetLastError();
+    if (small_dx || small_dw) {
+        SmallParams sp{};
+        sp.X = static_cast<const uint16_t *>(a.X);
+        sp.W = static_cast<const uint16_t *>(a.W);
+        sp.G = static_cast<const uint16_t *>(a.dY);
+        sp.dX = small_dx ? static_cast<uint16_t *>(a.dX) : nullptr;
+        sp.dW = small_dw ? a.dW : nullptr;
+        sp.M = a.M;
+        sp.K = a.K;
+        sp.N = a.N;
+        sp.splits = 1;
+        int64_t reduce_quads = 0;
+        if (small_dx) {
+            // splits of the reduction: aim at ~512 blocks, each split a whole
+            // number of 512-element chunks, partials within the workspace
+            const int64_t groups = (a.K + kDxsBK - 1) / kDxsBK;
+            const int64_t chunks = (a.N + kDxsChunk - 1) / kDxsChunk;
+            int64_t splits = std::min(chunks, std::max<int64_t>(1, (512 + groups - 1) / groups));
+            splits = std::min<int64_t>(splits, kDxsMaxSplits);
+            if (a.dx_partial == nullptr)
+                splits = 1;
+            else
+                splits = std::min(splits, a.dx_partial_floats / (a.M * a.K));
+            splits = std::max<int64_t>(splits, 1);
+            const int64_t split_len = (chunks + splits - 1) / splits * kDxsChunk;
+            splits = (a.N + split_len - 1) / split_len;
+            sp.split_len = split_len;
+            sp.splits = (int)splits;
+            sp.part = a.dx_partial;
+            const int64_t blocks = groups * splits;
+            if (blocks > 0x7fffffff)
+                return hipErrorInvalidConfiguration;
+            if (a.M <= 16)
+                hipLaunchKernelGGL(k_dx_smallm<1>, dim3((unsigned)blocks), dim3(256), 0, s, sp);
+            else if (a.M <= 32)
+                hipLaunchKernelGGL(k_dx_smallm<2>, dim3((unsigned)blocks), dim3(256), 0, s, sp);
+            else
+                hipLaunchKernelGGL(k_dx_smallm<4>, dim3((unsigned)blocks), dim3(256), 0, s, sp);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+            if (splits > 1)
+                reduce_quads = a.M * a.K / 4;
+        }
+        const int64_t reduce_blocks = (reduce_quads + 255) / 256;
+        if (small_dw) {
+            sp.dw_tiles_n = ceil_div(a.N, kDwsBN);
+            const int64_t blocks = (int64_t)sp.dw_tiles_n * ceil_div(a.K, kDwsBK);
+            if (blocks > 0x7fffffff)
+                return hipErrorInvalidConfiguration;
+            if (reduce_blocks <= blocks) { // else the reduction gets its own launch below
+                sp.reduce_blocks = (int)reduce_blocks;
+                reduce_quads = 0;
+            }
+            if (a.M <= 32)
+                hipLaunchKernelGGL(k_dw_smallm<1>, dim3((unsigned)blocks), dim3(256), 0, s, sp);
+            else
+                hipLaunchKernelGGL(k_dw_smallm<2>, dim3((unsigned)blocks), dim3(256), 0, s, sp);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+        if (reduce_quads > 0) {
+            hipLaunchKernelGGL(k_dx_smallm_reduce, dim3((unsigned)reduce_blocks), dim3(256), 0, s, sp);
+            return hipGetLastError();
+        }
+        return hipSuccess;
     }
     return hipSuccess;
 }

@@ -70,6 +70,34 @@ def test_bf16_shapes_match_oracle(M, K, N):
     check_full(case, dX, dW)
 
 
+# The M <= 64 kernels: dW in 64x256 tiles with one or two 32-row reduction
+# slabs; dX over 64-column groups with the reduction split across blocks (fp32
+# partials summed in split order) in chunks of 512.  Shapes: M in each of the
+# 16/32/64-row variants and across the slab boundary, ragged k groups, n tiles
+# and chunks, several chunks per split (K = 4096, N = 8192: 8 splits of 1024),
+# and M*K above the 2^21-float partial workspace, which runs unsplit and stores
+# bf16 directly.
+SMALL_M_SHAPES = [
+    (1, 264, 1544), (16, 4104, 520), (17, 1032, 2056), (32, 640, 3080), (33, 200, 3080),
+    (48, 72, 264), (63, 520, 1032), (64, 8, 40), (32, 4096, 8192), (64, 33792, 64),
+]
+
+
+@pytest.mark.parametrize("M,K,N", SMALL_M_SHAPES)
+def test_small_m_shapes_match_oracle(M, K, N):
+    case = synth.linear_case(M, K, N, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=3 * M + K + N)
+    dX, dW = run(case)
+    check_full(case, dX, dW)
+
+
+def test_small_m_repeatable():
+    """The split reduction adds partials in a fixed order: two runs agree bit for bit."""
+    case = synth.linear_case(32, 4096, 4096, "bf16", seed=11)
+    a = [t.clone() for t in run(case)]
+    b = run(case)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
 # Reduction lengths around the 32-deep slab, the 64-deep dX slab pair (a
 # partial last pair when R % 64 != 0) and the padding of the slab count to a
 # multiple of four.
