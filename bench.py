@@ -200,8 +200,30 @@ def bench_block(steps, warmup, seed):
     return result, (cases, opt)
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def hold_queue(ms):
+    """Enqueue a sleep kernel of about `ms` milliseconds on the current stream, so that
+    the launches queued behind it while it runs start back to back on the GPU: HIP events
+    around them then bracket GPU time, not the host's per-call launch latency (a few tens
+    of microseconds through Python and ctypes, longer than an M = 32 call on the GPU)."""
+    import torch
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(1 << 20)
+        b.record()
+        _sync()
+        _SLEEP_CYCLES_PER_MS = (1 << 20) / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
+
+
 def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
-    """lin_bwd alone at one shape; rotates over buffer sets larger than the 256 MB MALL."""
+    """lin_bwd alone at one shape; rotates over buffer sets larger than the 256 MB MALL.
+    The timed calls are queued behind a sleep kernel (hold_queue), so each call's HIP
+    events measure the GPU's time for it."""
     import torch
 
     import linear_layer_backward_bwd_amd as lb
@@ -218,6 +240,8 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
         c, dX, dW = sets[i % nsets]
         lb.lin_bwd(c.X, c.W, c.G, dX, dW)
     timer = Timer(["lin_bwd"])
+    _sync()
+    hold_queue(steps * 0.1 + 2.0)
     for i in range(steps):
         c, dX, dW = sets[i % nsets]
         timer.run("lin_bwd", lambda: lb.lin_bwd(c.X, c.W, c.G, dX, dW))
@@ -230,7 +254,7 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
             "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "gbps_alg": round(q / (ms * 1e-3) / 1e9, 1),
             "intensity_pages": round(ideal_intensity(M, K, N), 2),
-            "rotating_sets": nsets}
+            "rotating_sets": nsets, "timing": "GPU time per call, calls queued behind a sleep kernel"}
 
 
 def bench_adamw(n, steps, warmup, seed):

@@ -192,6 +192,17 @@ __device__ __forceinline__ void lgkm_wait(Frags &a, Frags &b) {
                  : "memory");
 }
 
+// Wait for this wave's LDS reads of one W fragment and MB dY fragments.
+template <int MB>
+__device__ __forceinline__ void lgkm_wait_n(bf16x8_t &w, bf16x8_t (&g)[MB]) {
+    if constexpr (MB == 1)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w), "+v"(g[0])::"memory");
+    else if constexpr (MB == 2)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w), "+v"(g[0]), "+v"(g[1])::"memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w), "+v"(g[0]), "+v"(g[1]), "+v"(g[2]), "+v"(g[3])::"memory");
+}
+
 // Wait until at most `n` (a multiple of 8, <= 24) of this wave's DMA
 // instructions are still in flight (DMA completes in issue order).
 __device__ __forceinline__ void dma_wait(int n) {
@@ -839,74 +850,110 @@ __device__ __forceinline__ void dw_small_block(const SmallParams &p, int b, LDS 
 }
 
 // dX[m,k] = Σ_n dY[m,n]·W[k,n] with M <= 16*MB: bound by streaming W once.
-// Block (s, grp): dX columns k0 = 64grp .. +63 (wave w: 16 of them, the rows
-// of W it streams) over the reduction range of split s, in chunks of 512 n.
-// Per chunk every lane issues all 16 of its W loads (16 bytes each, one per
-// 32-deep MFMA step) before waiting, and the block stages dY[0:M, chunk] in
-// LDS once for its four waves (16-byte chunk c of row m at chunk c ^ (m % 16):
-// the 16 rows one fragment read serves sit on distinct banks).  With one split
-// the block stores dX in bf16.  With several, each block stores its fp32
-// partial sums part[s][m][k] and k_dx_smallm_reduce adds them in split order.
-// (A last-block-reduces variant, counting finished splits with a device-scope
-// atomic, needs a device-scope release and acquire per block; on this part
-// those write back and invalidate the XCD's L2, and dX took 5x longer.)
-constexpr int kDxsBK = 64;     // dX columns per block
-constexpr int kDxsChunk = 512; // reduction elements per chunk (16 MFMA steps)
+// Block (s, grp): dX columns k0 = 64grp .. +63 over the reduction range of
+// split s, in chunks of 256 n through a three-slot LDS ring (two slots for
+// M > 32, where three do not fit).  Wave w streams
+// rows k0+16w .. +15 of W: each of its DMA instructions fetches two rows x
+// 512 contiguous bytes (loading MFMA fragments straight from memory touches
+// 16 rows x 64 bytes per instruction, which the HBM served at 2.2 TB/s), and
+// the wave only ever reads its own rows back.  dY[0:M, chunk] is shared by
+// the four waves.  In both, 16-byte chunk c of a 512-byte LDS row r sits at
+// chunk c ^ (r % 16), so the 16 rows one fragment read serves hit distinct
+// banks.  Per chunk: wait for its DMA, barrier, DMA of the chunk two (one)
+// ahead into the slot freed by the barrier, 8 MFMA steps.  With one split the block
+// stores dX in bf16; with several it stores fp32 partial sums part[s][m][k]
+// that are added in split order afterwards.  (A last-block-reduces variant,
+// counting finished splits with a device-scope atomic, needs a device-scope
+// release and acquire per block; on this part those write back and
+// invalidate the XCD's L2, and dX took 5x longer.)
+constexpr int kDxsBK = 64;         // dX columns per block
+constexpr int kDxsChunk = 256;     // reduction elements per chunk (8 MFMA steps)
+constexpr int kDxsWSlot = 64 * 512; // W rows of a chunk: 64 x 512 B
 template <int MB>
-constexpr int dx_small_lds() { return MB * 16 * kDxsChunk * 2; }
+constexpr int dx_small_slot() { return kDxsWSlot + MB * 16 * 512; }
+template <int MB> // ring slots: three where they fit in LDS
+constexpr int dx_small_slots() { return 3 * dx_small_slot<MB>() <= 160 * 1024 ? 3 : 2; }
+template <int MB>
+constexpr int dx_small_lds() { return dx_small_slots<MB>() * dx_small_slot<MB>(); }
+
+// Wait until at most `c` chunks' DMA (kPerChunk instructions each) are in flight.
+template <int kPerChunk>
+__device__ __forceinline__ void dx_chunk_wait(int c) {
+    if (c >= 2)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPerChunk) : "memory");
+    else if (c == 1)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPerChunk) : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
 template <int MB>
-__device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS char *gs) {
+__device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS char *smem) {
+    constexpr int kSlot = dx_small_slot<MB>();
+    constexpr int kS = dx_small_slots<MB>();
+    constexpr int kGInst = MB * 2;         // dY DMA instructions per wave per chunk (2 rows each)
+    constexpr int kPerChunk = 8 + kGInst;  // DMA instructions per wave per chunk
+    static_assert((kS - 1) * kPerChunk <= 63, "the chunks in flight fit the vmcnt counter");
     const int64_t M = p.M, K = p.K, N = p.N;
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int s = b % p.splits, grp = b / p.splits;
     const int64_t k0 = (int64_t)grp * kDxsBK;
     const int64_t n_beg = (int64_t)s * p.split_len;
     const int64_t n_end = min(N, n_beg + p.split_len);
-    const int64_t krow = k0 + 16 * w + (lane & 15);
-    const bool kok = krow < K;
-    const int sub = 8 * (lane >> 4);
+    const int nc = (int)((n_end - n_beg + kDxsChunk - 1) / kDxsChunk);
+    // W rows from k0 on, and dY; offsets are 32-bit (2KN, 2MN < 2^31) and
+    // rows or columns out of range read zero through kOOB
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.W + k0 * N, (uint32_t)(2 * (K - k0) * N));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.G, (uint32_t)(2 * M * N));
+    auto issue = [&](int j) { // chunk j into slot j % kS
+        const int64_t c0 = n_beg + (int64_t)j * kDxsChunk;
+        LDS char *slot = smem + (j % kS) * kSlot;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 16 * w + 2 * i + (lane >> 5);
+            const int64_t n = c0 + 8 * ((lane & 31) ^ (r & 15));
+            const bool ok = k0 + r < K && n < n_end;
+            dma16(rw, slot + (16 * w + 2 * i) * 512, ok ? (uint32_t)(2 * (r * N + n)) : kOOB);
+        }
+#pragma unroll
+        for (int i = 0; i < kGInst; ++i) {
+            const int m = 2 * (w * kGInst + i) + (lane >> 5);
+            const int64_t n = c0 + 8 * ((lane & 31) ^ (m & 15));
+            const bool ok = m < M && n < n_end;
+            dma16(rg, slot + kDxsWSlot + 2 * (w * kGInst + i) * 512, ok ? (uint32_t)(2 * (m * N + n)) : kOOB);
+        }
+    };
 
     f32x4_t acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
         acc[mb] = f32x4_t{};
-    for (int64_t c0 = n_beg; c0 < n_end; c0 += kDxsChunk) {
-        constexpr int kGLoads = MB * 16 * 64 / 256; // 16-byte dY chunks per thread
-        u32x4_t gv[kGLoads];
+    const int sw = lane & 15; // row % 16 of every fragment row this lane reads
+    // chunk j: wait for its DMA, barrier (after which every wave is done with
+    // chunk j-1, so its slot takes chunk j + kS - 1), then its 8 MFMA steps
+    for (int i = 0; i < kS - 1 && i < nc; ++i)
+        issue(i);
+    for (int j = 0; j < nc; ++j) {
+        dx_chunk_wait<kPerChunk>(min(kS - 2, nc - 1 - j));
+        slab_barrier();
+        if (j + kS - 1 < nc)
+            issue(j + kS - 1);
+        const LDS char *slot = smem + (j % kS) * kSlot;
 #pragma unroll
-        for (int j = 0; j < kGLoads; ++j) {
-            const int e = 256 * j + threadIdx.x;
-            const int m = e >> 6, ch = e & 63;
-            const int64_t n = c0 + 8 * ch;
-            gv[j] = u32x4_t{0u, 0u, 0u, 0u};
-            if (m < M && n < n_end) // N % 8 == 0, split_len % 8 == 0
-                gv[j] = *reinterpret_cast<const u32x4_t *>(p.G + m * N + n);
+        for (int u = 0; u < kDxsChunk / 32; ++u) {
+            const int c = 4 * u + (lane >> 4);
+            bf16x8_t wf = read_rc<0>(slot + (16 * w + sw) * 512 + ((c ^ sw) << 4));
+            bf16x8_t gf[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                gf[mb] = read_rc<0>(slot + kDxsWSlot + (16 * mb + sw) * 512 + ((c ^ sw) << 4));
+            lgkm_wait_n<MB>(wf, gf);
+            // lane l: dX[16mb + l%16][k0 + 16w + 4(l/16) .. +3]
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, gf[mb], acc[mb], 0, 0, 0);
         }
-        bf16x8_t wf[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int64_t n = c0 + 32 * u + sub;
-            wf[u] = (kok && n < n_end) ? *reinterpret_cast<const bf16x8_t *>(p.W + krow * N + n) : bf16x8_t{};
-        }
-#pragma unroll
-        for (int j = 0; j < kGLoads; ++j) {
-            const int e = 256 * j + threadIdx.x;
-            const int m = e >> 6, ch = e & 63;
-            *reinterpret_cast<LDS u32x4_t *>(gs + m * 1024 + ((ch ^ (m & 15)) << 4)) = gv[j];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int m = 16 * mb + (lane & 15), ch = 4 * u + (lane >> 4);
-                const bf16x8_t gf = *reinterpret_cast<const LDS bf16x8_t *>(gs + m * 1024 + ((ch ^ (m & 15)) << 4));
-                // lane l: dX[16mb + l%16][k0 + 16w + 4(l/16) .. +3]
-                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], gf, acc[mb], 0, 0, 0);
-            }
-        __syncthreads();
     }
     const int64_t k = k0 + 16 * w + 4 * (lane >> 4);
     if (p.splits == 1) {
@@ -1178,11 +1225,12 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
         sp.splits = 1;
         int64_t reduce_quads = 0;
         if (small_dx) {
-            // splits of the reduction: aim at ~512 blocks, each split a whole
-            // number of 512-element chunks, partials within the workspace
+            // splits of the reduction: aim at ~256 blocks (one per CU; a block
+            // streams its chunks through its ring), each split a whole number of
+            // chunks, partials within the workspace
             const int64_t groups = (a.K + kDxsBK - 1) / kDxsBK;
             const int64_t chunks = (a.N + kDxsChunk - 1) / kDxsChunk;
-            int64_t splits = std::min(chunks, std::max<int64_t>(1, (512 + groups - 1) / groups));
+            int64_t splits = std::min(chunks, std::max<int64_t>(1, (256 + groups - 1) / groups));
             splits = std::min<int64_t>(splits, kDxsMaxSplits);
             if (a.dx_partial == nullptr)
                 splits = 1;
