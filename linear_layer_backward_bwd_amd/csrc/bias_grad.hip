@@ -28,11 +28,12 @@ constexpr int kUnroll = 8;          // rows of 16-byte loads in flight per threa
 constexpr int kFinalBatch = 16;     // independent partial loads per final-pass round
 constexpr int kTargetBlocks = 1024; // enough waves to keep HBM busy; 2048 was 5% slower (more partials)
 
+// dY is read once: non-temporal 16-byte loads.
 template <typename T> struct Elt;
 template <> struct Elt<uint16_t> { // bf16 bits
     static constexpr int kCols = 8;
     static __device__ __forceinline__ void load(const void *p, int64_t i, float (&x)[8]) {
-        const u32x4_t w = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(p) + i);
+        const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(p) + i));
         for (int e = 0; e < 4; ++e) {
             x[2 * e] = bf16_bits_to_f32(w[e] & 0xffffu);
             x[2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);
@@ -45,7 +46,7 @@ template <> struct Elt<uint16_t> { // bf16 bits
 template <> struct Elt<float> {
     static constexpr int kCols = 4;
     static __device__ __forceinline__ void load(const void *p, int64_t i, float (&x)[4]) {
-        const f32x4_t a = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(p) + i);
+        const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(static_cast<const float *>(p) + i));
         for (int e = 0; e < 4; ++e)
             x[e] = a[e];
     }

@@ -22,11 +22,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kVec = 8; // gradient elements per thread per iteration
 
+// The gradient is read once: non-temporal 16-byte loads.
 template <int GT> struct Load8;
 template <> struct Load8<GRAD_F32> {
     static __device__ __forceinline__ void load(const void *g, int64_t i, float (&x)[8]) {
-        const f32x4_t a = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(g) + i);
-        const f32x4_t b = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(g) + i + 4);
+        const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(static_cast<const float *>(g) + i));
+        const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(static_cast<const float *>(g) + i + 4));
         for (int e = 0; e < 4; ++e) {
             x[e] = a[e];
             x[4 + e] = b[e];
@@ -36,7 +37,7 @@ template <> struct Load8<GRAD_F32> {
 };
 template <> struct Load8<GRAD_F16> {
     static __device__ __forceinline__ void load(const void *g, int64_t i, float (&x)[8]) {
-        const u32x4_t w = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(g) + i);
+        const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(g) + i));
         for (int e = 0; e < 4; ++e) {
             x[2 * e] = f16_bits_to_f32((uint16_t)(w[e] & 0xffffu));
             x[2 * e + 1] = f16_bits_to_f32((uint16_t)(w[e] >> 16));
@@ -48,7 +49,7 @@ template <> struct Load8<GRAD_F16> {
 };
 template <> struct Load8<GRAD_BF16> {
     static __device__ __forceinline__ void load(const void *g, int64_t i, float (&x)[8]) {
-        const u32x4_t w = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(g) + i);
+        const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(g) + i));
         for (int e = 0; e < 4; ++e) {
             x[2 * e] = bf16_bits_to_f32(w[e] & 0xffffu);
             x[2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);

@@ -26,8 +26,10 @@ constexpr int kRowsPerBlock = kThreads / 64;
 template <typename T> struct V;
 template <> struct V<float> {
     static constexpr int kN = 4;
+    template <bool NT = false>
     static __device__ __forceinline__ void load(const void *p, int64_t i, float (&x)[4]) {
-        const f32x4_t a = *reinterpret_cast<const f32x4_t *>(static_cast<const float *>(p) + i);
+        const f32x4_t *q = reinterpret_cast<const f32x4_t *>(static_cast<const float *>(p) + i);
+        const f32x4_t a = NT ? __builtin_nontemporal_load(q) : *q;
         for (int e = 0; e < 4; ++e)
             x[e] = a[e];
     }
@@ -39,8 +41,10 @@ template <> struct V<float> {
 };
 template <> struct V<uint16_t> { // bf16 bits
     static constexpr int kN = 8;
+    template <bool NT = false>
     static __device__ __forceinline__ void load(const void *p, int64_t i, float (&x)[8]) {
-        const u32x4_t w = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(p) + i);
+        const u32x4_t *q = reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(p) + i);
+        const u32x4_t w = NT ? __builtin_nontemporal_load(q) : *q;
         for (int e = 0; e < 4; ++e) {
             x[2 * e] = bf16_bits_to_f32(w[e] & 0xffffu);
             x[2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);
@@ -86,8 +90,8 @@ __global__ __launch_bounds__(kThreads) void k_softmax_bwd_wave(const void *P, co
         const int64_t c0 = (int64_t)(v * 64 + lane) * kN;
         if (VEC) {
             if (c0 < cols) {
-                V<T>::load(P, base + c0, p[v]);
-                V<T>::load(dY, base + c0, g[v]);
+                V<T>::template load<true>(P, base + c0, p[v]); // read once: non-temporal
+                V<T>::template load<true>(dY, base + c0, g[v]);
             } else {
 #pragma unroll
                 for (int e = 0; e < kN; ++e)
