@@ -109,6 +109,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, LDS char *dst, uint32_t off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void *)dst, 16, (int)off, 0, 0, 0);
 }
+// The same for data read once: the non-temporal cache policy (aux bit 1).
+__device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t rs, LDS char *dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void *)dst, 16, (int)off, 0, 0, 2);
+}
 
 // Per-lane DMA source offsets of an OC slab, fixed for a tile.  Instruction p
 // of wave w fills LDS rows 2q, 2q+1 (r) of the slab, q = kDmaPerOp*w + p: lane
@@ -914,7 +918,7 @@ __device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS 
             const int r = 16 * w + 2 * i + (lane >> 5);
             const int64_t n = c0 + 8 * ((lane & 31) ^ (r & 15));
             const bool ok = k0 + r < K && n < n_end;
-            dma16(rw, slot + (16 * w + 2 * i) * 512, ok ? (uint32_t)(2 * (r * N + n)) : kOOB);
+            dma16_nt(rw, slot + (16 * w + 2 * i) * 512, ok ? (uint32_t)(2 * (r * N + n)) : kOOB);
         }
 #pragma unroll
         for (int i = 0; i < kGInst; ++i) {
