@@ -284,7 +284,7 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[kFrags][kFrags],
                 const u32x4_t v = *reinterpret_cast<const LDS u32x4_t *>(reg + r * 256 + ((k ^ (r & 15)) << 4));
                 const int64_t i = ib + 32 * h + r, j = jb0 + 8 * k;
                 if (i < jb.I && j < jb.J) // J % 8 == 0: j..j+7 all in range
-                    *reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(jb.c) + i * jb.J + j) = v;
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(jb.c) + i * jb.J + j));
             }
         }
     } else {
@@ -304,7 +304,7 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[kFrags][kFrags],
                 const f32x4_t v = *reinterpret_cast<const LDS f32x4_t *>(reg + r * 512 + ((k ^ r) << 4));
                 const int64_t i = ib + 16 * x + r, j = jb0 + 4 * k;
                 if (i < jb.I && j < jb.J)
-                    *reinterpret_cast<f32x4_t *>(static_cast<float *>(jb.c) + i * jb.J + j) = v;
+                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t *>(static_cast<float *>(jb.c) + i * jb.J + j));
             }
         }
     }
@@ -848,7 +848,7 @@ __device__ __forceinline__ void dw_small_block(const SmallParams &p, int b, LDS 
             const f32x4_t v = *reinterpret_cast<const LDS f32x4_t *>(stage + r * 256 + ((c ^ r) << 4));
             const int64_t k = k0 + 16 * w + r, n = n0 + 64 * q + 4 * c;
             if (k < K && n < N) // N % 8 == 0: n .. n+3 all in range
-                *reinterpret_cast<f32x4_t *>(p.dW + k * N + n) = v;
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t *>(p.dW + k * N + n));
         }
     }
 }
