@@ -58,6 +58,7 @@ def _sync():
 
 
 KERNEL_SOURCES = {"k_lin_bwd_mfma": "linear_layer_backward_bwd_amd/csrc/lin_bwd.hip",
+                  "k_dw_smallm": "linear_layer_backward_bwd_amd/csrc/lin_bwd.hip",
                   "k_adamw": "linear_layer_backward_bwd_amd/csrc/adamw.hip",
                   "k_norm_partial": "linear_layer_backward_bwd_amd/csrc/grad_norm.hip",
                   "k_bias_partial": "linear_layer_backward_bwd_amd/csrc/bias_grad.hip",
@@ -254,7 +255,8 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
             "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "gbps_alg": round(q / (ms * 1e-3) / 1e9, 1),
             "intensity_pages": round(ideal_intensity(M, K, N), 2),
-            "rotating_sets": nsets, "timing": "GPU time per call, calls queued behind a sleep kernel"}
+            "rotating_sets": nsets, "timing": "GPU time per call, calls queued behind a sleep kernel",
+            "traffic": recorded_traffic("k_dw_smallm", "lin_bwd_M%d_K%d_N%d" % (M, K, N)) if M <= 64 else None}
 
 
 def bench_adamw(n, steps, warmup, seed):
