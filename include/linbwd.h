@@ -62,8 +62,8 @@ extern "C" {
  * with zeros; with N = 0 dX is filled with zeros; K = 0 writes nothing.
  * Any pointer alignment and any sizes are accepted; 16-byte aligned pointers
  * with K and N multiples of 8 take the vectorised kernels.
- * For bf16 with 1 <= M <= 64 (decode-like), dX sums over n in several blocks
- * whose fp32 partial sums go to the library-owned workspace (about 12.2 MiB
+ * For bf16 with 1 <= M <= 256 (decode-like), dX sums over n in several blocks
+ * whose fp32 partial sums go to the library-owned workspace (about 36.2 MiB
  * per device, allocated on first use, kept until the process ends) and are
  * added in a fixed order (results repeat bit for bit); such calls that
  * overlap on one device race.
@@ -87,7 +87,7 @@ int lin_bwd(const void *X, const void *W, const void *dY, void *dX, float *dW,
  * fp32 per row range and the partials in fp64, in a fixed order (results
  * repeat bit for bit); M = 0 fills db with zeros.  X and W may be NULL when
  * only db is requested.  Additional error: LB_EINVAL for a NULL dY with db
- * requested and M, N > 0.  Uses the library-owned workspace (about 12.2 MiB
+ * requested and M, N > 0.  Uses the library-owned workspace (about 36.2 MiB
  * per device, allocated on first use, kept until the process ends); calls that
  * request db and overlap on one device race.
  */
@@ -181,7 +181,7 @@ int adamw_step_ex(float *W, const void *grad, int grad_dtype, float *m, float *v
  *
  * The summation order is fixed for a given n and 16-byte alignment of grad
  * (the result is reproducible).
- * Uses the library-owned workspace (about 12.2 MiB per device, allocated on
+ * Uses the library-owned workspace (about 36.2 MiB per device, allocated on
  * first use, kept until the process ends); calls that overlap on one device race.
  * Asynchronous on the thread's stream.  Errors: LB_EDTYPE for another
  * grad_dtype; LB_EINVAL for n < 0, NULL d_out, or NULL grad with n > 0;

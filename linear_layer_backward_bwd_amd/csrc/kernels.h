@@ -50,13 +50,13 @@ struct LinBwdArgs {
     float *dW; // may be null (skip)
     int64_t M, K, N;
     bool bf16; // operands bf16 (else fp32)
-    // workspace for the split reduction of the M <= 64 dX path (fp32 partials),
+    // workspace for the split reduction of the small-M dX path (fp32 partials),
     // or null: then that path runs unsplit
     float *dx_partial;
     int64_t dx_partial_floats;
 };
 
-constexpr int64_t kDxPartialFloats = 1 << 21; // 8 MiB of dX partials
+constexpr int64_t kDxPartialFloats = 1 << 23; // 32 MiB of dX partials
 
 
 // Chooses kernels by dtype, alignment and M; enqueues 1-2 launches.

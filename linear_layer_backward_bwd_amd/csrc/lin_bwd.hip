@@ -734,7 +734,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
 // merged kernel's lower occupancy, and at N = 16384 the mixed read and write
 // streams made it 40% slower than the two launches in turn.)
 // ------------------------------------------------------------------------
-constexpr int kSmallMaxM = 64;
+constexpr int kSmallMaxM = 64;    // dW: the small-tile kernel up to this M
+constexpr int kSmallMaxDxM = 256; // dX: the split-reduction kernel up to this M
 
 struct SmallParams {
     const uint16_t *X, *W, *G; // X[M,K], W[K,N], dY[M,N]
@@ -853,28 +854,30 @@ __device__ __forceinline__ void dw_small_block(const SmallParams &p, int b, LDS 
     }
 }
 
-// dX[m,k] = Σ_n dY[m,n]·W[k,n] with M <= 16*MB: bound by streaming W once.
-// Block (s, grp): dX columns k0 = 64grp .. +63 over the reduction range of
-// split s, in chunks of 256 n through a three-slot LDS ring (two slots for
-// M > 32, where three do not fit).  Wave w streams
-// rows k0+16w .. +15 of W: each of its DMA instructions fetches two rows x
-// 512 contiguous bytes (loading MFMA fragments straight from memory touches
-// 16 rows x 64 bytes per instruction, which the HBM served at 2.2 TB/s), and
+// dX[m,k] = Σ_n dY[m,n]·W[k,n] with M <= 16*MB, for small M (up to 256): the
+// tile kernel would give it only K/256 tiles.  Bound by streaming W once at
+// M <= 64, by both W and the MFMAs near 256.  Block (s, grp): dX columns
+// k0 = 64grp .. +63 over the reduction range of split s, in chunks of CH n
+// through an LDS ring of three slots where they fit (two otherwise).  Wave w
+// streams rows k0+16w .. +15 of W: each DMA instruction fetches 1 KiB of
+// whole rows (two rows x 512 bytes at CH = 256, four x 256 at CH = 128) with
+// the non-temporal policy (W is read once; loading MFMA fragments straight
+// from memory touches 16 rows x 64 bytes per instruction and was slower), and
 // the wave only ever reads its own rows back.  dY[0:M, chunk] is shared by
-// the four waves.  In both, 16-byte chunk c of a 512-byte LDS row r sits at
-// chunk c ^ (r % 16), so the 16 rows one fragment read serves hit distinct
-// banks.  Per chunk: wait for its DMA, barrier, DMA of the chunk two (one)
-// ahead into the slot freed by the barrier, 8 MFMA steps.  With one split the block
-// stores dX in bf16; with several it stores fp32 partial sums part[s][m][k]
-// that are added in split order afterwards.  (A last-block-reduces variant,
-// counting finished splits with a device-scope atomic, needs a device-scope
-// release and acquire per block; on this part those write back and
-// invalidate the XCD's L2, and dX took 5x longer.)
-constexpr int kDxsBK = 64;         // dX columns per block
-constexpr int kDxsChunk = 256;     // reduction elements per chunk (8 MFMA steps)
-constexpr int kDxsWSlot = 64 * 512; // W rows of a chunk: 64 x 512 B
+// the four waves.  In both, 16-byte chunk c of an LDS row r sits at chunk
+// c ^ (r % 16), so the 16 rows one fragment read serves hit distinct banks.
+// Per chunk: wait for its DMA, barrier, DMA of the chunk kS-1 ahead into the
+// slot the barrier freed, CH/32 MFMA steps.  With one split the block stores
+// dX in bf16; with several it stores fp32 partial sums part[s][m][k] that are
+// added in split order afterwards.  (A last-block-reduces variant, counting
+// finished splits with a device-scope atomic, needs a device-scope release
+// and acquire per block; on this part those write back and invalidate the
+// XCD's L2, and dX took 5x longer.)
+constexpr int kDxsBK = 64; // dX columns per block
+template <int MB> // reduction elements per chunk: dY's slot stays within LDS
+constexpr int dx_small_chunk() { return MB <= 4 ? 256 : 128; }
 template <int MB>
-constexpr int dx_small_slot() { return kDxsWSlot + MB * 16 * 512; }
+constexpr int dx_small_slot() { return (64 + MB * 16) * dx_small_chunk<MB>() * 2; }
 template <int MB> // ring slots: three where they fit in LDS
 constexpr int dx_small_slots() { return 3 * dx_small_slot<MB>() <= 160 * 1024 ? 3 : 2; }
 template <int MB>
@@ -893,10 +896,17 @@ __device__ __forceinline__ void dx_chunk_wait(int c) {
 
 template <int MB>
 __device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS char *smem) {
+    constexpr int kCH = dx_small_chunk<MB>();
+    constexpr int kRow = 2 * kCH;                // bytes per LDS row
+    constexpr int kCPR = kRow / 16;              // 16-byte chunks per row
+    constexpr int kRPI = 1024 / kRow;            // rows per DMA instruction
+    constexpr int kWSlot = 64 * kRow;            // W part of a slot
     constexpr int kSlot = dx_small_slot<MB>();
     constexpr int kS = dx_small_slots<MB>();
-    constexpr int kGInst = MB * 2;         // dY DMA instructions per wave per chunk (2 rows each)
-    constexpr int kPerChunk = 8 + kGInst;  // DMA instructions per wave per chunk
+    constexpr int kWInst = 16 / kRPI;            // W DMA instructions per wave per chunk
+    constexpr int kGInst = MB * 16 / kRPI / 4;   // dY DMA instructions per wave per chunk
+    constexpr int kPerChunk = kWInst + kGInst;
+    static_assert(kCPR >= 16, "the XOR swizzle spans 16 chunks");
     static_assert((kS - 1) * kPerChunk <= 63, "the chunks in flight fit the vmcnt counter");
     const int64_t M = p.M, K = p.K, N = p.N;
     const int lane = threadIdx.x & 63;
@@ -905,27 +915,29 @@ __device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS 
     const int64_t k0 = (int64_t)grp * kDxsBK;
     const int64_t n_beg = (int64_t)s * p.split_len;
     const int64_t n_end = min(N, n_beg + p.split_len);
-    const int nc = (int)((n_end - n_beg + kDxsChunk - 1) / kDxsChunk);
+    const int nc = (int)((n_end - n_beg + kCH - 1) / kCH);
     // W rows from k0 on, and dY; offsets are 32-bit (2KN, 2MN < 2^31) and
     // rows or columns out of range read zero through kOOB
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.W + k0 * N, (uint32_t)(2 * (K - k0) * N));
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.G, (uint32_t)(2 * M * N));
+    const int lrow = lane / kCPR, lchunk = lane % kCPR; // this lane's row and chunk within an instruction
     auto issue = [&](int j) { // chunk j into slot j % kS
-        const int64_t c0 = n_beg + (int64_t)j * kDxsChunk;
+        const int64_t c0 = n_beg + (int64_t)j * kCH;
         LDS char *slot = smem + (j % kS) * kSlot;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 16 * w + 2 * i + (lane >> 5);
-            const int64_t n = c0 + 8 * ((lane & 31) ^ (r & 15));
+        for (int i = 0; i < kWInst; ++i) {
+            const int r = 16 * w + kRPI * i + lrow;
+            const int64_t n = c0 + 8 * (lchunk ^ (r & 15));
             const bool ok = k0 + r < K && n < n_end;
-            dma16_nt(rw, slot + (16 * w + 2 * i) * 512, ok ? (uint32_t)(2 * (r * N + n)) : kOOB);
+            dma16_nt(rw, slot + (16 * w + kRPI * i) * kRow, ok ? (uint32_t)(2 * (r * N + n)) : kOOB);
         }
 #pragma unroll
         for (int i = 0; i < kGInst; ++i) {
-            const int m = 2 * (w * kGInst + i) + (lane >> 5);
-            const int64_t n = c0 + 8 * ((lane & 31) ^ (m & 15));
+            const int m0 = kRPI * (w * kGInst + i);
+            const int m = m0 + lrow;
+            const int64_t n = c0 + 8 * (lchunk ^ (m & 15));
             const bool ok = m < M && n < n_end;
-            dma16(rg, slot + kDxsWSlot + 2 * (w * kGInst + i) * 512, ok ? (uint32_t)(2 * (m * N + n)) : kOOB);
+            dma16(rg, slot + kWSlot + m0 * kRow, ok ? (uint32_t)(2 * (m * N + n)) : kOOB);
         }
     };
 
@@ -935,7 +947,7 @@ __device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS 
         acc[mb] = f32x4_t{};
     const int sw = lane & 15; // row % 16 of every fragment row this lane reads
     // chunk j: wait for its DMA, barrier (after which every wave is done with
-    // chunk j-1, so its slot takes chunk j + kS - 1), then its 8 MFMA steps
+    // chunk j-1, so its slot takes chunk j + kS - 1), then its MFMA steps
     for (int i = 0; i < kS - 1 && i < nc; ++i)
         issue(i);
     for (int j = 0; j < nc; ++j) {
@@ -945,18 +957,22 @@ __device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS 
             issue(j + kS - 1);
         const LDS char *slot = smem + (j % kS) * kSlot;
 #pragma unroll
-        for (int u = 0; u < kDxsChunk / 32; ++u) {
+        for (int u = 0; u < kCH / 32; ++u) {
             const int c = 4 * u + (lane >> 4);
-            bf16x8_t wf = read_rc<0>(slot + (16 * w + sw) * 512 + ((c ^ sw) << 4));
-            bf16x8_t gf[MB];
+            bf16x8_t wf = read_rc<0>(slot + (16 * w + sw) * kRow + ((c ^ sw) << 4));
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                gf[mb] = read_rc<0>(slot + kDxsWSlot + (16 * mb + sw) * 512 + ((c ^ sw) << 4));
-            lgkm_wait_n<MB>(wf, gf);
-            // lane l: dX[16mb + l%16][k0 + 16w + 4(l/16) .. +3]
+            for (int m4 = 0; m4 < MB; m4 += 4) { // dY fragments four at a time
+                constexpr int kG = MB < 4 ? MB : 4;
+                bf16x8_t gf[kG];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, gf[mb], acc[mb], 0, 0, 0);
+                for (int q = 0; q < kG; ++q)
+                    gf[q] = read_rc<0>(slot + kWSlot + (16 * (m4 + q) + sw) * kRow + ((c ^ sw) << 4));
+                lgkm_wait_n<kG>(wf, gf);
+                // lane l: dX[16mb + l%16][k0 + 16w + 4(l/16) .. +3]
+#pragma unroll
+                for (int q = 0; q < kG; ++q)
+                    acc[m4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, gf[q], acc[m4 + q], 0, 0, 0);
+            }
         }
     }
     const int64_t k = k0 + 16 * w + 4 * (lane >> 4);
@@ -1166,7 +1182,7 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
     if (2 * a.M * a.K >= lim || 2 * a.K * a.N >= lim || 2 * a.M * a.N >= lim)
         return launch_simt(a, need_dx, need_dw, s);
 
-    const bool small_dx = need_dx && a.M <= kSmallMaxM && a.N > 0;
+    const bool small_dx = need_dx && a.M <= kSmallMaxDxM && a.N > 0;
     const bool small_dw = need_dw && a.M > 0 && a.M <= kSmallMaxM;
     MfmaParams p{};
     int nj = 0;
@@ -1231,9 +1247,11 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
         if (small_dx) {
             // splits of the reduction: aim at ~256 blocks (one per CU; a block
             // streams its chunks through its ring), each split a whole number of
-            // chunks, partials within the workspace
+            // chunks, at most kDxsMaxSplits, partials within the workspace
+            const int mb = a.M <= 16 ? 1 : a.M <= 32 ? 2 : a.M <= 64 ? 4 : a.M <= 128 ? 8 : 16;
+            const int64_t chunk = mb <= 4 ? dx_small_chunk<4>() : dx_small_chunk<8>();
             const int64_t groups = (a.K + kDxsBK - 1) / kDxsBK;
-            const int64_t chunks = (a.N + kDxsChunk - 1) / kDxsChunk;
+            const int64_t chunks = (a.N + chunk - 1) / chunk;
             int64_t splits = std::min(chunks, std::max<int64_t>(1, (256 + groups - 1) / groups));
             splits = std::min<int64_t>(splits, kDxsMaxSplits);
             if (a.dx_partial == nullptr)
@@ -1241,7 +1259,7 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
             else
                 splits = std::min(splits, a.dx_partial_floats / (a.M * a.K));
             splits = std::max<int64_t>(splits, 1);
-            const int64_t split_len = (chunks + splits - 1) / splits * kDxsChunk;
+            const int64_t split_len = (chunks + splits - 1) / splits * chunk;
             splits = (a.N + split_len - 1) / split_len;
             sp.split_len = split_len;
             sp.splits = (int)splits;
@@ -1249,12 +1267,14 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
             const int64_t blocks = groups * splits;
             if (blocks > 0x7fffffff)
                 return hipErrorInvalidConfiguration;
-            if (a.M <= 16)
-                hipLaunchKernelGGL(k_dx_smallm<1>, dim3((unsigned)blocks), dim3(256), 0, s, sp);
-            else if (a.M <= 32)
-                hipLaunchKernelGGL(k_dx_smallm<2>, dim3((unsigned)blocks), dim3(256), 0, s, sp);
-            else
-                hipLaunchKernelGGL(k_dx_smallm<4>, dim3((unsigned)blocks), dim3(256), 0, s, sp);
+            const dim3 grid((unsigned)blocks);
+            switch (mb) {
+            case 1: hipLaunchKernelGGL(k_dx_smallm<1>, grid, dim3(256), 0, s, sp); break;
+            case 2: hipLaunchKernelGGL(k_dx_smallm<2>, grid, dim3(256), 0, s, sp); break;
+            case 4: hipLaunchKernelGGL(k_dx_smallm<4>, grid, dim3(256), 0, s, sp); break;
+            case 8: hipLaunchKernelGGL(k_dx_smallm<8>, grid, dim3(256), 0, s, sp); break;
+            default: hipLaunchKernelGGL(k_dx_smallm<16>, grid, dim3(256), 0, s, sp); break;
+            }
             hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return e;

@@ -70,16 +70,19 @@ def test_bf16_shapes_match_oracle(M, K, N):
     check_full(case, dX, dW)
 
 
-# The M <= 64 kernels: dW in 64x256 tiles with one or two 32-row reduction
-# slabs; dX over 64-column groups with the reduction split across blocks (fp32
-# partials summed in split order) in chunks of 512.  Shapes: M in each of the
-# 16/32/64-row variants and across the slab boundary, ragged k groups, n tiles
-# and chunks, several chunks per split (K = 4096, N = 8192: 8 splits of 1024),
-# and M*K above the 2^21-float partial workspace, which runs unsplit and stores
-# bf16 directly.
+# The small-M kernels: dW (M <= 64) in 64x256 tiles with one or two 32-row
+# reduction slabs; dX (M <= 256) over 64-column groups with the reduction split
+# across blocks (fp32 partials summed in split order) in chunks of 256 (M <= 64)
+# or 128.  Shapes: M in each of the 16/32/64/128/256-row variants and across
+# their boundaries, ragged k groups, n tiles and chunks, several chunks per
+# split (K = 4096, N = 8192), M*K above the 2^23-float partial workspace (runs
+# unsplit and stores bf16 directly), and M > 64, where dW takes the tile kernel
+# and the partials are summed by a launch of their own.
 SMALL_M_SHAPES = [
     (1, 264, 1544), (16, 4104, 520), (17, 1032, 2056), (32, 640, 3080), (33, 200, 3080),
     (48, 72, 264), (63, 520, 1032), (64, 8, 40), (32, 4096, 8192), (64, 33792, 64),
+    (65, 264, 1032), (128, 520, 2056), (129, 1032, 392), (200, 4104, 520), (256, 1032, 3080),
+    (256, 33792, 8),
 ]
 
 
