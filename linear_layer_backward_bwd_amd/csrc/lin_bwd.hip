@@ -735,7 +735,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
 // streams made it 40% slower than the two launches in turn.)
 // ------------------------------------------------------------------------
 constexpr int kSmallMaxM = 64;    // dW: the small-tile kernel up to this M
-constexpr int kSmallMaxDxM = 256; // dX: the split-reduction kernel up to this M
+constexpr int kSmallMaxDxM = 512; // dX: the split-reduction kernel up to this M (row groups above 256)
 
 struct SmallParams {
     const uint16_t *X, *W, *G; // X[M,K], W[K,N], dY[M,N]
@@ -744,7 +744,9 @@ struct SmallParams {
     float *part;               // split partials [splits][M][K] (splits > 1)
     int64_t M, K, N;
     int64_t split_len;         // reduction elements per dX split (a multiple of 512)
-    int splits;                // dX splits per column group; dX block b = (split, group) (b % splits, b / splits)
+    int splits;                // dX splits per column group
+    int mgroups;               // dX row groups of 16*MB rows; block b = ((group, row group), split):
+                               // split b % splits, row group (b / splits) % mgroups, group b / splits / mgroups
     int dw_tiles_n;            // dW block b = (n tile, k tile) (b % dw_tiles_n, b / dw_tiles_n)
     int reduce_blocks;         // dW blocks that also add up dX partials
 };
@@ -911,15 +913,16 @@ __device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS 
     const int64_t M = p.M, K = p.K, N = p.N;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int s = b % p.splits, grp = b / p.splits;
+    const int s = b % p.splits, mg = (b / p.splits) % p.mgroups, grp = b / p.splits / p.mgroups;
     const int64_t k0 = (int64_t)grp * kDxsBK;
+    const int64_t m0 = (int64_t)mg * 16 * MB; // this block's rows of dY and dX
     const int64_t n_beg = (int64_t)s * p.split_len;
     const int64_t n_end = min(N, n_beg + p.split_len);
     const int nc = (int)((n_end - n_beg + kCH - 1) / kCH);
     // W rows from k0 on, and dY; offsets are 32-bit (2KN, 2MN < 2^31) and
     // rows or columns out of range read zero through kOOB
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.W + k0 * N, (uint32_t)(2 * (K - k0) * N));
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.G, (uint32_t)(2 * M * N));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.G + m0 * N, (uint32_t)(2 * (M - m0) * N));
     const int lrow = lane / kCPR, lchunk = lane % kCPR; // this lane's row and chunk within an instruction
     auto issue = [&](int j) { // chunk j into slot j % kS
         const int64_t c0 = n_beg + (int64_t)j * kCH;
@@ -933,11 +936,11 @@ __device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS 
         }
 #pragma unroll
         for (int i = 0; i < kGInst; ++i) {
-            const int m0 = kRPI * (w * kGInst + i);
-            const int m = m0 + lrow;
+            const int mr = kRPI * (w * kGInst + i);
+            const int m = mr + lrow;
             const int64_t n = c0 + 8 * (lchunk ^ (m & 15));
-            const bool ok = m < M && n < n_end;
-            dma16(rg, slot + kWSlot + m0 * kRow, ok ? (uint32_t)(2 * (m * N + n)) : kOOB);
+            const bool ok = m0 + m < M && n < n_end;
+            dma16(rg, slot + kWSlot + mr * kRow, ok ? (uint32_t)(2 * (m * N + n)) : kOOB);
         }
     };
 
@@ -979,7 +982,7 @@ __device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS 
     if (p.splits == 1) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const int64_t m = 16 * mb + (lane & 15);
+            const int64_t m = m0 + 16 * mb + (lane & 15);
             if (m < M && k < K) { // K % 8 == 0: k .. k+3 all in range
                 const u32x2_t pk = {pack_bf16x2(acc[mb][0], acc[mb][1]), pack_bf16x2(acc[mb][2], acc[mb][3])};
                 *reinterpret_cast<u32x2_t *>(p.dX + m * K + k) = pk;
@@ -989,7 +992,7 @@ __device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS 
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        const int64_t m = 16 * mb + (lane & 15);
+        const int64_t m = m0 + 16 * mb + (lane & 15);
         if (m < M && k < K)
             *reinterpret_cast<f32x4_t *>(p.part + ((int64_t)s * M + m) * K + k) = acc[mb];
     }
@@ -1249,10 +1252,11 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
             // streams its chunks through its ring), each split a whole number of
             // chunks, at most kDxsMaxSplits, partials within the workspace
             const int mb = a.M <= 16 ? 1 : a.M <= 32 ? 2 : a.M <= 64 ? 4 : a.M <= 128 ? 8 : 16;
+            sp.mgroups = (int)((a.M + 16 * mb - 1) / (16 * mb)); // above 256 rows: groups of 256
             const int64_t chunk = mb <= 4 ? dx_small_chunk<4>() : dx_small_chunk<8>();
             const int64_t groups = (a.K + kDxsBK - 1) / kDxsBK;
             const int64_t chunks = (a.N + chunk - 1) / chunk;
-            int64_t splits = std::min(chunks, std::max<int64_t>(1, (256 + groups - 1) / groups));
+            int64_t splits = std::min(chunks, std::max<int64_t>(1, (256 + groups * sp.mgroups - 1) / (groups * sp.mgroups)));
             splits = std::min<int64_t>(splits, kDxsMaxSplits);
             if (a.dx_partial == nullptr)
                 splits = 1;
@@ -1264,7 +1268,7 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
             sp.split_len = split_len;
             sp.splits = (int)splits;
             sp.part = a.dx_partial;
-            const int64_t blocks = groups * splits;
+            const int64_t blocks = groups * sp.mgroups * splits;
             if (blocks > 0x7fffffff)
                 return hipErrorInvalidConfiguration;
             const dim3 grid((unsigned)blocks);
