@@ -94,12 +94,44 @@ def test_small_m_shapes_match_oracle(M, K, N):
     check_full(case, dX, dW)
 
 
-def test_small_m_repeatable():
-    """The split reduction adds partials in a fixed order: two runs agree bit for bit."""
-    case = synth.linear_case(32, 4096, 4096, "bf16", seed=11)
+@pytest.mark.parametrize("M", [32, 384])
+def test_small_m_repeatable(M):
+    """The split reduction adds partials in a fixed order: two runs agree bit for bit
+    (M = 384 also has two row groups)."""
+    case = synth.linear_case(M, 4096, 4096, "bf16", seed=11)
     a = [t.clone() for t in run(case)]
     b = run(case)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("M,K,N", [(24, 520, 2056), (200, 264, 3080)])
+def test_small_m_one_output_at_a_time(M, K, N):
+    """dX alone (its split partials then get a summing launch of their own) and dW alone."""
+    case = synth.linear_case(M, K, N, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=M + 5)
+    dX, _ = run(case, need_dw=False)
+    check_full(case, dX, None)
+    _, dW = run(case, need_dx=False)
+    check_full(case, None, dW)
+
+
+@pytest.mark.parametrize("M,K,N", [(40, 264, 2056), (200, 520, 1032), (384, 136, 1544)])
+def test_small_m_integer_inputs_are_exact(M, K, N):
+    """Values in {-2..2}: every partial and their sum are exact in fp32, so dW is bitwise and
+    dX = RNE(exact) whatever the split (small-M dW, tile-kernel dW, row groups)."""
+    rng = np.random.default_rng(M + 1)
+    mk = lambda *sh: torch.tensor(rng.integers(-2, 3, size=sh), dtype=torch.float32).to(torch.bfloat16)
+    case = synth.LinearCase(M, K, N, "bf16", mk(M, K), mk(K, N), mk(M, N))
+    dX, dW = run(case)
+    rX, rW = oracle.lin_bwd(synth.bits(case.X), synth.bits(case.W), synth.bits(case.G), "bf16")
+    assert np.array_equal(dW.cpu().numpy(), rW.astype(np.float32))
+    assert torch.equal(dX.cpu(), torch.from_numpy(rX.astype(np.float32)).to(torch.bfloat16))
+
+
+def test_small_m_non_default_stream():
+    case = synth.linear_case(48, 1032, 2056, "bf16", seed=12)
+    s = torch.cuda.Stream()
+    dX, dW = run(case, stream=s)
+    check_full(case, dX, dW)
 
 
 # Reduction lengths around the 32-deep slab, the 64-deep dX slab pair (a
