@@ -66,16 +66,28 @@ KERNEL_SOURCES = {"k_lin_bwd_mfma": "linear_layer_backward_bwd_amd/csrc/lin_bwd.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def source_hash(kernel):
+def code_hash(text):
+    """sha256 (16 hex digits) of C/HIP source with its comments and whitespace removed, so
+    that a record stays valid across edits of comments only (the kernels' source has no
+    string literal holding a comment marker)."""
     import hashlib
-    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    code = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    code = re.sub(r"//[^\n]*", " ", code)
+    code = re.sub(r"\s+", " ", code).strip()
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
+def source_hash(kernel):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), encoding="utf-8") as f:
+        return code_hash(f.read())
 
 
 def recorded_traffic(kernel, workload):
     """HBM bytes per launch measured by rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a copy
     kernel of known size), as recorded in profiles/traffic.json -- or None when there is no
-    record for this kernel and workload or the kernel's source changed since it was taken."""
+    record for this kernel and workload or the kernel's code (comments aside) changed since
+    it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)[kernel][workload]

@@ -22,10 +22,11 @@
 //                    One launch runs the tiles of both products; blocks are ordered
 //                    longest reduction first and mapped so that each XCD works on a
 //                    compact group of tiles.
-//   k_dx_smallm      dX for M <= 64 (decode-like): streams W once, the reduction
-//                    over n split across blocks; the fp32 partials are added in
-//                    split order by the first blocks of k_dw_smallm (or by
-//                    k_dx_smallm_reduce when dW is not requested).
+//   k_dx_smallm      dX for M <= 512 (decode-like and small batches): streams W
+//                    once per 256-row group, the reduction over n split across
+//                    blocks; the fp32 partials are added in split order by the
+//                    first blocks of k_dw_smallm (M <= 64), else by
+//                    k_dx_smallm_reduce.
 //   k_dw_smallm      dW for M <= 64: bound by writing the fp32 output; small tiles,
 //                    several per CU, so stores overlap other tiles' loads.
 //   k_lin_bwd_simt   any dtype / alignment / shape: fp32 path and ragged bf16 shapes.
@@ -727,9 +728,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
 }
 
 // ------------------------------------------------------------------------
-// small M (M <= 64, decode-like): both products are bound by HBM, not MFMA:
-// dX streams W (2KN bytes), dW writes the fp32 output (4KN bytes).  They run
-// as two launches.  (One launch holding the blocks of both was slower where it
+// small M: at M <= 64 both products are bound by HBM, not MFMA: dX streams W
+// (2KN bytes), dW writes the fp32 output (4KN bytes).  Up to M = 512 the tile
+// kernel would give dX only (M/256)(K/256) tiles, so dX keeps the
+// split-reduction kernel (dW returns to the tile kernel above M = 64).  They
+// run as two launches.  (One launch holding the blocks of both was slower where it
 // mattered: the dX blocks took every CU first, the dW blocks then ran at the
 // merged kernel's lower occupancy, and at N = 16384 the mixed read and write
 // streams made it 40% slower than the two launches in turn.)
@@ -743,7 +746,7 @@ struct SmallParams {
     float *dW;                 // [K,N] fp32, or null
     float *part;               // split partials [splits][M][K] (splits > 1)
     int64_t M, K, N;
-    int64_t split_len;         // reduction elements per dX split (a multiple of 512)
+    int64_t split_len;         // reduction elements per dX split (a whole number of chunks)
     int splits;                // dX splits per column group
     int mgroups;               // dX row groups of 16*MB rows; block b = ((group, row group), split):
                                // split b % splits, row group (b / splits) % mgroups, group b / splits / mgroups
