@@ -62,11 +62,11 @@ extern "C" {
  * with zeros; with N = 0 dX is filled with zeros; K = 0 writes nothing.
  * Any pointer alignment and any sizes are accepted; 16-byte aligned pointers
  * with K and N multiples of 8 take the vectorised kernels.
- * For bf16 with 1 <= M <= 512 (decode-like), dX sums over n in several blocks
- * whose fp32 partial sums go to the library-owned workspace (about 36.2 MiB
- * per device, allocated on first use, kept until the process ends) and are
- * added in a fixed order (results repeat bit for bit); such calls that
- * overlap on one device race.
+ * For bf16 with 1 <= M <= 1024 (decode-like and small batches), dX sums over
+ * n in several blocks whose fp32 partial sums go to the library-owned
+ * workspace (about 36.2 MiB per device, allocated on first use, kept until
+ * the process ends) and are added in a fixed order (results repeat bit for
+ * bit); such calls that overlap on one device race.
  * Errors: LB_EINVAL for a negative size, or a NULL operand that a requested
  * output needs (X for dW; W for dX; dY for either); LB_EDTYPE for another
  * dtype; LB_EHIP when the workspace cannot be allocated or a launch fails.

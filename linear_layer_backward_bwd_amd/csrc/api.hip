@@ -34,7 +34,7 @@ bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; } // false for NaN
 // Library-owned workspace, allocated on first use on each device and kept
 // until the process ends: grad_norm's per-block partial sums and flags,
 // lin_bwd_ex's per-split bias partials and the fp32 dX partials of lin_bwd's
-// M <= 512 path, in separate regions.  Calls of one entry point that overlap on
+// M <= 1024 path, in separate regions.  Calls of one entry point that overlap on
 // one device share its region (and would race).
 struct Workspace {
     double *norm_partial = nullptr;
@@ -139,7 +139,7 @@ int lin_bwd_ex(const void *X, const void *W, const void *dY, void *dX, float *dW
     if (db && N > 0 && M > 0 && !dY)
         return fail(LB_EINVAL, "%s: db requested but dY is NULL", name);
     Workspace ws;
-    const bool small_dx = dX && dtype == LB_BF16 && M > 0 && M <= 512 && K > 0 && N > 0;
+    const bool small_dx = dX && dtype == LB_BF16 && M > 0 && M <= 1024 && K > 0 && N > 0;
     if ((db && N > 0) || small_dx) {
         hipError_t e = workspace(ws);
         if (e != hipSuccess)

@@ -22,7 +22,7 @@
 //                    One launch runs the tiles of both products; blocks are ordered
 //                    longest reduction first and mapped so that each XCD works on a
 //                    compact group of tiles.
-//   k_dx_smallm      dX for M <= 512 (decode-like and small batches): streams W
+//   k_dx_smallm      dX for M <= 1024 (decode-like and small batches): streams W
 //                    once per 256-row group, the reduction over n split across
 //                    blocks; the fp32 partials are added in split order by the
 //                    first blocks of k_dw_smallm (M <= 64), else by
@@ -206,6 +206,22 @@ __device__ __forceinline__ void lgkm_wait_n(bf16x8_t &w, bf16x8_t (&g)[MB]) {
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w), "+v"(g[0]), "+v"(g[1])::"memory");
     else
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w), "+v"(g[0]), "+v"(g[1]), "+v"(g[2]), "+v"(g[3])::"memory");
+}
+
+// Wait for this wave's LDS reads of XW W fragments and MW dY fragments.
+template <int XW, int MW>
+__device__ __forceinline__ void lgkm_wait_wg(bf16x8_t (&w)[XW], bf16x8_t (&g)[MW]) {
+    if constexpr (XW == 1) {
+        lgkm_wait_n<MW>(w[0], g);
+    } else if constexpr (MW == 2) {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(g[0]), "+v"(g[1])::"memory");
+    } else {
+        static_assert(XW == 4 && MW == 4, "fragment counts of the small-M dX kernel");
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(g[0]), "+v"(g[1]), "+v"(g[2]),
+                       "+v"(g[3])::"memory");
+    }
 }
 
 // Wait until at most `n` (a multiple of 8, <= 24) of this wave's DMA
@@ -729,7 +745,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
 
 // ------------------------------------------------------------------------
 // small M: at M <= 64 both products are bound by HBM, not MFMA: dX streams W
-// (2KN bytes), dW writes the fp32 output (4KN bytes).  Up to M = 512 the tile
+// (2KN bytes), dW writes the fp32 output (4KN bytes).  Up to M = 1024 the tile
 // kernel would give dX only (M/256)(K/256) tiles, so dX keeps the
 // split-reduction kernel (dW returns to the tile kernel above M = 64).  They
 // run as two launches.  (One launch holding the blocks of both was slower where it
@@ -738,7 +754,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
 // streams made it 40% slower than the two launches in turn.)
 // ------------------------------------------------------------------------
 constexpr int kSmallMaxM = 64;    // dW: the small-tile kernel up to this M
-constexpr int kSmallMaxDxM = 512; // dX: the split-reduction kernel up to this M (row groups above 256)
+constexpr int kSmallMaxDxM = 1024; // dX: the split-reduction kernel up to this M (row groups above 256)
 
 struct SmallParams {
     const uint16_t *X, *W, *G; // X[M,K], W[K,N], dY[M,N]
@@ -947,58 +963,66 @@ __device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS 
         }
     };
 
-    f32x4_t acc[MB];
+    // Fragment layout.  MB <= 4: wave w owns dX columns k0+16w .. +15 and all
+    // M rows (one W fragment and MB dY fragments per 32-deep step, MB MFMAs).
+    // MB >= 8: wave w owns row blocks w*MW .. +MW-1 and all 64 columns (four W
+    // fragments and MW dY fragments per step, 4*MW MFMAs): with one column
+    // block per wave every MFMA would need a fresh dY fragment, more LDS
+    // traffic than the LDS delivers.
+    constexpr bool kWide = MB >= 8;
+    constexpr int MW = kWide ? MB / 4 : MB; // dY fragments per step
+    constexpr int XW = kWide ? 4 : 1;       // W fragments per step
+    f32x4_t acc[MW][XW];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-        acc[mb] = f32x4_t{};
+    for (int j = 0; j < MW; ++j)
+#pragma unroll
+        for (int x = 0; x < XW; ++x)
+            acc[j][x] = f32x4_t{};
     const int sw = lane & 15; // row % 16 of every fragment row this lane reads
     // chunk j: wait for its DMA, barrier (after which every wave is done with
     // chunk j-1, so its slot takes chunk j + kS - 1), then its MFMA steps
     for (int i = 0; i < kS - 1 && i < nc; ++i)
         issue(i);
-    for (int j = 0; j < nc; ++j) {
-        dx_chunk_wait<kPerChunk>(min(kS - 2, nc - 1 - j));
+    for (int jc = 0; jc < nc; ++jc) {
+        dx_chunk_wait<kPerChunk>(min(kS - 2, nc - 1 - jc));
         slab_barrier();
-        if (j + kS - 1 < nc)
-            issue(j + kS - 1);
-        const LDS char *slot = smem + (j % kS) * kSlot;
+        if (jc + kS - 1 < nc)
+            issue(jc + kS - 1);
+        const LDS char *slot = smem + (jc % kS) * kSlot;
 #pragma unroll
         for (int u = 0; u < kCH / 32; ++u) {
             const int c = 4 * u + (lane >> 4);
-            bf16x8_t wf = read_rc<0>(slot + (16 * w + sw) * kRow + ((c ^ sw) << 4));
+            bf16x8_t wf[XW], gf[MW];
 #pragma unroll
-            for (int m4 = 0; m4 < MB; m4 += 4) { // dY fragments four at a time
-                constexpr int kG = MB < 4 ? MB : 4;
-                bf16x8_t gf[kG];
+            for (int x = 0; x < XW; ++x)
+                wf[x] = read_rc<0>(slot + (16 * (kWide ? x : w) + sw) * kRow + ((c ^ sw) << 4));
 #pragma unroll
-                for (int q = 0; q < kG; ++q)
-                    gf[q] = read_rc<0>(slot + kWSlot + (16 * (m4 + q) + sw) * kRow + ((c ^ sw) << 4));
-                lgkm_wait_n<kG>(wf, gf);
-                // lane l: dX[16mb + l%16][k0 + 16w + 4(l/16) .. +3]
+            for (int j = 0; j < MW; ++j)
+                gf[j] = read_rc<0>(slot + kWSlot + (16 * (kWide ? w * MW + j : j) + sw) * kRow + ((c ^ sw) << 4));
+            lgkm_wait_wg<XW, MW>(wf, gf);
+            // lane l: dX[row block's 16 rows: l%16][column block's 16: 4(l/16) .. +3]
 #pragma unroll
-                for (int q = 0; q < kG; ++q)
-                    acc[m4 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, gf[q], acc[m4 + q], 0, 0, 0);
-            }
+            for (int j = 0; j < MW; ++j)
+#pragma unroll
+                for (int x = 0; x < XW; ++x)
+                    acc[j][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[x], gf[j], acc[j][x], 0, 0, 0);
         }
     }
-    const int64_t k = k0 + 16 * w + 4 * (lane >> 4);
-    if (p.splits == 1) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int64_t m = m0 + 16 * mb + (lane & 15);
-            if (m < M && k < K) { // K % 8 == 0: k .. k+3 all in range
-                const u32x2_t pk = {pack_bf16x2(acc[mb][0], acc[mb][1]), pack_bf16x2(acc[mb][2], acc[mb][3])};
+    for (int j = 0; j < MW; ++j)
+#pragma unroll
+        for (int x = 0; x < XW; ++x) {
+            const int64_t m = m0 + 16 * (kWide ? w * MW + j : j) + (lane & 15);
+            const int64_t k = k0 + 16 * (kWide ? x : w) + 4 * (lane >> 4);
+            if (m >= M || k >= K) // K % 8 == 0: k .. k+3 all in range
+                continue;
+            if (p.splits == 1) {
+                const u32x2_t pk = {pack_bf16x2(acc[j][x][0], acc[j][x][1]), pack_bf16x2(acc[j][x][2], acc[j][x][3])};
                 *reinterpret_cast<u32x2_t *>(p.dX + m * K + k) = pk;
+            } else {
+                *reinterpret_cast<f32x4_t *>(p.part + ((int64_t)s * M + m) * K + k) = acc[j][x];
             }
         }
-        return;
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int64_t m = m0 + 16 * mb + (lane & 15);
-        if (m < M && k < K)
-            *reinterpret_cast<f32x4_t *>(p.part + ((int64_t)s * M + m) * K + k) = acc[mb];
-    }
 }
 
 // dX = bf16(Σ_s part[s]) over the splits in order (splits <= kDxsMaxSplits)

@@ -71,7 +71,7 @@ def test_bf16_shapes_match_oracle(M, K, N):
 
 
 # The small-M kernels: dW (M <= 64) in 64x256 tiles with one or two 32-row
-# reduction slabs; dX (M <= 512, in row groups of 256 above 256) over
+# reduction slabs; dX (M <= 1024, in row groups of 256 above 256) over
 # 64-column groups with the reduction split
 # across blocks (fp32 partials summed in split order) in chunks of 256 (M <= 64)
 # or 128.  Shapes: M in each of the 16/32/64/128/256-row variants and across
@@ -84,6 +84,7 @@ SMALL_M_SHAPES = [
     (48, 72, 264), (63, 520, 1032), (64, 8, 40), (32, 4096, 8192), (64, 33792, 64),
     (65, 264, 1032), (128, 520, 2056), (129, 1032, 392), (200, 4104, 520), (256, 1032, 3080),
     (256, 33792, 8), (257, 264, 1032), (384, 1032, 520), (512, 520, 2056), (513, 264, 392),
+    (768, 1032, 520), (1024, 264, 1032), (1025, 136, 264),
 ]
 
 
