@@ -25,10 +25,10 @@
 //   k_dx_smallm      dX for M <= 1024 (decode-like and small batches): streams W
 //                    once per 256-row group, the reduction over n split across
 //                    blocks; the fp32 partials are added in split order by the
-//                    first blocks of k_dw_smallm (M <= 64), else by
+//                    first blocks of k_dw_smallm (M <= 256), else by
 //                    k_dx_smallm_reduce.
-//   k_dw_smallm      dW for M <= 64: bound by writing the fp32 output; small tiles,
-//                    several per CU, so stores overlap other tiles' loads.
+//   k_dw_smallm      dW for M <= 256: bound by writing the fp32 output at small M;
+//                    small tiles, several per CU, so stores overlap other tiles' loads.
 //   k_lin_bwd_simt   any dtype / alignment / shape: fp32 path and ragged bf16 shapes.
 #include "device.h"
 #include "kernels.h"
@@ -185,6 +185,14 @@ __device__ __forceinline__ void lgkm_wait_tr(TrHalves &t) {
                  : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]), "+v"(t[2][0]), "+v"(t[2][1]),
                    "+v"(t[3][0]), "+v"(t[3][1]), "+v"(t[4][0]), "+v"(t[4][1]), "+v"(t[5][0]), "+v"(t[5][1]),
                    "+v"(t[6][0]), "+v"(t[6][1]), "+v"(t[7][0]), "+v"(t[7][1])
+                 :
+                 : "memory");
+}
+__device__ __forceinline__ void lgkm_wait_tr_x(TrHalves &t, bf16x4_t &x0, bf16x4_t &x1) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]), "+v"(t[2][0]), "+v"(t[2][1]),
+                   "+v"(t[3][0]), "+v"(t[3][1]), "+v"(t[4][0]), "+v"(t[4][1]), "+v"(t[5][0]), "+v"(t[5][1]),
+                   "+v"(t[6][0]), "+v"(t[6][1]), "+v"(t[7][0]), "+v"(t[7][1]), "+v"(x0), "+v"(x1)
                  :
                  : "memory");
 }
@@ -747,13 +755,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
 // small M: at M <= 64 both products are bound by HBM, not MFMA: dX streams W
 // (2KN bytes), dW writes the fp32 output (4KN bytes).  Up to M = 1024 the tile
 // kernel would give dX only (M/256)(K/256) tiles, so dX keeps the
-// split-reduction kernel (dW returns to the tile kernel above M = 64).  They
+// split-reduction kernel (dW returns to the tile kernel above M = 256).  They
 // run as two launches.  (One launch holding the blocks of both was slower where it
 // mattered: the dX blocks took every CU first, the dW blocks then ran at the
 // merged kernel's lower occupancy, and at N = 16384 the mixed read and write
 // streams made it 40% slower than the two launches in turn.)
 // ------------------------------------------------------------------------
-constexpr int kSmallMaxM = 64;    // dW: the small-tile kernel up to this M
+constexpr int kSmallMaxM = 256;   // dW: the small-tile kernel up to this M
 constexpr int kSmallMaxDxM = 1024; // dX: the split-reduction kernel up to this M (row groups above 256)
 
 struct SmallParams {
@@ -770,67 +778,51 @@ struct SmallParams {
     int reduce_blocks;         // dW blocks that also add up dX partials
 };
 
-// dW[k,n] = Σ_m X[m,k]·dY[m,n] with M <= 32*NS: a rank-M product whose cost is
+// dW[k,n] = Σ_m X[m,k]·dY[m,n] for M <= 256: a rank-M product whose cost is
 // writing the output.  Small 64x256 tiles (several resident per CU) let one
 // tile's stores overlap other tiles' loads and MFMAs; a 256x256 tile of the
 // main kernel holds a CU for its whole tile and every CU then stores at once.
-// Per block: dY[0:M, n0:n0+256] goes to LDS by DMA as OC slabs (the main
-// kernel's layout and fragment reads), X[0:M, k0:k0+64] by plain loads as
-// 32-row slabs of 128-byte rows; wave w owns dW rows k0+16w .. +15 (16 blocks
-// of 16x16, one MFMA per block and slab), then passes them through 4 KiB of
-// LDS per wave in rounds of 64 columns so that each store instruction writes
-// 4 rows x 256 contiguous bytes.
+// Per block the reduction runs in 32-row slabs through a two-slot LDS ring,
+// both operands by DMA: dY[slab, n0:n0+256] as an OC slab (the main kernel's
+// layout and fragment reads), X[slab, k0:k0+64] as 32 rows of 128 bytes.
+// Wave w owns dW rows k0+16w .. +15 (16 blocks of 16x16, one MFMA per block
+// and slab), then passes them through 4 KiB of LDS per wave in rounds of 64
+// columns so that each store instruction writes 4 rows x 256 contiguous bytes.
 constexpr int kDwsBK = 64;                 // dW rows per block (16 per wave)
 constexpr int kDwsBN = kTile;              // dW columns per block (one OC slab row)
 constexpr int kDwsXSlab = 32 * kDwsBK * 2; // X slab in LDS: 32 rows x 128 B
+constexpr int kDwsSlot = kOperandBytes + kDwsXSlab;
 constexpr int kDwsStage = 4096;            // per-wave epilogue staging: 16 rows x 256 B
-template <int NS>
-constexpr int dw_small_lds() { return NS * (kOperandBytes + kDwsXSlab) + 4 * kDwsStage; }
+constexpr int kDwsLds = 2 * kDwsSlot + 4 * kDwsStage;
 
 __device__ __forceinline__ bf16x8_t join4(bf16x4_t lo, bf16x4_t hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-__device__ __forceinline__ bf16x4_t lds_tr(const LDS char *p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4_t *)p);
-}
 
-template <int NS>
 __device__ __forceinline__ void dw_small_block(const SmallParams &p, int b, LDS char *smem) {
     const int64_t M = p.M, K = p.K, N = p.N;
-    LDS char *const gs = smem;                      // NS OC slabs of dY (32 r x 256 n)
-    LDS char *const xs = smem + NS * kOperandBytes; // NS slabs of X (32 r x 64 k)
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    LDS char *const stage = xs + NS * kDwsXSlab + w * kDwsStage;
+    LDS char *const stage = smem + 2 * kDwsSlot + w * kDwsStage;
     const int64_t n0 = (int64_t)(b % p.dw_tiles_n) * kDwsBN;
     const int64_t k0 = (int64_t)(b / p.dw_tiles_n) * kDwsBK;
-
-    // dY slabs: rows past M (and columns past N) read zero through the buffer
-    // descriptor's size / an out-of-range offset
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int64_t r0 = 32 * s;
-        const uint32_t bytes = r0 < M ? (uint32_t)(2 * (M - r0) * N) : 0u;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.G + (r0 < M ? r0 * N : 0), bytes);
+    const int nslab = (int)((M + 31) / 32);
+    // dY rows from the slab on (rows past M and columns past N read zero through
+    // the descriptor's size or kOOB); X by row: lane l of wave w's instruction
+    // fetches chunk l%8 of slab row 8w + l/8 (offsets are 32-bit: 2MK < 2^31)
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X, (uint32_t)(2 * M * K));
+    const int xrow = 8 * w + (lane >> 3);
+    const int64_t xk = k0 + 8 * (lane & 7);
+    auto issue = [&](int s) { // slab s into slot s % 2: 5 DMA instructions per wave
+        LDS char *slot = smem + (s & 1) * kDwsSlot;
+        const int64_t r0 = 32 * (int64_t)s;
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.G + r0 * N, (uint32_t)(2 * (M - r0) * N));
 #pragma unroll
         for (int q = 0; q < kDmaPerOp; ++q)
-            dma16(rs, gs + s * kOperandBytes + (w * kDmaPerOp + q) * 1024, dma_oc_off(q, N, N, n0, w, lane));
-    }
-    // X slabs: thread t loads 16 bytes of row t/8 (chunk t%8)
-    {
-        const int row = threadIdx.x >> 3, ch = threadIdx.x & 7;
-        const int64_t k = k0 + 8 * ch;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int64_t m = 32 * s + row;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (m < M && k < K) // K % 8 == 0: the chunk is all in or all out
-                v = *reinterpret_cast<const u32x4_t *>(p.X + m * K + k);
-            *reinterpret_cast<LDS u32x4_t *>(xs + s * kDwsXSlab + row * 128 + ch * 16) = v;
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+            dma16(rg, slot + (w * kDmaPerOp + q) * 1024, dma_oc_off(q, N, N, n0, w, lane));
+        const int64_t m = r0 + xrow;
+        dma16(rx, slot + kOperandBytes + 8 * w * 128, m < M && xk < K ? (uint32_t)(2 * (m * K + xk)) : kOOB);
+    };
 
     // fragments: lane l holds outer index ob + l%16 and r = 8(l/16) .. +7,
     // read as two transposing halves (r 4h .. 4h+3 of each 8)
@@ -839,19 +831,38 @@ __device__ __forceinline__ void dw_small_block(const SmallParams &p, int b, LDS 
     for (int y = 0; y < 16; ++y)
         acc[y] = f32x4_t{};
     const int g = lane >> 4, sl = lane & 15;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const LDS char *xb = xs + s * kDwsXSlab;
+    issue(0);
+    if (nslab > 1)
+        issue(1);
+    for (int s = 0; s < nslab; ++s) {
+        if (s + 1 < nslab)
+            asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); // the next slab may stay in flight
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        slab_barrier();
+        // fragment reads as inline asm with explicit waits: with the builtin the
+        // compiler waits for all DMA in flight (the next slab's too) first
+        const LDS char *gb = smem + (s & 1) * kDwsSlot;
+        const LDS char *xb = gb + kOperandBytes;
         const int xcol = 16 * w + 4 * (sl & 3);
-        const bf16x8_t xf = join4(lds_tr(xb + (8 * g + (sl >> 2)) * 128 + xcol * 2),
-                                  lds_tr(xb + (8 * g + 4 + (sl >> 2)) * 128 + xcol * 2));
-        const LDS char *gb = gs + s * kOperandBytes;
+        bf16x4_t x0 = read_tr<0>(xb + (8 * g + (sl >> 2)) * 128 + xcol * 2);
+        bf16x4_t x1 = read_tr<0>(xb + (8 * g + 4 + (sl >> 2)) * 128 + xcol * 2);
+        TrHalves tr[2]; // all 16 dY fragments in registers of their own: no read overwrites an MFMA source
 #pragma unroll
-        for (int y = 0; y < 16; ++y) {
-            const bf16x8_t gf = join4(lds_tr(gb + frag_off_oc(16 * y, lane, 0)),
-                                      lds_tr(gb + frag_off_oc(16 * y, lane, 1)));
-            // lane l: dW[k0 + 16w + l%16][n0 + 16y + 4(l/16) .. +3]
-            acc[y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf, xf, acc[y], 0, 0, 0);
+        for (int y = 0; y < 16; ++y)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                tr[y >> 3][y & 7][h] = read_tr<0>(gb + frag_off_oc(16 * y, lane, h));
+        lgkm_wait_tr_x(tr[0], x0, x1);
+        lgkm_wait_tr(tr[1]);
+        const bf16x8_t xf = join4(x0, x1);
+#pragma unroll
+        for (int y = 0; y < 16; ++y) // lane l: dW[k0 + 16w + l%16][n0 + 16y + 4(l/16) .. +3]
+            acc[y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(join4(tr[y >> 3][y & 7][0], tr[y >> 3][y & 7][1]), xf,
+                                                             acc[y], 0, 0, 0);
+        if (s + 2 < nslab) {
+            slab_barrier(); // every wave has read this slot
+            issue(s + 2);
         }
     }
 
@@ -1060,12 +1071,13 @@ __global__ __launch_bounds__(256) void k_dx_smallm(SmallParams p) {
 
 // dW blocks; with reduce_blocks > 0 the first reduce_blocks blocks also finish
 // the preceding dX launch's split reduction, 1024 entries each.
-template <int NS>
 __global__ __launch_bounds__(256) void k_dw_smallm(SmallParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem_raw[dw_small_lds<NS>()];
-    if ((int)blockIdx.x < p.reduce_blocks)
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kDwsLds];
+    if ((int)blockIdx.x < p.reduce_blocks) {
         dx_reduce_quad(p, (int64_t)blockIdx.x * 256 + threadIdx.x);
-    dw_small_block<NS>(p, blockIdx.x, (LDS char *)smem_raw);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // the slab waits below count DMA only
+    }
+    dw_small_block(p, blockIdx.x, (LDS char *)smem_raw);
 }
 
 // ------------------------------------------------------------------------
@@ -1322,10 +1334,7 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
                 sp.reduce_blocks = (int)reduce_blocks;
                 reduce_quads = 0;
             }
-            if (a.M <= 32)
-                hipLaunchKernelGGL(k_dw_smallm<1>, dim3((unsigned)blocks), dim3(256), 0, s, sp);
-            else
-                hipLaunchKernelGGL(k_dw_smallm<2>, dim3((unsigned)blocks), dim3(256), 0, s, sp);
+            hipLaunchKernelGGL(k_dw_smallm, dim3((unsigned)blocks), dim3(256), 0, s, sp);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return e;
