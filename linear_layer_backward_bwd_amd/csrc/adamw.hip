@@ -82,13 +82,19 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamWArgs a) {
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= a.n)
         return;
-    if (a.skip && *a.skip != 0)
-        return;
-    const float clip = a.clip ? *a.clip : 1.0f;
+    // The four loads go out before the skip flag and clip factor are read:
+    // waiting for those (two scalar round trips) before issuing the loads made
+    // every wave start later, and the pass 5% slower.  A skipped step reads
+    // and writes nothing else.
     float w = __builtin_nontemporal_load(a.W + i);
     float m = __builtin_nontemporal_load(a.m + i);
     float v = __builtin_nontemporal_load(a.v + i);
-    update(w, m, v, Grad<GT>::load(a.g, i), clip, a);
+    const float graw = Grad<GT>::load(a.g, i);
+    const bool skipped = a.skip && *a.skip != 0;
+    const float clip = a.clip ? *a.clip : 1.0f;
+    update(w, m, v, graw, clip, a);
+    if (skipped)
+        return;
     a.W[i] = w;
     a.m[i] = m;
     a.v[i] = v;
