@@ -90,13 +90,16 @@ __global__ __launch_bounds__(kThreads) void k_softmax_bwd_wave(const void *P, co
     for (int v = 0; v < NV; ++v) {
         const int64_t c0 = (int64_t)(v * 64 + lane) * kN;
         if (VEC) {
-            if (c0 < cols) {
-                V<T>::template load<true>(P, base + c0, p[v]); // read once: non-temporal
-                V<T>::template load<true>(dY, base + c0, g[v]);
-            } else {
+            // Unconditional loads (a lane past the row end reads the row's first
+            // vector and zeroes it): a load under a branch must land before the
+            // branch rejoins, which had serialized the NV loads of a wave.
+            const bool in = c0 < cols;
+            V<T>::template load<true>(P, base + (in ? c0 : 0), p[v]); // read once: non-temporal
+            V<T>::template load<true>(dY, base + (in ? c0 : 0), g[v]);
 #pragma unroll
-                for (int e = 0; e < kN; ++e)
-                    p[v][e] = g[v][e] = 0.0f;
+            for (int e = 0; e < kN; ++e) {
+                p[v][e] = in ? p[v][e] : 0.0f;
+                g[v][e] = in ? g[v][e] : 0.0f;
             }
         } else {
 #pragma unroll
