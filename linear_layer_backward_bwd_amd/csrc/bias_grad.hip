@@ -128,12 +128,18 @@ __global__ __launch_bounds__(kThreads) void k_bias_final(const float *partial, i
     double s = 0.0;
     if (n < N) {
         for (int s0 = g; s0 < splits; s0 += kFinalGroups * kFinalBatch) {
+            // unconditional loads (a split past the end reads split 0 and is
+            // dropped): a load under a branch must land before the branch
+            // rejoins, which had made the batch's loads go out one at a time
             float p[kFinalBatch];
 #pragma unroll
             for (int k = 0; k < kFinalBatch; ++k) {
                 const int sp = s0 + k * kFinalGroups;
-                p[k] = sp < splits ? partial[(int64_t)sp * N + n] : 0.0f;
+                p[k] = partial[(int64_t)(sp < splits ? sp : 0) * N + n];
             }
+#pragma unroll
+            for (int k = 0; k < kFinalBatch; ++k)
+                p[k] = s0 + k * kFinalGroups < splits ? p[k] : 0.0f;
 #pragma unroll
             for (int k = 0; k < kFinalBatch; ++k)
                 s += (double)p[k];
