@@ -40,3 +40,31 @@ def test_every_traffic_record_names_a_known_kernel_and_matches_its_code():
 def test_a_changed_kernel_voids_its_record(monkeypatch):
     monkeypatch.setattr(bench, "source_hash", lambda kernel: "0" * 16)
     assert bench.recorded_traffic("k_adamw", "adamw_2p28_f16") is None
+
+
+def test_tile_traffic_model_closed_forms():
+    # M = K = N = 8192: 32 x 32 tiles per product, 128 per XCD; the 32 tiles an XCD
+    # runs together are 4 tile rows x 8 tile columns, i.e. 12 panels of 256 rows
+    # over the 8192-long reduction (4 MiB each) per 32 tiles
+    M = K = N = 8192
+    panel = 256 * 8192 * 2
+    per_product = (1024 // 32) * 12 * panel
+    out = 2 * M * K + 4 * K * N
+    assert bench.lin_bwd_tiled_bytes(M, K, N) == 2 * per_product + out
+    # one tile at a time per XCD shares nothing: two panels per tile
+    assert bench.lin_bwd_tiled_bytes(M, K, N, cus_per_xcd=1) == 2 * 1024 * 2 * panel + out
+    # one tile per product: each product reads its two operands once, so G is read
+    # twice (once per product) and everything else as in the algorithmic bytes
+    assert bench.lin_bwd_tiled_bytes(256, 256, 256) == bench.lin_bwd_min_bytes(256, 256, 256) + 2 * 256 * 256
+
+
+def test_tile_traffic_model_rotation_splits_sharing():
+    # rows 32 KiB apart (N = 16384): tiles of the four rotation groups (by tile
+    # column) read the dX panels from different starting slabs, so the 4 x 8 group
+    # fetches 4 x 4 + 8 panels instead of 4 + 8
+    M, K, N = 4096, 2048, 16384
+    dx_tiles = (M // 256) * (K // 256)          # 128: 16 per XCD, fewer than 32
+    assert dx_tiles % 8 == 0
+    rotated = bench.lin_bwd_tiled_bytes(M, K, N)
+    plain = bench.lin_bwd_tiled_bytes(M, K, N - 8)   # same tiles, no rotation
+    assert rotated > plain
