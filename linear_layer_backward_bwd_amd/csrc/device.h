@@ -27,9 +27,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// two floats -> packed bf16 pair (low half = a), round to nearest even.
+// two floats -> packed bf16 pair (low half = a), round to nearest even: one
+// v_cvt_pk_bf16_f32 (converted one at a time, the halves took four instructions)
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+    typedef float f32x2_v __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_v){a, b}, bf16x2_v));
 }
 
 __device__ __forceinline__ bool aligned16(const void *p) {
