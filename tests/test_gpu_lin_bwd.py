@@ -143,14 +143,27 @@ REDUCTIONS = [8, 24, 32, 40, 64, 72, 96, 128, 136, 200, 256, 264, 392]
 
 @pytest.mark.parametrize("R", REDUCTIONS)
 def test_short_and_ragged_reductions(R):
-    # dX on the tile path (M > 64): reduction over n = R
-    case = synth.linear_case(96, 72, R, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=R)
-    dX, _ = run(case, need_dw=False)
-    check_full(case, dX, None)
+    # dX, reduction over n = R: on the split-reduction kernel (M = 96) and on the
+    # tile kernel (M = 1040 > 1024: four whole tile rows and a 16-row one)
+    for M in (96, 1040):
+        case = synth.linear_case(M, 72, R, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=R + M)
+        dX, _ = run(case, need_dw=False)
+        check_full(case, dX, None)
     # dW: reduction over m = R
     case = synth.linear_case(R, 72, 80, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=R + 1)
     _, dW = run(case, need_dx=False)
     check_full(case, None, dW)
+
+
+# Both products on the tile kernel (M > 1024) with ragged output edges: each
+# 256x256 tile's four 128x128 quadrants are whole, partial or wholly outside the
+# output (M = 1152: dX rows 1152..1279 of the last tile row; N = 96: dW columns
+# 128..255), and the reductions end in partial slab pairs.
+@pytest.mark.parametrize("M,K,N", [(1152, 384, 200), (1100, 264, 520), (2000, 520, 96), (1300, 136, 1032)])
+def test_tile_kernel_ragged_edges(M, K, N):
+    case = synth.linear_case(M, K, N, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=M ^ K ^ N)
+    dX, dW = run(case)
+    check_full(case, dX, dW)
 
 
 @pytest.mark.parametrize("M,K,N", [(64, 64, 64), (33, 100, 70), (130, 264, 96)])
