@@ -230,6 +230,19 @@ const char *lb_last_error(void);
 /* lb_version -- the library's version string (static storage). */
 const char *lb_version(void);
 
+/*
+ * lb_shutdown -- frees the library-owned workspace of every device (the
+ * gradient norm's partial sums, lin_bwd_ex's bias partials and lin_bwd's dX
+ * partials for bf16 with 1 <= M <= 1024, allocated on first use per device;
+ * without this call they are kept until the process ends).  A later call that
+ * needs a workspace allocates it again.  No call of this library may be in
+ * flight on any device, on any stream, nor may another thread call into the
+ * library meanwhile: the caller synchronizes first.  The calling thread's
+ * current device is unchanged.  Returns LB_OK, or LB_EHIP
+ * when a free fails (the remaining workspaces are still freed and forgotten).
+ */
+int lb_shutdown(void);
+
 #ifdef __cplusplus
 }
 #endif

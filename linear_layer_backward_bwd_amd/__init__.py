@@ -12,7 +12,7 @@ import ctypes
 import os
 
 __all__ = ["lin_bwd", "adamw_step", "adamw_step_f16", "adamw_step_bf16", "lb_set_stream",
-           "lb_last_error", "lb_version", "library", "LIB_PATH", "LB_F32", "LB_BF16"]
+           "lb_last_error", "lb_version", "lb_shutdown", "library", "LIB_PATH", "LB_F32", "LB_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinbwd.so")
 LB_F32, LB_BF16, LB_F16 = 0, 1, 2
@@ -52,6 +52,8 @@ def library() -> ctypes.CDLL:
     lib.lb_last_error.restype = ctypes.c_char_p
     lib.lb_version.argtypes = []
     lib.lb_version.restype = ctypes.c_char_p
+    lib.lb_shutdown.argtypes = []
+    lib.lb_shutdown.restype = i32
     _lib = lib
     return lib
 
@@ -62,6 +64,11 @@ def lb_last_error() -> str:
 
 def lb_version() -> str:
     return library().lb_version().decode()
+
+
+def lb_shutdown() -> None:
+    """Frees the library-owned per-device workspace; no call may be in flight."""
+    _check(library().lb_shutdown(), "lb_shutdown")
 
 
 def lb_set_stream(stream) -> None:

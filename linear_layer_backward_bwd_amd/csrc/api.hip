@@ -292,4 +292,26 @@ const char *lb_last_error(void) { return tl_error.c_str(); }
 
 const char *lb_version(void) { return "linbwd 0.1.0 gfx950"; }
 
+int lb_shutdown(void) {
+    tl_error.clear();
+    int cur = 0;
+    hipError_t first = hipGetDevice(&cur);
+    if (first != hipSuccess)
+        return hip_fail("lb_shutdown", first);
+    std::lock_guard<std::mutex> lock(ws_mutex);
+    for (const auto &kv : ws_by_device) {
+        // one allocation per device; norm_partial is its start
+        hipError_t e = hipSetDevice(kv.first);
+        if (e == hipSuccess)
+            e = hipFree(kv.second.norm_partial);
+        if (e != hipSuccess && first == hipSuccess)
+            first = e;
+    }
+    ws_by_device.clear();
+    const hipError_t e = hipSetDevice(cur);
+    if (first == hipSuccess)
+        first = e;
+    return first == hipSuccess ? LB_OK : hip_fail("lb_shutdown", first);
+}
+
 } // extern "C"

@@ -25,7 +25,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("lin_bwd", "adamw_step", "adamw_step_f16", "adamw_step_bf16", "adamw_step_ex",
                  "grad_norm", "lin_bwd_ex", "softmax_bwd",
-                 "lb_set_stream", "lb_last_error", "lb_version"):
+                 "lb_set_stream", "lb_last_error", "lb_version", "lb_shutdown"):
         assert want in names
 
 

@@ -166,6 +166,18 @@ def test_tile_kernel_ragged_edges(M, K, N):
     check_full(case, dX, dW)
 
 
+def test_shutdown_then_calls_allocate_again():
+    # M = 48 keeps its dX split partials in the library's workspace
+    case = synth.linear_case(48, 1032, 2056, "bf16", seed=21)
+    dX0, dW0 = run(case)
+    lb.lb_shutdown()
+    lb.lb_shutdown()  # nothing left to free
+    dX1, dW1 = run(case)
+    assert torch.equal(dX0.view(torch.int16), dX1.view(torch.int16))
+    assert torch.equal(dW0.view(torch.int32), dW1.view(torch.int32))
+    check_full(case, dX1, dW1)
+
+
 @pytest.mark.parametrize("M,K,N", [(64, 64, 64), (33, 100, 70), (130, 264, 96)])
 def test_f32_shapes_match_oracle(M, K, N):
     case = synth.linear_case(M, K, N, "f32", x_std=1.0, w_std=1.0, g_std=1.0, seed=7)
