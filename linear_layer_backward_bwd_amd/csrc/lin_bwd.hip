@@ -638,7 +638,7 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
     };
     // Read LDS read number j (0 .. kReads-1) of a slab held in ring slot `stage`
     // (an int, or a compile-time constant that becomes the immediate offset).
-    auto read_frag = [&](auto stage, int j, Frags &an, Frags &bn, TrHalves (&tr)[2]) {
+    auto read_frag = [&](auto stage, int j, TrHalves (&tr)[2]) {
         const int op = j / (kFrags * kRPF), xb = (j % (kFrags * kRPF)) / kRPF, h = j % kRPF;
         const LDS char *base = smem + fo[op][xb][h];
         if constexpr (std::is_integral_v<decltype(stage)>) {
@@ -702,7 +702,7 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
             mfma16(acc[x][y], bf[y], af[x]);
             __builtin_amdgcn_sched_barrier(0);
             if (i % kReadSlot == 0 && i / kReadSlot < kReads)
-                read_frag(next_stage(stage), i / kReadSlot, an, bn, tr);
+                read_frag(next_stage(stage), i / kReadSlot, tr);
             if (dmas && i >= kDmaSlot0 && i < kDmaSlot0 + kDmaStep * kDmaPerSlab &&
                 (i - kDmaSlot0) % kDmaStep == 0) {
                 const int d = (i - kDmaSlot0) / kDmaStep;
@@ -734,7 +734,7 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
             TrHalves tr[2];
 #pragma unroll
             for (int j = 0; j < kReads; ++j)
-                read_frag(0, j, af, bf, tr);
+                read_frag(0, j, tr);
             finish_reads(af, bf, tr);
         }
         // steady state: slabs s+1..s+3 exist and slab s+4 is a full slab, branch free
