@@ -311,6 +311,16 @@ def test_large_m2048_sampled():
     assert torch.equal(dX, dX2) and torch.equal(dW, dW2)
 
 
+def test_operand_of_2gib_takes_the_general_path():
+    """W of exactly 2 GiB (32768 x 32768 bf16) is past the 32-bit buffer offsets of the MFMA
+    kernels, so lin_bwd runs the general kernel: sampled entries against the oracle, and the
+    4 GiB dW written without touching the guard words around it."""
+    case = synth.linear_case(8, 32768, 32768, "bf16", x_std=1.0, w_std=0.02, g_std=1e-4, seed=31)
+    dX, dW = run(case)
+    assert not torch.isnan(dX).any() and not torch.isnan(dW).any()
+    _sampled_check(case, dX, dW, 256, 31)
+
+
 @pytest.mark.parametrize("proj", range(4))
 def test_block_projection_sampled(proj):
     """One Transformer block's projections at M = 16384 (QKV, out, up, down), sampled."""
