@@ -124,3 +124,13 @@ def test_block_projections_full():
         lb.lin_bwd_ex(None, None, c.G, db=db)
         torch.cuda.synchronize()
         check(db.cpu().numpy(), c.G, "bf16")
+
+
+def test_after_shutdown_the_workspace_is_allocated_again():
+    G = synth.to_storage(synth.normal((3000, 2056), 1e-4, synth._gen(99)), "bf16")
+    before = gpu_db(G)
+    torch.cuda.synchronize()
+    lb.lb_shutdown()
+    after = gpu_db(G)
+    check(after, G, "bf16")
+    assert np.array_equal(np.asarray(before), np.asarray(after))

@@ -197,3 +197,14 @@ def test_found_inf_skips_adamw_step_ex():
     assert np.array_equal(W.cpu().numpy(), case.W.numpy())
     assert np.array_equal(m.cpu().numpy(), case.m.numpy())
     assert np.array_equal(v.cpu().numpy(), case.v.numpy())
+
+
+def test_after_shutdown_the_workspace_is_allocated_again():
+    case = synth.adamw_case(1 << 20, "f16", g_scale=1024.0, seed=77)
+    ref = oracle.grad_norm(synth.bits(case.g), "f16", case.inv_scale, 1.0)
+    before = gpu_norm(case.g, case.inv_scale, 1.0)
+    torch.cuda.synchronize()
+    lb.lb_shutdown()
+    after = gpu_norm(case.g, case.inv_scale, 1.0)
+    check(after, ref, 1.0)
+    assert list(before) == list(after)
