@@ -70,7 +70,13 @@ def _load():
     for name in ("oracle_dx", "oracle_dw"):
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, i32, i64, i64, i64, vp]
-        fn.restype = None
+    lib.oracle_dx.restype = i32
+    lib.oracle_dw.restype = None
+    for name in ("oracle_dx_rows", "oracle_dw_rows"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, i32, i64, i64, i64, vp, i64, vp]
+    lib.oracle_dx_rows.restype = i32
+    lib.oracle_dw_rows.restype = None
     for name in ("oracle_dx_at", "oracle_dw_at"):
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, i32, i64, i64, i64, vp, vp, i64, vp]
@@ -144,7 +150,8 @@ def lin_bwd(X, W, G, dtype: str, need_dx: bool = True, need_dw: bool = True):
     dX = dW = None
     if need_dx:
         dX = np.empty((M, K), dtype=np.float64)
-        lib.oracle_dx(_ptr(G), _ptr(W), _DTYPES[dtype], M, K, N, _ptr(dX))
+        if lib.oracle_dx(_ptr(G), _ptr(W), _DTYPES[dtype], M, K, N, _ptr(dX)) != 0:
+            raise MemoryError("oracle_dx: no host memory for the copy of W")
     if need_dw:
         dW = np.empty((K, N), dtype=np.float64)
         lib.oracle_dw(_ptr(X), _ptr(G), _DTYPES[dtype], M, K, N, _ptr(dW))
@@ -171,6 +178,42 @@ def softmax_bwd(P, dY, dtype: str) -> np.ndarray:
     dX = np.empty((rows, cols), dtype=np.float64)
     _load().oracle_softmax_bwd(_ptr(P), _ptr(dY), _DTYPES[dtype], rows, cols, _ptr(dX))
     return dX
+
+
+def _row_list(rows, limit):
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+    if rows.size and (rows.min() < 0 or rows.max() >= limit):
+        raise ValueError("row index out of range")
+    return rows
+
+
+def dx_rows(G, W, dtype: str, rows) -> np.ndarray:
+    """Whole rows of dX = G·Wᵀ in float64: out[i, :] = dX[rows[i], :] (shape len(rows) x K)."""
+    G, W = _as_input(G, dtype), _as_input(W, dtype)
+    M, N = G.shape
+    K = W.shape[0]
+    if W.shape[1] != N:
+        raise ValueError("shape mismatch: G%s W%s" % (G.shape, W.shape))
+    rows = _row_list(rows, M)
+    out = np.empty((rows.size, K), dtype=np.float64)
+    if _load().oracle_dx_rows(_ptr(G), _ptr(W), _DTYPES[dtype], M, K, N, _ptr(rows), rows.size,
+                              _ptr(out)) != 0:
+        raise MemoryError("oracle_dx_rows: no host memory for the copy of W")
+    return out
+
+
+def dw_rows(X, G, dtype: str, rows) -> np.ndarray:
+    """Whole rows of dW = Xᵀ·G in float64: out[i, :] = dW[rows[i], :] (shape len(rows) x N)."""
+    X, G = _as_input(X, dtype), _as_input(G, dtype)
+    M, K = X.shape
+    N = G.shape[1]
+    if G.shape[0] != M:
+        raise ValueError("shape mismatch: X%s G%s" % (X.shape, G.shape))
+    rows = _row_list(rows, K)
+    out = np.empty((rows.size, N), dtype=np.float64)
+    _load().oracle_dw_rows(_ptr(X), _ptr(G), _DTYPES[dtype], M, K, N, _ptr(rows), rows.size,
+                           _ptr(out))
+    return out
 
 
 def dx_at(G, W, dtype: str, rows, cols) -> np.ndarray:

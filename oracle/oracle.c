@@ -21,7 +21,9 @@
  *    到 Kernel", section "一个线性层，前向和反向到底在算什么" (shapes with batch
  *    and sequence merged into M, transposes expressed through strides).
  *    The oracle evaluates both sums in fp64 on the exact decoded input values,
- *    as plain loops with no blocking or reordering.
+ *    as plain loops with no blocking: every entry is its sum taken in index
+ *    order from 0.0 (the whole-row functions add the terms of one output row
+ *    side by side, which changes no entry's operations or their order).
  *
  *  - AdamW with decoupled weight decay on an fp32 master copy, after
  *    unscaling a loss-scaled gradient:
@@ -60,6 +62,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -123,32 +126,104 @@ int oracle_num_threads(void)
 
 /* ---- Linear backward, fp64 ---------------------------------------------- */
 
-/* dX[m,k] = Σ_n G[m,n]·W[k,n], all M·K entries.  Row-major, contiguous. */
-void oracle_dx(const void *G, const void *W, int dtype,
-               int64_t M, int64_t K, int64_t N, double *dX)
+/* acc[j] += x * value(p[off + j]) for j = 0 .. n-1: one fp64 product and one
+ * fp64 addition per j (the element type is tested once, outside the loop). */
+static void add_scaled_row(double *acc, double x, const void *p, int dtype, int64_t off, int64_t n)
+{
+    if (dtype == ORACLE_F32) {
+        const float *q = (const float *)p + off;
+        for (int64_t j = 0; j < n; ++j)
+            acc[j] += x * (double)q[j];
+    } else if (dtype == ORACLE_BF16) {
+        const uint16_t *q = (const uint16_t *)p + off;
+        for (int64_t j = 0; j < n; ++j)
+            acc[j] += x * oracle_bf16_to_f64(q[j]);
+    } else {
+        const uint16_t *q = (const uint16_t *)p + off;
+        for (int64_t j = 0; j < n; ++j)
+            acc[j] += x * oracle_f16_to_f64(q[j]);
+    }
+}
+
+/* Size in bytes of one stored element. */
+static size_t elt_size(int dtype)
+{
+    return dtype == ORACLE_F32 ? 4 : 2;
+}
+
+/*
+ * Whole rows of dX: out[i*K + k] = dX[rows[i], k] = Σ_n G[rows[i],n]·W[k,n] for
+ * every k (rows == NULL: every row m = i of dX, nrows = M).
+ *
+ * Each entry is the plain sum over n = 0, 1, ..., N-1, started from 0.0, one
+ * fp64 product (exact for bf16, fp16 and fp32 inputs) and one fp64 addition per
+ * term, in that order: the same operations as the dot product of oracle_dx_at.
+ * The terms of all k of one row are added side by side (n outer, k inner), so
+ * that memory is read in order; for that W's elements are first copied into
+ * Wt[n,k] = W[k,n] (a copy of the stored values, no arithmetic).
+ * Returns 0, or -1 when the copy cannot be allocated.
+ */
+int oracle_dx_rows(const void *G, const void *W, int dtype,
+                   int64_t M, int64_t K, int64_t N,
+                   const int64_t *rows, int64_t nrows, double *out)
+{
+    (void)M;
+    const size_t es = elt_size(dtype);
+    char *Wt = malloc((size_t)(K * N > 0 ? K * N : 1) * es);
+    if (!Wt)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            memcpy(Wt + (size_t)(n * K + k) * es, (const char *)W + (size_t)(k * N + n) * es, es);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; ++i) {
+        const int64_t m = rows ? rows[i] : i;
+        double *acc = out + i * K;
+        for (int64_t k = 0; k < K; ++k)
+            acc[k] = 0.0;
+        for (int64_t n = 0; n < N; ++n)
+            add_scaled_row(acc, elt(G, dtype, m * N + n), Wt, dtype, n * K, K);
+    }
+    free(Wt);
+    return 0;
+}
+
+/*
+ * Whole rows of dW: out[i*N + n] = dW[rows[i], n] = Σ_m X[m,rows[i]]·G[m,n] for
+ * every n (rows == NULL: every row k = i of dW, nrows = K).  Each entry is the
+ * plain sum over m = 0, 1, ..., M-1 from 0.0, the same operations in the same
+ * order as the dot product of oracle_dw_at; the terms of all n of one row are
+ * added side by side (m outer, n inner).
+ */
+void oracle_dw_rows(const void *X, const void *G, int dtype,
+                    int64_t M, int64_t K, int64_t N,
+                    const int64_t *rows, int64_t nrows, double *out)
 {
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t m = 0; m < M; ++m)
-        for (int64_t k = 0; k < K; ++k) {
-            double s = 0.0;
-            for (int64_t n = 0; n < N; ++n)
-                s += elt(G, dtype, m * N + n) * elt(W, dtype, k * N + n);
-            dX[m * K + k] = s;
-        }
+    for (int64_t i = 0; i < nrows; ++i) {
+        const int64_t k = rows ? rows[i] : i;
+        double *acc = out + i * N;
+        for (int64_t n = 0; n < N; ++n)
+            acc[n] = 0.0;
+        for (int64_t m = 0; m < M; ++m)
+            add_scaled_row(acc, elt(X, dtype, m * K + k), G, dtype, m * N, N);
+    }
+}
+
+/* dX[m,k] = Σ_n G[m,n]·W[k,n], all M·K entries.  Row-major, contiguous.
+ * Returns 0, or -1 when out of host memory. */
+int oracle_dx(const void *G, const void *W, int dtype,
+              int64_t M, int64_t K, int64_t N, double *dX)
+{
+    return oracle_dx_rows(G, W, dtype, M, K, N, NULL, M, dX);
 }
 
 /* dW[k,n] = Σ_m X[m,k]·G[m,n], all K·N entries. */
 void oracle_dw(const void *X, const void *G, int dtype,
                int64_t M, int64_t K, int64_t N, double *dW)
 {
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t k = 0; k < K; ++k)
-        for (int64_t n = 0; n < N; ++n) {
-            double s = 0.0;
-            for (int64_t m = 0; m < M; ++m)
-                s += elt(X, dtype, m * K + k) * elt(G, dtype, m * N + n);
-            dW[k * N + n] = s;
-        }
+    oracle_dw_rows(X, G, dtype, M, K, N, NULL, K, dW);
 }
 
 /* The same sums at a list of (row, col) positions only: out[i] = dX[rows[i], cols[i]]. */

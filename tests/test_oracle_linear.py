@@ -167,3 +167,37 @@ def test_rejects_bad_shapes_and_samples():
         oracle.dx_at(np.zeros((2, 3), np.float32), np.zeros((4, 3), np.float32), "f32", [2], [0])
     with pytest.raises(TypeError):
         oracle.lin_bwd(a.astype(np.float64), a, a, "f32")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+def test_whole_rows_equal_entry_by_entry_dot_products(dtype):
+    """The whole-row functions (terms of one output row added side by side, used for the
+    full tensors) against the entry-by-entry dot products: the same fp64 operations in the
+    same order, so every entry must agree bit for bit -- at every position of a ragged shape
+    and for each element type."""
+    M, K, N = 23, 37, 31
+    case = synth.linear_case(M, K, N, dtype, x_std=1.0, w_std=1.0, g_std=1.0, seed=17)
+    Xb, Wb, Gb = synth.bits(case.X), synth.bits(case.W), synth.bits(case.G)
+    dX, dW = oracle.lin_bwd(Xb, Wb, Gb, dtype)
+    r, c = np.meshgrid(np.arange(M), np.arange(K), indexing="ij")
+    assert np.array_equal(oracle.dx_at(Gb, Wb, dtype, r.ravel(), c.ravel()).reshape(M, K), dX)
+    r, c = np.meshgrid(np.arange(K), np.arange(N), indexing="ij")
+    assert np.array_equal(oracle.dw_at(Xb, Gb, dtype, r.ravel(), c.ravel()).reshape(K, N), dW)
+
+
+def test_row_subsets_equal_the_full_tensors():
+    """dx_rows / dw_rows on a shuffled subset with a repeated row give those rows of the full
+    tensors, bit for bit; an out-of-range row is refused."""
+    M, K, N = 19, 26, 33
+    case = synth.linear_case(M, K, N, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=18)
+    Xb, Wb, Gb = synth.bits(case.X), synth.bits(case.W), synth.bits(case.G)
+    dX, dW = oracle.lin_bwd(Xb, Wb, Gb, "bf16")
+    rows = np.array([M - 1, 0, 7, 7, 3])
+    assert np.array_equal(oracle.dx_rows(Gb, Wb, "bf16", rows), dX[rows])
+    rows = np.array([K - 1, 2, 2, 11])
+    assert np.array_equal(oracle.dw_rows(Xb, Gb, "bf16", rows), dW[rows])
+    assert oracle.dx_rows(Gb, Wb, "bf16", []).shape == (0, K)
+    with pytest.raises(ValueError):
+        oracle.dx_rows(Gb, Wb, "bf16", [M])
+    with pytest.raises(ValueError):
+        oracle.dw_rows(Xb, Gb, "bf16", [-1])
