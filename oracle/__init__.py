@@ -44,7 +44,7 @@ _lib = None
 def build() -> str:
     """Compile oracle.c with gcc into liboracle.so (IEEE scalar float, no contraction)."""
     tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+    cmd = ["gcc", "-O2", "-ftree-vectorize", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
            "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)

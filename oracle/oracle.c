@@ -76,7 +76,7 @@
 /* ---- exact decoders ---------------------------------------------------- */
 
 /* bf16 is the upper half of an IEEE binary32: widening is a 16-bit shift. */
-double oracle_bf16_to_f64(uint16_t h)
+static double bf16_value(uint16_t h)
 {
     uint32_t bits = (uint32_t)h << 16;
     float f;
@@ -85,7 +85,7 @@ double oracle_bf16_to_f64(uint16_t h)
 }
 
 /* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 mantissa bits. */
-double oracle_f16_to_f64(uint16_t h)
+static double f16_value(uint16_t h)
 {
     int sign = (h >> 15) & 1;
     int e = (h >> 10) & 0x1f;
@@ -100,13 +100,25 @@ double oracle_f16_to_f64(uint16_t h)
     return sign ? -mag : mag;
 }
 
+/* The decoders, exported for the pins (the loops below use the static ones,
+ * which the compiler can inline). */
+double oracle_bf16_to_f64(uint16_t h)
+{
+    return bf16_value(h);
+}
+
+double oracle_f16_to_f64(uint16_t h)
+{
+    return f16_value(h);
+}
+
 static double elt(const void *p, int dtype, int64_t i)
 {
     if (dtype == ORACLE_F32)
         return (double)((const float *)p)[i];
     if (dtype == ORACLE_BF16)
-        return oracle_bf16_to_f64(((const uint16_t *)p)[i]);
-    return oracle_f16_to_f64(((const uint16_t *)p)[i]);
+        return bf16_value(((const uint16_t *)p)[i]);
+    return f16_value(((const uint16_t *)p)[i]);
 }
 
 void oracle_decode(const void *p, int dtype, int64_t n, double *out)
@@ -127,7 +139,10 @@ int oracle_num_threads(void)
 /* ---- Linear backward, fp64 ---------------------------------------------- */
 
 /* acc[j] += x * value(p[off + j]) for j = 0 .. n-1: one fp64 product and one
- * fp64 addition per j (the element type is tested once, outside the loop). */
+ * fp64 addition per j (the element type is tested once, outside the loop).
+ * Built twice, for AVX2 and for any x86-64, and picked at load time by the CPU:
+ * wider vectors, the same IEEE operations (no contraction, no reassociation). */
+__attribute__((target_clones("avx2", "default")))
 static void add_scaled_row(double *acc, double x, const void *p, int dtype, int64_t off, int64_t n)
 {
     if (dtype == ORACLE_F32) {
@@ -137,13 +152,18 @@ static void add_scaled_row(double *acc, double x, const void *p, int dtype, int6
     } else if (dtype == ORACLE_BF16) {
         const uint16_t *q = (const uint16_t *)p + off;
         for (int64_t j = 0; j < n; ++j)
-            acc[j] += x * oracle_bf16_to_f64(q[j]);
+            acc[j] += x * bf16_value(q[j]);
     } else {
         const uint16_t *q = (const uint16_t *)p + off;
         for (int64_t j = 0; j < n; ++j)
-            acc[j] += x * oracle_f16_to_f64(q[j]);
+            acc[j] += x * f16_value(q[j]);
     }
 }
+
+/* Output rows that the whole-row functions build side by side, so that one
+ * pass over the shared operand serves them all (each row's own operations and
+ * their order do not depend on it). */
+#define ORACLE_ROW_GROUP 8
 
 /* Size in bytes of one stored element. */
 static size_t elt_size(int dtype)
@@ -158,8 +178,8 @@ static size_t elt_size(int dtype)
  * Each entry is the plain sum over n = 0, 1, ..., N-1, started from 0.0, one
  * fp64 product (exact for bf16, fp16 and fp32 inputs) and one fp64 addition per
  * term, in that order: the same operations as the dot product of oracle_dx_at.
- * The terms of all k of one row are added side by side (n outer, k inner), so
- * that memory is read in order; for that W's elements are first copied into
+ * The terms of all k of a few rows are added side by side (n outer, k inner),
+ * so that memory is read in order; for that W's elements are first copied into
  * Wt[n,k] = W[k,n] (a copy of the stored values, no arithmetic).
  * Returns 0, or -1 when the copy cannot be allocated.
  */
@@ -177,13 +197,16 @@ int oracle_dx_rows(const void *G, const void *W, int dtype,
         for (int64_t n = 0; n < N; ++n)
             memcpy(Wt + (size_t)(n * K + k) * es, (const char *)W + (size_t)(k * N + n) * es, es);
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t i = 0; i < nrows; ++i) {
-        const int64_t m = rows ? rows[i] : i;
-        double *acc = out + i * K;
-        for (int64_t k = 0; k < K; ++k)
-            acc[k] = 0.0;
+    for (int64_t i0 = 0; i0 < nrows; i0 += ORACLE_ROW_GROUP) {
+        const int64_t cnt = nrows - i0 < ORACLE_ROW_GROUP ? nrows - i0 : ORACLE_ROW_GROUP;
+        for (int64_t i = i0; i < i0 + cnt; ++i)
+            for (int64_t k = 0; k < K; ++k)
+                out[i * K + k] = 0.0;
         for (int64_t n = 0; n < N; ++n)
-            add_scaled_row(acc, elt(G, dtype, m * N + n), Wt, dtype, n * K, K);
+            for (int64_t i = i0; i < i0 + cnt; ++i) {
+                const int64_t m = rows ? rows[i] : i;
+                add_scaled_row(out + i * K, elt(G, dtype, m * N + n), Wt, dtype, n * K, K);
+            }
     }
     free(Wt);
     return 0;
@@ -193,21 +216,24 @@ int oracle_dx_rows(const void *G, const void *W, int dtype,
  * Whole rows of dW: out[i*N + n] = dW[rows[i], n] = Σ_m X[m,rows[i]]·G[m,n] for
  * every n (rows == NULL: every row k = i of dW, nrows = K).  Each entry is the
  * plain sum over m = 0, 1, ..., M-1 from 0.0, the same operations in the same
- * order as the dot product of oracle_dw_at; the terms of all n of one row are
- * added side by side (m outer, n inner).
+ * order as the dot product of oracle_dw_at; the terms of all n of a few rows
+ * are added side by side (m outer, n inner).
  */
 void oracle_dw_rows(const void *X, const void *G, int dtype,
                     int64_t M, int64_t K, int64_t N,
                     const int64_t *rows, int64_t nrows, double *out)
 {
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t i = 0; i < nrows; ++i) {
-        const int64_t k = rows ? rows[i] : i;
-        double *acc = out + i * N;
-        for (int64_t n = 0; n < N; ++n)
-            acc[n] = 0.0;
+    for (int64_t i0 = 0; i0 < nrows; i0 += ORACLE_ROW_GROUP) {
+        const int64_t cnt = nrows - i0 < ORACLE_ROW_GROUP ? nrows - i0 : ORACLE_ROW_GROUP;
+        for (int64_t i = i0; i < i0 + cnt; ++i)
+            for (int64_t n = 0; n < N; ++n)
+                out[i * N + n] = 0.0;
         for (int64_t m = 0; m < M; ++m)
-            add_scaled_row(acc, elt(X, dtype, m * K + k), G, dtype, m * N, N);
+            for (int64_t i = i0; i < i0 + cnt; ++i) {
+                const int64_t k = rows ? rows[i] : i;
+                add_scaled_row(out + i * N, elt(X, dtype, m * K + k), G, dtype, m * N, N);
+            }
     }
 }
 
