@@ -19,6 +19,11 @@
  *    at the caller's next synchronisation, as for any HIP kernel.
  *  - Outputs must not alias inputs or each other.
  *  - Calls enqueued on different streams that write the same memory race.
+ *  - The few calls that need temporary device memory (noted below) take it
+ *    from a library-owned workspace of about 36.2 MiB per (device, stream)
+ *    pair, allocated on the first such call on that stream and kept until the
+ *    process ends or lb_shutdown(): calls on one stream run in order and share
+ *    it, calls on different streams use different workspaces and may overlap.
  */
 #ifndef LINBWD_H
 #define LINBWD_H
@@ -64,12 +69,13 @@ extern "C" {
  * with K and N multiples of 8 take the vectorised kernels.
  * For bf16 with 1 <= M <= 1024 (decode-like and small batches), dX sums over
  * n in several blocks whose fp32 partial sums go to the library-owned
- * workspace (about 36.2 MiB per device, allocated on first use, kept until
- * the process ends) and are added in a fixed order (results repeat bit for
- * bit); such calls that overlap on one device race.
- * Errors: LB_EINVAL for a negative size, or a NULL operand that a requested
- * output needs (X for dW; W for dX; dY for either); LB_EDTYPE for another
- * dtype; LB_EHIP when the workspace cannot be allocated or a launch fails.
+ * workspace of the calling thread's stream and are added in a fixed order
+ * (results repeat bit for bit).  The kernels are chosen by dtype, alignment
+ * and M unless lb_set_lin_bwd_path() forces a path.
+ * Errors: LB_EINVAL for a negative size, a NULL operand that a requested
+ * output needs (X for dW; W for dX; dY for either), or a forced kernel path
+ * that cannot run the call; LB_EDTYPE for another dtype; LB_EHIP when the
+ * workspace cannot be allocated or a launch fails.
  * Both outputs NULL is a no-op (LB_OK).
  */
 int lin_bwd(const void *X, const void *W, const void *dY, void *dX, float *dW,
@@ -87,12 +93,12 @@ int lin_bwd(const void *X, const void *W, const void *dY, void *dX, float *dW,
  * fp32 per row range and the partials in fp64, in a fixed order (results
  * repeat bit for bit); M = 0 fills db with zeros.  X and W may be NULL when
  * only db is requested.  Additional error: LB_EINVAL for a NULL dY with db
- * requested and M, N > 0.  Uses the library-owned workspace (about 36.2 MiB
- * per device, allocated on first use, kept until the process ends); calls that
- * request db and overlap on one device race.
+ * requested and M, N > 0.  db's row partials go to the library-owned
+ * workspace of the calling thread's stream.
  */
 int lin_bwd_ex(const void *X, const void *W, const void *dY, void *dX, float *dW, float *db,
                int64_t M, int64_t K, int64_t N, int dtype);
+
 
 /*
  * adamw_step -- one fused pass over n parameters that unscales the gradient
@@ -181,9 +187,8 @@ int adamw_step_ex(float *W, const void *grad, int grad_dtype, float *m, float *v
  *
  * The summation order is fixed for a given n and 16-byte alignment of grad
  * (the result is reproducible).
- * Uses the library-owned workspace (about 36.2 MiB per device, allocated on
- * first use, kept until the process ends); calls that overlap on one device race.
- * Asynchronous on the thread's stream.  Errors: LB_EDTYPE for another
+ * The per-block partials go to the library-owned workspace of the calling
+ * thread's stream.  Asynchronous on the thread's stream.  Errors: LB_EDTYPE for another
  * grad_dtype; LB_EINVAL for n < 0, NULL d_out, or NULL grad with n > 0;
  * LB_EHIP when the workspace cannot be allocated or a launch fails.
  */
@@ -217,12 +222,38 @@ int softmax_bwd(const void *P, const void *dY, void *dX, int64_t rows, int64_t c
  * lb_set_stream -- the HIP stream (a hipStream_t, passed as void*) on which
  * the calling thread's later calls enqueue their kernels; NULL selects the
  * null stream.  The setting is per thread.  Returns LB_OK.
+ * ("GPU 优化实战 Part 2", section "完整训练循环（整合一切）": the step's kernels
+ * are launched asynchronously in stream order, with one synchronisation at
+ * the end.)
  */
 int lb_set_stream(void *hip_stream);
 
 /*
+ * lb_set_lin_bwd_path -- forces which kernels lin_bwd / lin_bwd_ex use for
+ * the calling thread's later calls (per thread, like the stream), so that
+ * the kernels can be compared with each other on the same inputs and a
+ * caller can pin a choice; every path computes the same sums, rounded once.
+ *   LB_PATH_AUTO     chosen by dtype, alignment and M (the default)
+ *   LB_PATH_TILE     both products on the 256x256 MFMA tile kernel
+ *   LB_PATH_SMALL_M  dX on the split-reduction kernel (M <= 1024), dW on the
+ *                    small-tile kernel (M <= 256)
+ *   LB_PATH_GENERAL  both products on the element-wise kernel
+ * A forced MFMA path (TILE, SMALL_M) needs bf16 operands, K and N multiples
+ * of 8, 16-byte aligned pointers and operands below 2 GiB, and SMALL_M the M
+ * limits above; a call it cannot run fails with LB_EINVAL before anything is
+ * enqueued.  Returns LB_OK, or LB_EINVAL for another value.
+ */
+#define LB_PATH_AUTO 0
+#define LB_PATH_TILE 1
+#define LB_PATH_SMALL_M 2
+#define LB_PATH_GENERAL 3
+int lb_set_lin_bwd_path(int path);
+
+/*
  * lb_last_error -- a description of the calling thread's last non-zero
- * return, or "" if there was none.  The string is owned by the library and
+ * return, or "" if there was none.  (The pages' listings check no error;
+ * every entry point here validates its arguments on the host and reports
+ * why it refused a call.)  The string is owned by the library and
  * valid until the thread's next call.
  */
 const char *lb_last_error(void);
@@ -231,10 +262,11 @@ const char *lb_last_error(void);
 const char *lb_version(void);
 
 /*
- * lb_shutdown -- frees the library-owned workspace of every device (the
- * gradient norm's partial sums, lin_bwd_ex's bias partials and lin_bwd's dX
- * partials for bf16 with 1 <= M <= 1024, allocated on first use per device;
- * without this call they are kept until the process ends).  A later call that
+ * lb_shutdown -- frees the library-owned workspaces of every device and
+ * stream (the gradient norm's partial sums, lin_bwd_ex's bias partials and
+ * lin_bwd's dX partials for bf16 with 1 <= M <= 1024, allocated on first use
+ * per device and stream; without this call they are kept until the process
+ * ends).  A later call that
  * needs a workspace allocates it again.  No call of this library may be in
  * flight on any device, on any stream, nor may another thread call into the
  * library meanwhile: the caller synchronizes first.  The calling thread's

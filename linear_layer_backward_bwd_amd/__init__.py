@@ -11,12 +11,16 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["lin_bwd", "adamw_step", "adamw_step_f16", "adamw_step_bf16", "lb_set_stream",
-           "lb_last_error", "lb_version", "lb_shutdown", "library", "LIB_PATH", "LB_F32", "LB_BF16"]
+__all__ = ["lin_bwd", "lin_bwd_ex", "adamw_step", "adamw_step_f16", "adamw_step_bf16",
+           "adamw_step_ex", "grad_norm", "softmax_bwd", "lb_set_stream", "lb_set_lin_bwd_path",
+           "lin_bwd_path", "lb_last_error", "lb_version", "lb_shutdown", "library", "LIB_PATH",
+           "LB_F32", "LB_BF16", "LB_F16", "LB_PATH_AUTO", "LB_PATH_TILE", "LB_PATH_SMALL_M",
+           "LB_PATH_GENERAL"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinbwd.so")
 LB_F32, LB_BF16, LB_F16 = 0, 1, 2
 LB_OK, LB_EINVAL, LB_EDTYPE, LB_EHIP = 0, -1, -2, -4
+LB_PATH_AUTO, LB_PATH_TILE, LB_PATH_SMALL_M, LB_PATH_GENERAL = 0, 1, 2, 3
 
 _lib = None
 
@@ -48,6 +52,8 @@ def library() -> ctypes.CDLL:
     lib.grad_norm.restype = i32
     lib.lb_set_stream.argtypes = [vp]
     lib.lb_set_stream.restype = i32
+    lib.lb_set_lin_bwd_path.argtypes = [i32]
+    lib.lb_set_lin_bwd_path.restype = i32
     lib.lb_last_error.argtypes = []
     lib.lb_last_error.restype = ctypes.c_char_p
     lib.lb_version.argtypes = []
@@ -75,6 +81,27 @@ def lb_set_stream(stream) -> None:
     """Select the HIP stream (a torch.cuda.Stream, a raw handle int, or None)."""
     handle = getattr(stream, "cuda_stream", stream)
     library().lb_set_stream(ctypes.c_void_p(handle or 0))
+
+
+def lb_set_lin_bwd_path(path: int) -> None:
+    """Force the kernels of this thread's later lin_bwd / lin_bwd_ex calls (LB_PATH_*)."""
+    _check(library().lb_set_lin_bwd_path(int(path)), "lb_set_lin_bwd_path")
+
+
+class lin_bwd_path:
+    """Context manager: ``with lin_bwd_path(LB_PATH_TILE): ...`` forces a kernel path for
+    the calls inside and restores automatic selection afterwards."""
+
+    def __init__(self, path: int):
+        self.path = path
+
+    def __enter__(self):
+        lb_set_lin_bwd_path(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        lb_set_lin_bwd_path(LB_PATH_AUTO)
+        return False
 
 
 def _check(rc: int, name: str) -> None:

@@ -3,9 +3,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
 #include <mutex>
 #include <string>
-#include <unordered_map>
+#include <utility>
 
 #include "../../include/linbwd.h"
 #include "kernels.h"
@@ -13,6 +14,7 @@
 namespace {
 
 thread_local hipStream_t tl_stream = nullptr;
+thread_local int tl_path = lb::PATH_AUTO;
 thread_local std::string tl_error;
 
 int fail(int code, const char *fmt, ...) {
@@ -31,11 +33,12 @@ int hip_fail(const char *what, hipError_t e) {
 
 bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; } // false for NaN
 
-// Library-owned workspace, allocated on first use on each device and kept
-// until the process ends: grad_norm's per-block partial sums and flags,
-// lin_bwd_ex's per-split bias partials and the fp32 dX partials of lin_bwd's
-// M <= 1024 path, in separate regions.  Calls of one entry point that overlap on
-// one device share its region (and would race).
+// Library-owned workspace, allocated on first use for each (device, stream)
+// pair and kept until the process ends or lb_shutdown(): grad_norm's
+// per-block partial sums and flags, lin_bwd_ex's per-split bias partials and
+// the fp32 dX partials of lin_bwd's M <= 1024 path, in separate regions.
+// Calls on one stream run in order, so they can share one workspace; calls on
+// two streams of a device get two workspaces and may overlap.
 struct Workspace {
     double *norm_partial = nullptr;
     int *norm_flag = nullptr;
@@ -43,7 +46,11 @@ struct Workspace {
     float *dx_partial = nullptr;
 };
 std::mutex ws_mutex;
-std::unordered_map<int, Workspace> ws_by_device;
+std::map<std::pair<int, hipStream_t>, Workspace> ws_by_stream;
+
+constexpr size_t kNormBytes = lb::kNormMaxBlocks * (sizeof(double) + sizeof(int));
+constexpr size_t kBiasBytes = lb::kBiasWorkspaceFloats * sizeof(float);
+constexpr size_t kDxBytes = lb::kDxPartialFloats * sizeof(float);
 
 hipError_t workspace(Workspace &out) {
     int dev = 0;
@@ -51,25 +58,88 @@ hipError_t workspace(Workspace &out) {
     if (e != hipSuccess)
         return e;
     std::lock_guard<std::mutex> lock(ws_mutex);
-    auto it = ws_by_device.find(dev);
-    if (it == ws_by_device.end()) {
-        const size_t norm_bytes = lb::kNormMaxBlocks * (sizeof(double) + sizeof(int));
-        const size_t bias_bytes = lb::kBiasWorkspaceFloats * sizeof(float);
-        const size_t dx_bytes = lb::kDxPartialFloats * sizeof(float);
+    const auto key = std::make_pair(dev, tl_stream);
+    auto it = ws_by_stream.find(key);
+    if (it == ws_by_stream.end()) {
         void *p = nullptr;
-        e = hipMalloc(&p, norm_bytes + bias_bytes + dx_bytes);
+        e = hipMalloc(&p, kNormBytes + kBiasBytes + kDxBytes);
         if (e != hipSuccess)
             return e;
         Workspace w;
         w.norm_partial = static_cast<double *>(p);
         w.norm_flag = reinterpret_cast<int *>(w.norm_partial + lb::kNormMaxBlocks);
-        w.bias_partial = reinterpret_cast<float *>(static_cast<char *>(p) + norm_bytes);
-        w.dx_partial = reinterpret_cast<float *>(static_cast<char *>(p) + norm_bytes + bias_bytes);
-        it = ws_by_device.emplace(dev, w).first;
+        w.bias_partial = reinterpret_cast<float *>(static_cast<char *>(p) + kNormBytes);
+        w.dx_partial = reinterpret_cast<float *>(static_cast<char *>(p) + kNormBytes + kBiasBytes);
+        it = ws_by_stream.emplace(key, w).first;
     }
     out = it->second;
     return hipSuccess;
 }
+
+// lin_bwd and lin_bwd_ex: the temporaries go to the stream's workspace.
+int lin_bwd_impl(const char *name, const void *X, const void *W, const void *dY, void *dX, float *dW, float *db,
+                 int64_t M, int64_t K, int64_t N, int dtype) {
+    tl_error.clear();
+    if (dtype != LB_F32 && dtype != LB_BF16)
+        return fail(LB_EDTYPE, "%s: dtype %d is not LB_F32 (0) or LB_BF16 (1)", name, dtype);
+    if (M < 0 || K < 0 || N < 0)
+        return fail(LB_EINVAL, "%s: negative size M=%lld K=%lld N=%lld", name, (long long)M, (long long)K,
+                    (long long)N);
+    const int64_t lim = (int64_t)1 << 31;
+    if (M >= lim || K >= lim || N >= lim)
+        return fail(LB_EINVAL, "%s: sizes must be below 2^31 (M=%lld K=%lld N=%lld)", name, (long long)M,
+                    (long long)K, (long long)N);
+    // dX has M*K entries and sums over N; dW has K*N entries and sums over M;
+    // db has N entries and sums over M.
+    if (dX && M > 0 && K > 0 && N > 0 && (!dY || !W))
+        return fail(LB_EINVAL, "%s: dX requested but dY or W is NULL", name);
+    if (dW && K > 0 && N > 0 && M > 0 && (!X || !dY))
+        return fail(LB_EINVAL, "%s: dW requested but X or dY is NULL", name);
+    if (db && N > 0 && M > 0 && !dY)
+        return fail(LB_EINVAL, "%s: db requested but dY is NULL", name);
+    lb::LinBwdArgs a;
+    a.X = X;
+    a.W = W;
+    a.dY = dY;
+    a.dX = dX;
+    a.dW = dW;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.bf16 = dtype == LB_BF16;
+    a.path = tl_path;
+    if (const char *why = lb::lin_bwd_path_refusal(a))
+        return fail(LB_EINVAL, "%s: the forced kernel path (%d) cannot run this call: %s", name, tl_path, why);
+    float *dx_partial = nullptr, *bias_partial = nullptr;
+    const bool small_dx = dX && dtype == LB_BF16 && M > 0 && M <= 1024 && K > 0 && N > 0;
+    if ((db && N > 0) || small_dx) {
+        Workspace ws;
+        hipError_t e = workspace(ws);
+        if (e != hipSuccess)
+            return hip_fail("lin_bwd_ex (workspace)", e);
+        dx_partial = ws.dx_partial;
+        bias_partial = ws.bias_partial;
+    }
+    a.dx_partial = dx_partial;
+    a.dx_partial_floats = dx_partial ? lb::kDxPartialFloats : 0;
+    hipError_t e = lb::launch_lin_bwd(a, tl_stream);
+    if (e != hipSuccess)
+        return hip_fail(name, e);
+    if (db) {
+        lb::BiasArgs b;
+        b.dY = dY;
+        b.db = db;
+        b.M = M;
+        b.N = N;
+        b.bf16 = dtype == LB_BF16;
+        b.partial = bias_partial;
+        e = lb::launch_bias_grad(b, tl_stream);
+        if (e != hipSuccess)
+            return hip_fail(name, e);
+    }
+    return LB_OK;
+}
+
 
 int adamw_impl(const char *name, lb::GradType gt, float *W, const void *g, float *m, float *v, int64_t n,
                float lr, float b1, float b2, float eps, float wd, int step, float inv_scale,
@@ -119,60 +189,7 @@ extern "C" {
 
 int lin_bwd_ex(const void *X, const void *W, const void *dY, void *dX, float *dW, float *db, int64_t M,
                int64_t K, int64_t N, int dtype) {
-    const char *name = db ? "lin_bwd_ex" : "lin_bwd";
-    tl_error.clear();
-    if (dtype != LB_F32 && dtype != LB_BF16)
-        return fail(LB_EDTYPE, "%s: dtype %d is not LB_F32 (0) or LB_BF16 (1)", name, dtype);
-    if (M < 0 || K < 0 || N < 0)
-        return fail(LB_EINVAL, "%s: negative size M=%lld K=%lld N=%lld", name, (long long)M, (long long)K,
-                    (long long)N);
-    const int64_t lim = (int64_t)1 << 31;
-    if (M >= lim || K >= lim || N >= lim)
-        return fail(LB_EINVAL, "%s: sizes must be below 2^31 (M=%lld K=%lld N=%lld)", name, (long long)M,
-                    (long long)K, (long long)N);
-    // dX has M*K entries and sums over N; dW has K*N entries and sums over M;
-    // db has N entries and sums over M.
-    if (dX && M > 0 && K > 0 && N > 0 && (!dY || !W))
-        return fail(LB_EINVAL, "%s: dX requested but dY or W is NULL", name);
-    if (dW && K > 0 && N > 0 && M > 0 && (!X || !dY))
-        return fail(LB_EINVAL, "%s: dW requested but X or dY is NULL", name);
-    if (db && N > 0 && M > 0 && !dY)
-        return fail(LB_EINVAL, "%s: db requested but dY is NULL", name);
-    Workspace ws;
-    const bool small_dx = dX && dtype == LB_BF16 && M > 0 && M <= 1024 && K > 0 && N > 0;
-    if ((db && N > 0) || small_dx) {
-        hipError_t e = workspace(ws);
-        if (e != hipSuccess)
-            return hip_fail("lin_bwd_ex (workspace)", e);
-    }
-    lb::LinBwdArgs a;
-    a.X = X;
-    a.W = W;
-    a.dY = dY;
-    a.dX = dX;
-    a.dW = dW;
-    a.M = M;
-    a.K = K;
-    a.N = N;
-    a.bf16 = dtype == LB_BF16;
-    a.dx_partial = ws.dx_partial;
-    a.dx_partial_floats = ws.dx_partial ? lb::kDxPartialFloats : 0;
-    hipError_t e = lb::launch_lin_bwd(a, tl_stream);
-    if (e != hipSuccess)
-        return hip_fail(name, e);
-    if (db) {
-        lb::BiasArgs b;
-        b.dY = dY;
-        b.db = db;
-        b.M = M;
-        b.N = N;
-        b.bf16 = dtype == LB_BF16;
-        b.partial = ws.bias_partial;
-        e = lb::launch_bias_grad(b, tl_stream);
-        if (e != hipSuccess)
-            return hip_fail("lin_bwd_ex (bias)", e);
-    }
-    return LB_OK;
+    return lin_bwd_impl(db ? "lin_bwd_ex" : "lin_bwd", X, W, dY, dX, dW, db, M, K, N, dtype);
 }
 
 int lin_bwd(const void *X, const void *W, const void *dY, void *dX, float *dW, int64_t M, int64_t K,
@@ -288,6 +305,14 @@ int lb_set_stream(void *hip_stream) {
     return LB_OK;
 }
 
+int lb_set_lin_bwd_path(int path) {
+    tl_error.clear();
+    if (path < LB_PATH_AUTO || path > LB_PATH_GENERAL)
+        return fail(LB_EINVAL, "lb_set_lin_bwd_path: %d is not an LB_PATH_* value", path);
+    tl_path = path;
+    return LB_OK;
+}
+
 const char *lb_last_error(void) { return tl_error.c_str(); }
 
 const char *lb_version(void) { return "linbwd 0.1.0 gfx950"; }
@@ -299,15 +324,15 @@ int lb_shutdown(void) {
     if (first != hipSuccess)
         return hip_fail("lb_shutdown", first);
     std::lock_guard<std::mutex> lock(ws_mutex);
-    for (const auto &kv : ws_by_device) {
-        // one allocation per device; norm_partial is its start
-        hipError_t e = hipSetDevice(kv.first);
+    for (const auto &kv : ws_by_stream) {
+        // one allocation per (device, stream); norm_partial is its start
+        hipError_t e = hipSetDevice(kv.first.first);
         if (e == hipSuccess)
             e = hipFree(kv.second.norm_partial);
         if (e != hipSuccess && first == hipSuccess)
             first = e;
     }
-    ws_by_device.clear();
+    ws_by_stream.clear();
     const hipError_t e = hipSetDevice(cur);
     if (first == hipSuccess)
         first = e;

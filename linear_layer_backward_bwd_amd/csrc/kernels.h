@@ -44,6 +44,14 @@ struct NormArgs {
 hipError_t launch_grad_norm(const NormArgs &a, GradType gt, hipStream_t s);
 
 // ---- Linear backward ----------------------------------------------------
+// Which kernels run the two products (LB_PATH_* of linbwd.h).
+enum LinPath {
+    PATH_AUTO = 0,    // chosen by dtype, alignment and M
+    PATH_TILE = 1,    // the 256x256 MFMA tile kernel for both products
+    PATH_SMALL_M = 2, // split-reduction dX (M <= 1024) and small-tile dW (M <= 256)
+    PATH_GENERAL = 3, // the element-wise kernel (any dtype, alignment, size)
+};
+
 struct LinBwdArgs {
     const void *X, *W, *dY;
     void *dX;  // may be null (skip)
@@ -54,13 +62,18 @@ struct LinBwdArgs {
     // or null: then that path runs unsplit
     float *dx_partial;
     int64_t dx_partial_floats;
+    int path = PATH_AUTO; // a LinPath
 };
 
 constexpr int64_t kDxPartialFloats = 1 << 23; // 32 MiB of dX partials
 
 
-// Chooses kernels by dtype, alignment and M; enqueues 1-2 launches.
+// Chooses kernels by dtype, alignment and M (or a.path); enqueues 1-3 launches.
 hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s);
+
+// nullptr when a.path can run this call, else why it cannot (checked on the
+// host before anything is enqueued).
+const char *lin_bwd_path_refusal(const LinBwdArgs &a);
 
 // ---- bias gradient ------------------------------------------------------
 constexpr int kBiasMaxSplits = 256;              // row splits per launch

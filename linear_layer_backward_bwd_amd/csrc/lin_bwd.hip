@@ -1230,30 +1230,56 @@ hipError_t launch_simt(const LinBwdArgs &a, bool need_dx, bool need_dw, hipStrea
     return hipGetLastError();
 }
 
+// The MFMA kernels read 16-byte chunks of bf16 rows (K and N multiples of 8,
+// 16-byte aligned pointers) through buffer descriptors whose 32-bit offsets
+// mark "out of range" with 2^31: each operand must be smaller than 2 GiB.
+bool mfma_eligible(const LinBwdArgs &a, bool need_dx, bool need_dw) {
+    bool vec = a.bf16 && (a.K % 8 == 0) && (a.N % 8 == 0);
+    if (need_dx)
+        vec = vec && is_aligned16(a.dX) && (a.N == 0 || (is_aligned16(a.dY) && is_aligned16(a.W)));
+    if (need_dw)
+        vec = vec && is_aligned16(a.dW) && (a.M == 0 || (is_aligned16(a.X) && is_aligned16(a.dY)));
+    const int64_t lim = (int64_t)1 << 31;
+    return vec && 2 * a.M * a.K < lim && 2 * a.K * a.N < lim && 2 * a.M * a.N < lim;
+}
+
 } // namespace
+
+const char *lin_bwd_path_refusal(const LinBwdArgs &a) {
+    if (a.path == PATH_AUTO || a.path == PATH_GENERAL)
+        return nullptr;
+    const bool need_dx = a.dX != nullptr && a.M > 0 && a.K > 0;
+    const bool need_dw = a.dW != nullptr && a.K > 0 && a.N > 0;
+    if (!need_dx && !need_dw)
+        return nullptr;
+    if (a.path != PATH_TILE && a.path != PATH_SMALL_M)
+        return "unknown path";
+    if (!mfma_eligible(a, need_dx, need_dw))
+        return "the MFMA kernels need bf16 operands, K and N multiples of 8, 16-byte aligned pointers "
+               "and operands smaller than 2 GiB";
+    if (a.path == PATH_SMALL_M) {
+        if (need_dx && a.M > kSmallMaxDxM)
+            return "the small-M dX kernel takes M <= 1024";
+        if (need_dw && a.M > kSmallMaxM)
+            return "the small-M dW kernel takes M <= 256";
+    }
+    return nullptr;
+}
 
 hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
     const bool need_dx = a.dX != nullptr && a.M > 0 && a.K > 0;
     const bool need_dw = a.dW != nullptr && a.K > 0 && a.N > 0;
     if (!need_dx && !need_dw)
         return hipSuccess;
-
-    bool vec = a.bf16 && (a.K % 8 == 0) && (a.N % 8 == 0);
-    if (need_dx)
-        vec = vec && is_aligned16(a.dX) && (a.N == 0 || (is_aligned16(a.dY) && is_aligned16(a.W)));
-    if (need_dw)
-        vec = vec && is_aligned16(a.dW) && (a.M == 0 || (is_aligned16(a.X) && is_aligned16(a.dY)));
-    if (!vec)
+    if (a.path == PATH_GENERAL || !mfma_eligible(a, need_dx, need_dw))
         return launch_simt(a, need_dx, need_dw, s);
 
-    // buffer offsets are 32-bit with 2^31 marking "out of range": each operand
-    // of the MFMA path must be smaller than 2 GiB
-    const int64_t lim = (int64_t)1 << 31;
-    if (2 * a.M * a.K >= lim || 2 * a.K * a.N >= lim || 2 * a.M * a.N >= lim)
-        return launch_simt(a, need_dx, need_dw, s);
-
-    const bool small_dx = need_dx && a.M <= kSmallMaxDxM && a.N > 0;
-    const bool small_dw = need_dw && a.M > 0 && a.M <= kSmallMaxM;
+    // the small-M kernels skip the empty sums (N = 0 for dX, M = 0 for dW),
+    // which the tile kernel writes as zeros
+    bool small_dx = need_dx && a.N > 0 && a.M <= kSmallMaxDxM;
+    bool small_dw = need_dw && a.M > 0 && a.M <= kSmallMaxM;
+    if (a.path == PATH_TILE)
+        small_dx = small_dw = false;
     MfmaParams p{};
     int nj = 0;
     TileJob jx{}, jw{};

@@ -109,3 +109,39 @@ def sample_positions(rows, cols, count, seed):
     edge_r = np.array([0, 0, rows - 1, rows - 1] + [rows - 1] * 16 + list(rng.integers(0, rows, 16)))
     edge_c = np.array([0, cols - 1, 0, cols - 1] + list(rng.integers(0, cols, 16)) + [cols - 1] * 16)
     return np.concatenate([r, edge_r]), np.concatenate([c, edge_c])
+
+
+# ---- per-element error bounds of the GEMM outputs -------------------------------------
+#
+# A kernel adds the R products of an entry in fp32: 32 at a time inside one MFMA, then into
+# the accumulator (and, split across blocks, partial sums added in a fixed order).  With
+# exact bf16 products and unit roundoff u = 2^-24 each entry's error is at most
+#     gamma(R) * S,   gamma(R) = u * (R / 32 + 64),   S = Σ |a·b|
+# (R / 32 accumulator additions, up to 32 inside an MFMA, and the split partials).  A bf16
+# output adds one rounding to nearest, at most 2^-8 of the value.
+
+U32 = 2.0 ** -24
+U_BF16 = 2.0 ** -8
+
+
+def gamma(R, sequential=False):
+    """Error factor for R products summed by an MFMA kernel, or one by one in fp32
+    (sequential: the element-wise kernel's chain of R roundings)."""
+    return U32 * (R if sequential else R / 32.0 + 64.0)
+
+
+def abs_bits(b, dtype):
+    """The stored elements with their sign cleared (|x| exactly)."""
+    if dtype == "f32":
+        return np.abs(b)
+    return b & np.uint16(0x7FFF)
+
+
+def assert_within_bound(got, ref, S, R, bf16_out, what, sequential=False):
+    got = np.asarray(got, np.float64)
+    bound = 1.01 * gamma(R, sequential) * S
+    if bf16_out:
+        bound = bound + U_BF16 * (np.abs(ref) + bound)
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), "%s: %d entries beyond the per-element bound, e.g. got %r ref %r bound %r" % (
+        what, int(bad.sum()), got[bad][:3], ref[bad][:3], bound[bad][:3])

@@ -25,7 +25,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("lin_bwd", "adamw_step", "adamw_step_f16", "adamw_step_bf16", "adamw_step_ex",
                  "grad_norm", "lin_bwd_ex", "softmax_bwd",
-                 "lb_set_stream", "lb_last_error", "lb_version", "lb_shutdown"):
+                 "lb_set_stream", "lb_set_lin_bwd_path", "lb_last_error", "lb_version",
+                 "lb_shutdown"):
         assert want in names
 
 
@@ -224,3 +225,52 @@ def test_softmax_bwd_binding_checks():
         lb.softmax_bwd(p, p, torch.zeros(4, 8, dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         lb.softmax_bwd(p.t(), p.t())
+
+
+@pytest.mark.parametrize("path", [-1, 4, 99])
+def test_set_lin_bwd_path_rejects_unknown_values(path):
+    assert lb.library().lb_set_lin_bwd_path(path) == -1
+    assert "LB_PATH" in lb.lb_last_error()
+
+
+# (path, M, K, N, dtype, X, W, dY, dX, dW): forced paths that cannot run the call are refused
+# on the host, before any workspace or launch (the fake pointers are never dereferenced)
+P16, P32, P48, P64 = (ctypes.c_void_p(v) for v in (4096, 8192, 12288, 16384))
+ODD = ctypes.c_void_p(4098)
+
+
+@pytest.mark.parametrize("path,M,K,N,dtype,ptrs", [
+    (lb.LB_PATH_TILE, 64, 64, 64, 0, (P16, P32, P48, P64, NULL)),        # fp32 operands
+    (lb.LB_PATH_SMALL_M, 64, 64, 64, 0, (P16, P32, P48, NULL, P64)),
+    (lb.LB_PATH_TILE, 64, 60, 64, 1, (P16, P32, P48, P64, NULL)),        # K not a multiple of 8
+    (lb.LB_PATH_TILE, 64, 64, 68, 1, (P16, P32, P48, NULL, P64)),        # N not a multiple of 8
+    (lb.LB_PATH_TILE, 64, 64, 64, 1, (P16, P32, ODD, P64, NULL)),        # misaligned dY
+    (lb.LB_PATH_TILE, 1 << 17, 1 << 14, 8, 1, (P16, P32, P48, P64, NULL)),  # dX of 4 GiB
+    (lb.LB_PATH_SMALL_M, 1025, 64, 64, 1, (P16, P32, P48, P64, NULL)),   # dX: M <= 1024 only
+    (lb.LB_PATH_SMALL_M, 257, 64, 64, 1, (P16, P32, P48, NULL, P64)),    # dW: M <= 256 only
+])
+def test_forced_path_refused_on_host(path, M, K, N, dtype, ptrs):
+    lib = lb.library()
+    X, W, dY, dX, dW = ptrs
+    assert lib.lb_set_lin_bwd_path(path) == 0
+    try:
+        assert lib.lin_bwd(X, W, dY, dX, dW, M, K, N, dtype) == -1
+        assert "forced kernel path" in lb.lb_last_error()
+        assert lib.lin_bwd_ex(X, W, dY, dX, dW, NULL, M, K, N, dtype) == -1
+    finally:
+        assert lib.lb_set_lin_bwd_path(lb.LB_PATH_AUTO) == 0
+
+
+def test_forced_path_is_per_thread_and_restored():
+    import threading
+    lib = lb.library()
+    seen = []
+    with lb.lin_bwd_path(lb.LB_PATH_TILE):
+        # another thread still runs with automatic selection: fp32 is accepted there
+        # (K = 0 writes nothing, so no GPU is touched)
+        t = threading.Thread(target=lambda: seen.append(
+            lib.lin_bwd(P16, P32, P48, P64, NULL, 64, 0, 64, 0)))
+        t.start()
+        t.join()
+        assert lib.lin_bwd(P16, P32, P48, P64, NULL, 64, 64, 64, 0) == -1
+    assert seen == [0]

@@ -11,8 +11,8 @@ import torch
 import linear_layer_backward_bwd_amd as lb
 import oracle
 import synth
-from gpu_util import (DW_RELF, DX_RELF, F32_OUT_RELF, Guarded, bits, host_f64, relf,
-                      sample_positions)
+from gpu_util import (DW_RELF, DX_RELF, F32_OUT_RELF, Guarded, abs_bits, assert_within_bound,
+                      bits, host_f64, relf, sample_positions)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -286,29 +286,69 @@ def test_decode_like_m32_full_compare():
 
 
 def _sampled_check(case, dX, dW, count, seed):
+    """Sampled entries (plus corners and edges): relative Frobenius error over the sample and
+    the per-element bound of every sampled entry."""
     Xb, Wb, Gb = synth.bits(case.X), synth.bits(case.W), synth.bits(case.G)
+    aX, aW, aG = (abs_bits(b, "bf16") for b in (Xb, Wb, Gb))
     r, c = sample_positions(case.M, case.K, count, seed)
     ref = oracle.dx_at(Gb, Wb, "bf16", r, c)
     got = host_f64(dX[torch.from_numpy(r), torch.from_numpy(c)])
     assert relf(got, ref) <= DX_RELF, "dX sampled relF %.3g" % relf(got, ref)
-    # each bf16 entry is within one rounding (2^-8 relative) of the exact value, plus
-    # the fp32 accumulation error of its sum
-    scale = np.abs(ref) + 1e-3 * np.sqrt(np.mean(ref ** 2))
-    assert np.all(np.abs(got - ref) <= 2 ** -8 * scale)
+    assert_within_bound(got, ref, oracle.dx_at(aG, aW, "bf16", r, c), case.N, True, "dX")
     r, c = sample_positions(case.K, case.N, count, seed + 1)
     ref = oracle.dw_at(Xb, Gb, "bf16", r, c)
     got = host_f64(dW[torch.from_numpy(r), torch.from_numpy(c)])
     assert relf(got, ref) <= DW_RELF, "dW sampled relF %.3g" % relf(got, ref)
+    assert_within_bound(got, ref, oracle.dw_at(aX, aG, "bf16", r, c), case.M, False, "dW")
 
 
-def test_large_m2048_sampled():
-    """bf16 X[2048,4096], W[4096,4096], G[2048,4096]: sampled entries + determinism."""
+def check_full_with_bounds(case, dX, dW, bound_rows=256, seed=0):
+    """Every entry against the oracle (the relative Frobenius bars over the whole tensors),
+    then the per-element bound on `bound_rows` seeded whole rows of each output."""
+    rX, rW = check_full(case, dX, dW)
+    Xb, Wb, Gb = synth.bits(case.X), synth.bits(case.W), synth.bits(case.G)
+    aX, aW, aG = (abs_bits(b, case.dtype) for b in (Xb, Wb, Gb))
+    rng = np.random.default_rng(seed)
+    if dX is not None:
+        rows = np.unique(np.concatenate([rng.integers(0, case.M, bound_rows), [0, case.M - 1]]))
+        assert_within_bound(host_f64(dX[torch.from_numpy(rows)]), rX[rows],
+                            oracle.dx_rows(aG, aW, case.dtype, rows), case.N,
+                            case.dtype == "bf16", "dX")
+    if dW is not None:
+        rows = np.unique(np.concatenate([rng.integers(0, case.K, bound_rows), [0, case.K - 1]]))
+        assert_within_bound(host_f64(dW[torch.from_numpy(rows)]), rW[rows],
+                            oracle.dw_rows(aX, aG, case.dtype, rows), case.M, False, "dW")
+    return rX, rW
+
+
+def test_large_m2048_full():
+    """bf16 X[2048,4096], W[4096,4096], G[2048,4096]: every entry of dX and dW against the
+    oracle, per-element bounds on 256 rows of each, and a second run bit for bit."""
     case = synth.linear_m2048(seed=0)
     dX, dW = run(case)
-    assert not torch.isnan(dX).any() and not torch.isnan(dW).any()
-    _sampled_check(case, dX, dW, 4096, 0)
+    check_full_with_bounds(case, dX, dW)
     dX2, dW2 = run(case)
     assert torch.equal(dX, dX2) and torch.equal(dW, dW2)
+
+
+# The tile kernel starts the reduction of four groups of dX tiles (by tile column) 32
+# slabs apart when the rows of dY and W are a multiple of 32 KiB apart (N = 16384):
+# M > 1024 puts dX on the tile kernel, K > 512 gives tile columns with a nonzero start.
+def test_rotated_dx_reduction_full():
+    case = synth.linear_case(1040, 2056, 16384, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=41)
+    dX, dW = run(case)
+    check_full_with_bounds(case, dX, dW, bound_rows=64)
+
+
+def test_rotated_dx_reduction_integer_inputs_are_exact():
+    rng = np.random.default_rng(42)
+    M, K, N = 1040, 776, 16384
+    mk = lambda *sh: torch.tensor(rng.integers(-2, 3, size=sh), dtype=torch.float32).to(torch.bfloat16)
+    case = synth.LinearCase(M, K, N, "bf16", mk(M, K), mk(K, N), mk(M, N))
+    dX, dW = run(case)
+    rX, rW = oracle.lin_bwd(synth.bits(case.X), synth.bits(case.W), synth.bits(case.G), "bf16")
+    assert np.array_equal(dW.cpu().numpy(), rW.astype(np.float32))
+    assert torch.equal(dX.cpu(), torch.from_numpy(rX.astype(np.float32)).to(torch.bfloat16))
 
 
 def test_operand_of_2gib_takes_the_general_path():
@@ -322,11 +362,11 @@ def test_operand_of_2gib_takes_the_general_path():
 
 
 @pytest.mark.parametrize("proj", range(4))
-def test_block_projection_sampled(proj):
-    """One Transformer block's projections at M = 16384 (QKV, out, up, down), sampled."""
+def test_block_projection_full(proj):
+    """One Transformer block's projections at M = 16384 (QKV, out, up, down): every entry of
+    dX and dW against the oracle, per-element bounds on 64 rows of each."""
     name, k, n = synth.BLOCK_PROJECTIONS[proj]
     case = synth.linear_case(synth.BLOCK_TOKENS, k, n, "bf16", x_std=1.0, w_std=0.02,
                              g_std=1e-4, seed=1 + proj, name=name)
     dX, dW = run(case)
-    assert not torch.isnan(dX).any() and not torch.isnan(dW).any()
-    _sampled_check(case, dX, dW, 2048, proj)
+    check_full_with_bounds(case, dX, dW, bound_rows=64, seed=proj)
