@@ -99,6 +99,25 @@ int lin_bwd(const void *X, const void *W, const void *dY, void *dX, float *dW,
 int lin_bwd_ex(const void *X, const void *W, const void *dY, void *dX, float *dW, float *db,
                int64_t M, int64_t K, int64_t N, int dtype);
 
+/*
+ * lin_bwd_ex_noalloc -- lin_bwd_ex for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops, harnesses
+ * that forbid hipMalloc.  It computes exactly what lin_bwd_ex computes (the
+ * same kernels, splits and summation order, so the same bits), with the same
+ * arguments, sizes and errors, but calls no allocating routine: its
+ * temporaries (the small-M dX split partials and db's row partials) live in a
+ * static device array of 36 MiB (8 Mi + 1 Mi floats) that the library holds on
+ * every device it runs on until the process ends.  The kernels size their
+ * splits to that array, so no size is refused for want of room.  Nothing in it
+ * needs to start at zero: every partial is written before it is read.
+ * All calls on one device share the one array, whatever their stream or
+ * thread: calls that overlap on a device race (unlike lin_bwd_ex, whose
+ * workspace is per stream), so the caller keeps them in one stream order.
+ * The first call on a device looks up the array's device address
+ * (hipGetSymbolAddress); LB_EHIP if that fails.
+ */
+int lin_bwd_ex_noalloc(const void *X, const void *W, const void *dY, void *dX, float *dW,
+                       float *db, int64_t M, int64_t K, int64_t N, int dtype);
 
 /*
  * adamw_step -- one fused pass over n parameters that unscales the gradient

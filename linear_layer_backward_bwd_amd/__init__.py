@@ -37,8 +37,10 @@ def library() -> ctypes.CDLL:
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     lib.lin_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32]
     lib.lin_bwd.restype = i32
-    lib.lin_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32]
-    lib.lin_bwd_ex.restype = i32
+    for name in ("lin_bwd_ex", "lin_bwd_ex_noalloc"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32]
+        fn.restype = i32
     lib.softmax_bwd.argtypes = [vp, vp, vp, i64, i64, i32]
     lib.softmax_bwd.restype = i32
     for name in ("adamw_step", "adamw_step_f16", "adamw_step_bf16"):
@@ -165,10 +167,12 @@ def lin_bwd(X, W, dY, dX=None, dW=None) -> None:
     _check(rc, "lin_bwd")
 
 
-def lin_bwd_ex(X, W, dY, dX=None, dW=None, db=None) -> None:
+def lin_bwd_ex(X, W, dY, dX=None, dW=None, db=None, no_alloc=False) -> None:
     """lin_bwd plus the bias gradient db[n] = Σ_m dY[m,n] (into db, float32 [N]).
 
-    X and W may be None when dX and dW are None (db only).
+    X and W may be None when dX and dW are None (db only).  no_alloc=True calls
+    lin_bwd_ex_noalloc: the same results, temporaries in the library's static array (no
+    device allocation; calls that overlap on one device race).
     """
     import torch
     if dY is None or dY.dim() != 2:
@@ -196,9 +200,10 @@ def lin_bwd_ex(X, W, dY, dX=None, dW=None, db=None) -> None:
         raise ValueError("db must be float32 with %d elements" % N)
     dev = _device_of([X, W, dY, dX, dW, db])
     _use_current_stream(dev)
-    rc = library().lin_bwd_ex(_ptr(X), _ptr(W), _ptr(dY), _ptr(dX), _ptr(dW), _ptr(db), M, K, N,
-                              LB_BF16 if dtype == torch.bfloat16 else LB_F32)
-    _check(rc, "lin_bwd_ex")
+    name = "lin_bwd_ex_noalloc" if no_alloc else "lin_bwd_ex"
+    rc = getattr(library(), name)(_ptr(X), _ptr(W), _ptr(dY), _ptr(dX), _ptr(dW), _ptr(db), M, K, N,
+                                  LB_BF16 if dtype == torch.bfloat16 else LB_F32)
+    _check(rc, name)
 
 
 def _adamw(name, W, grad, m, v, lr, b1, b2, eps, wd, step, inv_scale):

@@ -76,9 +76,42 @@ hipError_t workspace(Workspace &out) {
     return hipSuccess;
 }
 
-// lin_bwd and lin_bwd_ex: the temporaries go to the stream's workspace.
+// ---- static scratch for lin_bwd_ex_noalloc ----------------------------------
+// The temporaries of lin_bwd_ex (small-M dX split partials, then the bias row
+// partials) for callers that cannot allocate, in a file-scope device array of
+// the same capacity as a stream's workspace, so that both entry points choose
+// the same splits (the launchers fit them to the capacity; no size needs
+// more) and produce the same bits.  Each device holds its own copy for the
+// life of the process.  Its host-side name is not a device address: the
+// address comes from hipGetSymbolAddress, once per device with that device
+// current, and only that address is ever passed to a kernel.
+constexpr int64_t kScratchFloats = lb::kDxPartialFloats + lb::kBiasWorkspaceFloats;
+static __device__ __align__(256) float scratch[kScratchFloats];
+std::mutex scratch_mutex;
+std::map<int, float *> scratch_by_device;
+
+hipError_t scratch_address(float **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    auto it = scratch_by_device.find(dev);
+    if (it == scratch_by_device.end()) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        it = scratch_by_device.emplace(dev, static_cast<float *>(p)).first;
+    }
+    *out = it->second;
+    return hipSuccess;
+}
+
+// lin_bwd, lin_bwd_ex and lin_bwd_ex_noalloc: the temporaries go to the
+// stream's workspace, or with `no_alloc` to the static scratch array.
 int lin_bwd_impl(const char *name, const void *X, const void *W, const void *dY, void *dX, float *dW, float *db,
-                 int64_t M, int64_t K, int64_t N, int dtype) {
+                 int64_t M, int64_t K, int64_t N, int dtype, bool no_alloc) {
     tl_error.clear();
     if (dtype != LB_F32 && dtype != LB_BF16)
         return fail(LB_EDTYPE, "%s: dtype %d is not LB_F32 (0) or LB_BF16 (1)", name, dtype);
@@ -113,12 +146,21 @@ int lin_bwd_impl(const char *name, const void *X, const void *W, const void *dY,
     float *dx_partial = nullptr, *bias_partial = nullptr;
     const bool small_dx = dX && dtype == LB_BF16 && M > 0 && M <= 1024 && K > 0 && N > 0;
     if ((db && N > 0) || small_dx) {
-        Workspace ws;
-        hipError_t e = workspace(ws);
-        if (e != hipSuccess)
-            return hip_fail("lin_bwd_ex (workspace)", e);
-        dx_partial = ws.dx_partial;
-        bias_partial = ws.bias_partial;
+        if (no_alloc) {
+            float *p = nullptr;
+            hipError_t e = scratch_address(&p);
+            if (e != hipSuccess)
+                return hip_fail("lin_bwd_ex_noalloc (address of the scratch array)", e);
+            dx_partial = p;
+            bias_partial = p + lb::kDxPartialFloats;
+        } else {
+            Workspace ws;
+            hipError_t e = workspace(ws);
+            if (e != hipSuccess)
+                return hip_fail("lin_bwd_ex (workspace)", e);
+            dx_partial = ws.dx_partial;
+            bias_partial = ws.bias_partial;
+        }
     }
     a.dx_partial = dx_partial;
     a.dx_partial_floats = dx_partial ? lb::kDxPartialFloats : 0;
@@ -189,7 +231,12 @@ extern "C" {
 
 int lin_bwd_ex(const void *X, const void *W, const void *dY, void *dX, float *dW, float *db, int64_t M,
                int64_t K, int64_t N, int dtype) {
-    return lin_bwd_impl(db ? "lin_bwd_ex" : "lin_bwd", X, W, dY, dX, dW, db, M, K, N, dtype);
+    return lin_bwd_impl(db ? "lin_bwd_ex" : "lin_bwd", X, W, dY, dX, dW, db, M, K, N, dtype, false);
+}
+
+int lin_bwd_ex_noalloc(const void *X, const void *W, const void *dY, void *dX, float *dW, float *db,
+                       int64_t M, int64_t K, int64_t N, int dtype) {
+    return lin_bwd_impl("lin_bwd_ex_noalloc", X, W, dY, dX, dW, db, M, K, N, dtype, true);
 }
 
 int lin_bwd(const void *X, const void *W, const void *dY, void *dX, float *dW, int64_t M, int64_t K,

@@ -25,8 +25,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("lin_bwd", "adamw_step", "adamw_step_f16", "adamw_step_bf16", "adamw_step_ex",
                  "grad_norm", "lin_bwd_ex", "softmax_bwd",
-                 "lb_set_stream", "lb_set_lin_bwd_path", "lb_last_error", "lb_version",
-                 "lb_shutdown"):
+                 "lin_bwd_ex_noalloc", "lb_set_stream", "lb_set_lin_bwd_path", "lb_last_error",
+                 "lb_version", "lb_shutdown"):
         assert want in names
 
 
@@ -176,13 +176,16 @@ def test_grad_norm_binding_checks_types():
     (dict(db=FAKE, N=0), 0),                                    # N = 0: nothing to write
     (dict(), 0),                                                # nothing requested
 ])
-def test_lin_bwd_ex_rejects_on_host(args, code):
+@pytest.mark.parametrize("entry", ["lin_bwd_ex", "lin_bwd_ex_noalloc"])
+def test_lin_bwd_ex_rejects_on_host(args, code, entry):
     a = dict(M=8, K=8, N=8, dtype=1, db=NULL)
     a.update(args)
-    rc = lb.library().lin_bwd_ex(NULL, NULL, NULL, NULL, NULL, a["db"], a["M"], a["K"], a["N"],
-                                 a["dtype"])
+    rc = getattr(lb.library(), entry)(NULL, NULL, NULL, NULL, NULL, a["db"], a["M"], a["K"], a["N"],
+                                      a["dtype"])
     assert rc == code
     assert (lb.lb_last_error() != "") == (code != 0)
+    if code and entry == "lin_bwd_ex_noalloc":
+        assert lb.lb_last_error().startswith(entry)
 
 
 def test_lin_bwd_ex_binding_checks():

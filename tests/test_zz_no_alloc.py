@@ -1,0 +1,87 @@
+"""lin_bwd_ex_noalloc (temporaries in the library's static device array) against
+lin_bwd_ex (temporaries in the stream's workspace): the same kernels and splits, so
+the same bits; and both against the oracle's bars.  Two calls in a row, the second
+smaller, so the second reuses the array with the first call's partials still in it.
+Every call goes through the C ABI of liblinbwd.so.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import linear_layer_backward_bwd_amd as lb
+import oracle
+import synth
+from gpu_util import DB_RELF, DW_RELF, DX_RELF, host_f64, relf
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def call(entry, case, with_dx=True, with_dw=True, with_db=True):
+    X, W, G = (t.to(DEV) for t in (case.X, case.W, case.G))
+    dX = torch.full((case.M, case.K), float("nan"), dtype=torch.bfloat16, device=DEV) if with_dx else None
+    dW = torch.full((case.K, case.N), float("nan"), device=DEV) if with_dw else None
+    db = torch.full((case.N,), float("nan"), device=DEV) if with_db else None
+    torch.cuda.synchronize()
+    lib = lb.library()
+    lib.lb_set_stream(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    p = lambda t: None if t is None else t.data_ptr()
+    rc = getattr(lib, entry)(p(X), p(W), p(G), p(dX), p(dW), p(db), case.M, case.K, case.N, lb.LB_BF16)
+    assert rc == 0, lb.lb_last_error()
+    torch.cuda.synchronize()
+    return dX, dW, db
+
+
+def check(case, got, ref):
+    for a, b in zip(got, ref):
+        if a is not None:
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+    Xb, Wb, Gb = synth.bits(case.X), synth.bits(case.W), synth.bits(case.G)
+    rX, rW = oracle.lin_bwd(Xb, Wb, Gb, "bf16")
+    dX, dW, db = got
+    if dX is not None:
+        assert relf(host_f64(dX), rX) <= DX_RELF
+    if dW is not None:
+        assert relf(host_f64(dW), rW) <= DW_RELF
+    if db is not None:
+        assert relf(db.cpu().numpy(), oracle.bias_grad(Gb, "bf16")) <= DB_RELF
+
+
+# (M, K, N): M = 200 sums dX in 16 splits and db in row splits, both through the array;
+# the second call is smaller (M = 40: 4 splits) and reads back only what it wrote
+SHAPES = [(200, 1032, 4104), (40, 520, 1032)]
+
+
+def test_noalloc_matches_lin_bwd_ex_two_calls_in_a_row():
+    for M, K, N in SHAPES:
+        case = synth.linear_case(M, K, N, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=M + N)
+        got = call("lin_bwd_ex_noalloc", case)
+        ref = call("lin_bwd_ex", case)
+        check(case, got, ref)
+
+
+def test_noalloc_db_only_and_dx_only():
+    case = synth.linear_case(300, 264, 2056, "bf16", seed=5)
+    check(case, call("lin_bwd_ex_noalloc", case, with_dx=False, with_dw=False),
+          call("lin_bwd_ex", case, with_dx=False, with_dw=False))
+    case = synth.linear_case(24, 1032, 520, "bf16", seed=6)
+    check(case, call("lin_bwd_ex_noalloc", case, with_dw=False, with_db=False),
+          call("lin_bwd_ex", case, with_dw=False, with_db=False))
+
+
+def test_noalloc_through_the_binding():
+    case = synth.linear_case(64, 520, 1032, "bf16", seed=7)
+    X, W, G = (t.to(DEV) for t in (case.X, case.W, case.G))
+    outs = []
+    for no_alloc in (True, False):
+        dX = torch.empty(case.M, case.K, dtype=torch.bfloat16, device=DEV)
+        dW = torch.empty(case.K, case.N, device=DEV)
+        db = torch.empty(case.N, device=DEV)
+        lb.lin_bwd_ex(X, W, G, dX, dW, db, no_alloc=no_alloc)
+        outs.append((dX, dW, db))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
