@@ -102,6 +102,107 @@ def _sync():
     torch.cuda.synchronize()
 
 
+def lin_bwd_roofs(M, K, N):
+    """Roofline limits of lin_bwd at one shape (TFLOP/s): min(P, I·B) with the pages' ideal
+    traffic b(MK+KN+MN) per product ("GPU 如何训练模型：从算子到 Kernel", section "Roofline"),
+    and with the traffic the call must move at least (bf16 X, W, dY, dX and the fp32 dW)."""
+    flops = lin_bwd_flops(M, K, N)
+    i_pages = ideal_intensity(M, K, N)
+    i_actual = flops / lin_bwd_min_bytes(M, K, N)
+    return {"pages": min(PEAK_BF16_TFLOPS, i_pages * PEAK_HBM_GBPS / 1000.0),
+            "fp32_dw_aware": min(PEAK_BF16_TFLOPS, i_actual * PEAK_HBM_GBPS / 1000.0),
+            "intensity_pages": i_pages, "intensity_actual": i_actual}
+
+
+def cpu_description():
+    """CPU model, logical CPUs this process may use, and physical cores among them."""
+    model, phys = None, set()
+    cur = {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if not line.strip():
+                    if "processor" in cur:
+                        phys.add((cur.get("processor"), cur.get("physical id"), cur.get("core id")))
+                    cur = {}
+                    continue
+                k, _, v = line.partition(":")
+                cur[k.strip()] = v.strip()
+                if k.strip() == "model name" and model is None:
+                    model = v.strip()
+    except OSError:
+        pass
+    allowed = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else set(range(os.cpu_count() or 1))
+    cores = {(p, c) for proc, p, c in phys if proc is not None and int(proc) in allowed and c is not None}
+    return {"cpu_model": model, "logical_cpus_allowed": len(allowed),
+            "physical_cores_allowed": len(cores) or None}
+
+
+CALIB_PATH = os.path.join(ROOT, "linear_layer_backward_bwd_amd", "libcalib.so")
+
+
+def calibrate(reps=10):
+    """What this part sustains: a plain copy, a read-only pass, the AdamW traffic mix without
+    arithmetic (26 B per element, as the AdamW kernel issues it) and back-to-back bf16 MFMAs
+    on random values; HIP events around `reps` launches of each, best of two sizes where the
+    launch shape matters."""
+    import ctypes
+
+    import torch
+    if not os.path.exists(CALIB_PATH):
+        raise RuntimeError("%s is not built (python -m linear_layer_backward_bwd_amd.build)" % CALIB_PATH)
+    lib = ctypes.CDLL(CALIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.calib_copy.argtypes = [vp, vp, i64, vp]
+    lib.calib_read.argtypes = [vp, i64, vp, vp]
+    lib.calib_stream.argtypes = [vp, vp, vp, vp, i64, vp]
+    lib.calib_mfma.argtypes = [i32, i32, vp, vp]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def timed(fn):
+        for _ in range(3):
+            assert fn() == 0
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            assert fn() == 0
+        b.record()
+        _sync()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    out = {}
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    word = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t = timed(lambda: lib.calib_copy(dst.data_ptr(), src.data_ptr(), nbytes, stream))
+    out["copy_gbps"] = round(2 * nbytes / t / 1e9, 1)
+    big = torch.ones(2 * nbytes // 4, dtype=torch.float32, device="cuda")
+    t = timed(lambda: lib.calib_read(big.data_ptr(), 2 * nbytes, word.data_ptr(), stream))
+    out["read_gbps"] = round(2 * nbytes / t / 1e9, 1)
+    del src, dst, big
+    n = 1 << 28
+    W = torch.zeros(n, dtype=torch.float32, device="cuda")
+    m = torch.zeros_like(W)
+    v = torch.zeros_like(W)
+    g = torch.zeros(n, dtype=torch.int16, device="cuda")
+    t = timed(lambda: lib.calib_stream(W.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(), n, stream))
+    out["adamw_mix_stream_gbps"] = round(ADAMW_BYTES_16BIT_GRAD * n / t / 1e9, 1)
+    del W, m, v, g
+    torch.cuda.empty_cache()
+    best = 0.0
+    iters = 4000
+    for blocks in (256, 512, 1024):
+        t = timed(lambda: lib.calib_mfma(blocks, iters, word.data_ptr(), stream))
+        best = max(best, blocks * 4 * iters * 16 * 16384.0 / t / 1e12)
+    out["mfma_bf16_tflops"] = round(best, 1)
+    out["note"] = ("copy: one 16-byte vector per thread; read: 2 GiB once; adamw_mix_stream: reads "
+                   "a 16-bit g and fp32 W, m, v and writes W, m, v per element (26 B) with no "
+                   "arithmetic, 2^28 elements; mfma: v_mfma_f32_16x16x32_bf16 back to back on "
+                   "random bf16 values in registers, best of 1, 2 and 4 waves per SIMD")
+    return out
+
+
 KERNEL_SOURCES = {"k_lin_bwd_mfma": "linear_layer_backward_bwd_amd/csrc/lin_bwd.hip",
                   "k_dw_smallm": "linear_layer_backward_bwd_amd/csrc/lin_bwd.hip",
                   "k_adamw": "linear_layer_backward_bwd_amd/csrc/adamw.hip",
@@ -310,12 +411,22 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
     fl = lin_bwd_flops(M, K, N)
     tf = fl / (ms * 1e-3) / 1e12
     q = lin_bwd_min_bytes(M, K, N)
+    roofs = lin_bwd_roofs(M, K, N)
+    kernel = "k_dw_smallm" if M <= 64 else "k_lin_bwd_mfma"
     return {"M": M, "K": K, "N": N, "ms": round(ms, 5), "tflops": round(tf, 1),
             "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "bound": "hbm" if roofs["pages"] < PEAK_BF16_TFLOPS else "mfma",
+            "roof_pages_tflops": round(roofs["pages"], 1),
+            "frac_of_roof_pages": round(tf / roofs["pages"], 4),
+            "roof_fp32_dw_aware_tflops": round(roofs["fp32_dw_aware"], 1),
+            "frac_of_roof_fp32_dw_aware": round(tf / roofs["fp32_dw_aware"], 4),
             "gbps_alg": round(q / (ms * 1e-3) / 1e9, 1),
-            "intensity_pages": round(ideal_intensity(M, K, N), 2),
+            "frac_of_hbm_peak_alg": round(q / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "bytes_alg": q,
+            "intensity_pages": round(roofs["intensity_pages"], 2),
+            "intensity_actual": round(roofs["intensity_actual"], 2),
             "rotating_sets": nsets, "timing": "GPU time per call, calls queued behind a sleep kernel",
-            "traffic": recorded_traffic("k_dw_smallm", "lin_bwd_M%d_K%d_N%d" % (M, K, N)) if M <= 64 else None}
+            "traffic": recorded_traffic(kernel, "lin_bwd_M%d_K%d_N%d" % (M, K, N))}
 
 
 def bench_adamw(n, steps, warmup, seed):
@@ -471,7 +582,7 @@ def cpu_baseline(cases, opt, target_s=12.0):
     step_flops = sum(lin_bwd_flops(c.M, c.K, c.N) for c in cases)
     step_s = step_flops / gemm_rate + opt.W.numel() / adamw_rate
     return {"value": step_flops / step_s / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", **cpu_description(),
             "sample": ("%d dX + %d dW entries per projection (fp64 dot products on the bf16 inputs) "
                        "and one AdamW step over 2^23 params (scalar fp32), extrapolated to the "
                        "whole step; host GEMM %.2f GFLOP/s, host AdamW %.1f Mparam/s"
@@ -489,10 +600,10 @@ def main(argv=None):
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the M=32 / M=2048 / 2^28-param AdamW figures")
     ap.add_argument("--only", choices=["block", "m32", "m2048", "adamw", "clipped", "bias", "softmax",
-                                       "copycal"],
+                                       "copycal", "calib"],
                     default=None,
                     help="time one workload only (for profiling); copycal = 1 GiB copies for "
-                         "scaling HBM byte counters")
+                         "scaling HBM byte counters; calib = the calibration kernels")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus %d is not supported "
@@ -524,6 +635,9 @@ def main(argv=None):
     if args.only == "copycal":
         print(json.dumps(copy_calibration(args.steps)), flush=True)
         return 0
+    if args.only == "calib":
+        print(json.dumps(calibrate(args.steps)), flush=True)
+        return 0
 
     print("bench: block workload, warmup %d, steps %d" % (args.warmup, args.steps),
           file=sys.stderr, flush=True)
@@ -542,6 +656,16 @@ def main(argv=None):
     del cases, opt
     torch.cuda.empty_cache()
     if not args.no_extra:
+        print("bench: calibration kernels", file=sys.stderr, flush=True)
+        cal = calibrate()
+        out["calibration"] = cal
+        lin = out["parts"]["lin_bwd"]
+        lin["frac_of_measured_mfma_peak"] = round(lin["tflops"] / cal["mfma_bf16_tflops"], 4)
+        out["roofline"]["measured_peak"] = cal["mfma_bf16_tflops"]
+        out["roofline"]["frac_of_measured_peak"] = round(out["roofline"]["achieved"] / cal["mfma_bf16_tflops"], 4)
+        ad = out["parts"]["adamw"]
+        ad["frac_of_measured_copy"] = round(ad["gbps"] / cal["copy_gbps"], 4)
+        ad["frac_of_measured_adamw_mix_stream"] = round(ad["gbps"] / cal["adamw_mix_stream_gbps"], 4)
         print("bench: extra shapes", file=sys.stderr, flush=True)
         out["also"] = {
             "lin_bwd_M32_K4096_N4096": bench_linear(32, 4096, 4096, 50, 5, args.seed),
@@ -551,6 +675,14 @@ def main(argv=None):
             "bias_grad_block": bench_bias(20, 3, args.seed),
             "softmax_bwd_attention": bench_softmax(10, 2, args.seed),
         }
+        for key in ("lin_bwd_M32_K4096_N4096", "lin_bwd_M2048_K4096_N4096"):
+            out["also"][key]["frac_of_measured_mfma_peak"] = round(
+                out["also"][key]["tflops"] / cal["mfma_bf16_tflops"], 4)
+        out["also"]["lin_bwd_M32_K4096_N4096"]["frac_of_measured_copy_alg"] = round(
+            out["also"]["lin_bwd_M32_K4096_N4096"]["gbps_alg"] / cal["copy_gbps"], 4)
+        a2 = out["also"]["adamw_2p28_f16"]
+        a2["frac_of_measured_copy"] = round(a2["gbps"] / cal["copy_gbps"], 4)
+        a2["frac_of_measured_adamw_mix_stream"] = round(a2["gbps"] / cal["adamw_mix_stream_gbps"], 4)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -143,8 +143,8 @@ int lin_bwd_ex_noalloc(const void *X, const void *W, const void *dY, void *dX, f
  *
  * The fp32 arithmetic is done in the order written above, without fused
  * multiply-add contraction, with IEEE division and square root.
- * n = 0 is a no-op.  Any alignment is accepted; 16-byte aligned buffers take
- * the vectorised path.  NaN and infinity propagate (no skip, no detection).
+ * n = 0 is a no-op.  Any alignment of the element types is accepted (one
+ * parameter per thread).  NaN and infinity propagate (no skip, no detection).
  * Errors: LB_EINVAL for n < 0, a NULL buffer with n > 0, step < 1, or b1 / b2
  * outside [0, 1); LB_EHIP when the launch fails.
  */
@@ -179,8 +179,8 @@ int adamw_step_bf16(float *W, const uint16_t *grad, float *m, float *v, int64_t 
  *   w16_dtype   LB_BF16 or LB_F16; ignored when W16 is NULL
  *
  * All pointers are device memory owned by the caller; W16 must not alias the
- * other buffers.  Any alignment is accepted (16-byte aligned buffers take the
- * vector path).  Asynchronous on the thread's stream, like adamw_step.
+ * other buffers.  Any alignment of the element types is accepted.
+ * Asynchronous on the thread's stream, like adamw_step.
  * Errors: those of adamw_step; LB_EDTYPE for another grad_dtype, or a W16
  * with a w16_dtype other than LB_BF16 / LB_F16.
  */

@@ -13,6 +13,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "liblinbwd.so")
 SOURCES = ["api.hip", "lin_bwd.hip", "adamw.hip", "grad_norm.hip", "bias_grad.hip", "softmax_bwd.hip"]
+# measurement only (bench.py): copy / read / AdamW-mix stream and MFMA peak kernels
+CALIB_PATH = os.path.join(HERE, "libcalib.so")
+CALIB_SOURCES = ["calib.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -33,8 +36,9 @@ def hipcc() -> str:
     return path
 
 
-def build(extra_flags=(), out=LIB_PATH, verbose=False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+def build(extra_flags=(), out=LIB_PATH, verbose=False, sources=None) -> str:
+    """Compile liblinbwd.so (or, with `sources`, another library from csrc/)."""
+    srcs = [os.path.join(CSRC, s) for s in (sources or SOURCES)]
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *extra_flags, *srcs, "-o", tmp]
     if verbose:
@@ -44,5 +48,10 @@ def build(extra_flags=(), out=LIB_PATH, verbose=False) -> str:
     return out
 
 
+def build_calib(verbose=False) -> str:
+    return build(out=CALIB_PATH, verbose=verbose, sources=CALIB_SOURCES)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_calib(verbose=True))

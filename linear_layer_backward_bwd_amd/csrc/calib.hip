@@ -1,0 +1,149 @@
+// Calibration kernels for the measurement: what this part sustains for the two
+// bounds the hot path meets, measured beside the spec peaks (HBM 8 TB/s, dense
+// bf16 MFMA 2.5 PFLOP/s).  Built into libcalib.so, used by bench.py only; no
+// entry point of liblinbwd.so calls them.
+//
+// Roofline: an op of F FLOP moving Q bytes cannot finish before max(F/P, Q/B)
+// ("GPU 如何训练模型：从算子到 Kernel", section "Roofline：先判断“算不动”还是
+// “搬不动”"); these kernels measure the P and B that a kernel on this part can
+// reach, so that a kernel's fraction of the spec peak can be read against the
+// fraction of what is reachable.
+//
+//   calib_copy     dst = src, one 16-byte vector per thread over an exact grid
+//   calib_read     reads a buffer once (16-byte vectors), writes nothing in practice
+//   calib_stream   the fused AdamW pass's traffic without its arithmetic: per
+//                  element reads a 16-bit g and fp32 W, m, v, writes W, m, v
+//                  (26 B per element), one element per thread, non-temporal
+//                  loads, plain stores, as the AdamW kernel issues them
+//   calib_mfma     back-to-back v_mfma_f32_16x16x32_bf16 on random bf16 values
+//                  held in registers, 16 independent accumulators per wave
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void k_copy(const u32x4_t *src, u32x4_t *dst, int64_t n16) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n16)
+        dst[i] = __builtin_nontemporal_load(src + i);
+}
+
+__global__ __launch_bounds__(kThreads) void k_read(const u32x4_t *src, int64_t n16, uint32_t *out) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    uint32_t x = 0;
+    if (i < n16) {
+        const u32x4_t v = __builtin_nontemporal_load(src + i);
+        x = v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    // a value no input produces in practice: keeps the loads, writes nothing
+    if (x == 0x9e3779b9u)
+        out[0] = x;
+}
+
+__global__ __launch_bounds__(kThreads) void k_stream(float *W, const uint16_t *g, float *m, float *v, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n)
+        return;
+    const float w = __builtin_nontemporal_load(W + i);
+    const float mm = __builtin_nontemporal_load(m + i);
+    const float vv = __builtin_nontemporal_load(v + i);
+    const uint16_t gg = __builtin_nontemporal_load(g + i);
+    // one operation per output so that every load is used and no store is elided
+    W[i] = w + (float)(gg & 1u);
+    m[i] = mm + 1.0f;
+    v[i] = vv + 1.0f;
+}
+
+__device__ __forceinline__ uint32_t mix(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return x;
+}
+
+// a bf16 pattern with a random sign and mantissa and an exponent within 2^±4
+__device__ __forceinline__ uint16_t rand_bf16(uint32_t h) {
+    return (uint16_t)(((h >> 31) << 15) | ((123u + ((h >> 7) & 7u)) << 7) | (h & 0x7fu));
+}
+
+__global__ __launch_bounds__(kThreads) void k_mfma(int iters, float *out) {
+    const uint32_t seed = (uint32_t)(blockIdx.x * kThreads + threadIdx.x) * 2654435761u;
+    bf16x8_t a, b;
+    for (int j = 0; j < 8; ++j) {
+        a[j] = __builtin_bit_cast(__bf16, rand_bf16(mix(seed + 2 * j)));
+        b[j] = __builtin_bit_cast(__bf16, rand_bf16(mix(seed + 2 * j + 1)));
+    }
+    f32x4_t acc[16];
+    for (int k = 0; k < 16; ++k)
+        acc[k] = f32x4_t{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[k]) : "v"(a), "v"(b));
+    }
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    float s = 0.0f;
+    for (int k = 0; k < 16; ++k)
+        s += acc[k][0] + acc[k][1] + acc[k][2] + acc[k][3];
+    if (s == 1234.5f) // practically never: keeps the MFMAs without a store per lane
+        out[0] = s;
+}
+
+hipError_t grid_for(int64_t n, dim3 &grid) {
+    const int64_t blocks = (n + kThreads - 1) / kThreads;
+    if (blocks > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    grid = dim3((unsigned)(blocks > 0 ? blocks : 1));
+    return hipSuccess;
+}
+
+} // namespace
+
+extern "C" {
+
+// dst, src: device buffers of `bytes` bytes (a multiple of 16), 16-byte aligned.
+int calib_copy(void *dst, const void *src, int64_t bytes, void *stream) {
+    dim3 grid;
+    if (bytes % 16 || grid_for(bytes / 16, grid) != hipSuccess)
+        return -1;
+    hipLaunchKernelGGL(k_copy, grid, dim3(kThreads), 0, (hipStream_t)stream, (const u32x4_t *)src, (u32x4_t *)dst,
+                       bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// src: `bytes` bytes (a multiple of 16); out: one uint32 (not written in practice).
+int calib_read(const void *src, int64_t bytes, uint32_t *out, void *stream) {
+    dim3 grid;
+    if (bytes % 16 || grid_for(bytes / 16, grid) != hipSuccess)
+        return -1;
+    hipLaunchKernelGGL(k_read, grid, dim3(kThreads), 0, (hipStream_t)stream, (const u32x4_t *)src, bytes / 16, out);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// W, m, v: n floats, g: n 16-bit values; all device buffers.
+int calib_stream(float *W, const uint16_t *g, float *m, float *v, int64_t n, void *stream) {
+    dim3 grid;
+    if (grid_for(n, grid) != hipSuccess)
+        return -1;
+    hipLaunchKernelGGL(k_stream, grid, dim3(kThreads), 0, (hipStream_t)stream, W, g, m, v, n);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// blocks x 4 waves, each issuing iters x 16 MFMAs of 16x16x32 (16384 FLOP each);
+// out: one float (not written in practice).
+int calib_mfma(int blocks, int iters, float *out, void *stream) {
+    if (blocks < 1 || iters < 1)
+        return -1;
+    hipLaunchKernelGGL(k_mfma, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+} // extern "C"
