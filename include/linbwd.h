@@ -257,15 +257,21 @@ int lb_set_stream(void *hip_stream);
  *   LB_PATH_SMALL_M  dX on the split-reduction kernel (M <= 1024), dW on the
  *                    small-tile kernel (M <= 256)
  *   LB_PATH_GENERAL  both products on the element-wise kernel
- * A forced MFMA path (TILE, SMALL_M) needs bf16 operands, K and N multiples
- * of 8, 16-byte aligned pointers and operands below 2 GiB, and SMALL_M the M
- * limits above; a call it cannot run fails with LB_EINVAL before anything is
- * enqueued.  Returns LB_OK, or LB_EINVAL for another value.
+ *   LB_PATH_FUSED_SMALL_M  both products in one launch in which each block
+ *                    streams 16 rows of W and writes the same 16 rows of dW
+ *                    (1 <= M <= 64, dX and dW both requested; never chosen
+ *                    automatically: slower than the SMALL_M pair on the
+ *                    shapes measured)
+ * A forced MFMA path (TILE, SMALL_M, FUSED_SMALL_M) needs bf16 operands, K and
+ * N multiples of 8, 16-byte aligned pointers and operands below 2 GiB, and
+ * the M limits above; a call it cannot run fails with LB_EINVAL before
+ * anything is enqueued.  Returns LB_OK, or LB_EINVAL for another value.
  */
 #define LB_PATH_AUTO 0
 #define LB_PATH_TILE 1
 #define LB_PATH_SMALL_M 2
 #define LB_PATH_GENERAL 3
+#define LB_PATH_FUSED_SMALL_M 4
 int lb_set_lin_bwd_path(int path);
 
 /*

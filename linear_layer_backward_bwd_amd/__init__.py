@@ -15,12 +15,12 @@ __all__ = ["lin_bwd", "lin_bwd_ex", "adamw_step", "adamw_step_f16", "adamw_step_
            "adamw_step_ex", "grad_norm", "softmax_bwd", "lb_set_stream", "lb_set_lin_bwd_path",
            "lin_bwd_path", "lb_last_error", "lb_version", "lb_shutdown", "library", "LIB_PATH",
            "LB_F32", "LB_BF16", "LB_F16", "LB_PATH_AUTO", "LB_PATH_TILE", "LB_PATH_SMALL_M",
-           "LB_PATH_GENERAL"]
+           "LB_PATH_GENERAL", "LB_PATH_FUSED_SMALL_M"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinbwd.so")
 LB_F32, LB_BF16, LB_F16 = 0, 1, 2
 LB_OK, LB_EINVAL, LB_EDTYPE, LB_EHIP = 0, -1, -2, -4
-LB_PATH_AUTO, LB_PATH_TILE, LB_PATH_SMALL_M, LB_PATH_GENERAL = 0, 1, 2, 3
+LB_PATH_AUTO, LB_PATH_TILE, LB_PATH_SMALL_M, LB_PATH_GENERAL, LB_PATH_FUSED_SMALL_M = 0, 1, 2, 3, 4
 
 _lib = None
 

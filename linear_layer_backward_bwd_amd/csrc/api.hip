@@ -354,7 +354,7 @@ int lb_set_stream(void *hip_stream) {
 
 int lb_set_lin_bwd_path(int path) {
     tl_error.clear();
-    if (path < LB_PATH_AUTO || path > LB_PATH_GENERAL)
+    if (path < LB_PATH_AUTO || path > LB_PATH_FUSED_SMALL_M)
         return fail(LB_EINVAL, "lb_set_lin_bwd_path: %d is not an LB_PATH_* value", path);
     tl_path = path;
     return LB_OK;

@@ -50,6 +50,7 @@ enum LinPath {
     PATH_TILE = 1,    // the 256x256 MFMA tile kernel for both products
     PATH_SMALL_M = 2, // split-reduction dX (M <= 1024) and small-tile dW (M <= 256)
     PATH_GENERAL = 3, // the element-wise kernel (any dtype, alignment, size)
+    PATH_FUSED_SMALL_M = 4, // both products in one launch streaming W and dW (M <= 64)
 };
 
 struct LinBwdArgs {

@@ -1109,6 +1109,337 @@ __global__ __launch_bounds__(256) void k_dw_smallm(SmallParams p) {
 }
 
 // ------------------------------------------------------------------------
+// M <= 64: both products in one launch (LB_PATH_FUSED_SMALL_M; not chosen
+// automatically, see launch_lin_bwd).  dX[m, k] needs row k of W over the
+// whole reduction, and dW[k, :] is written row by row, so block (row group,
+// split) owns 16 rows k0 .. k0+15: it streams those rows of W once (2N bytes
+// each, non-temporal: read once) together with dY (shared by all blocks, from
+// the caches), accumulates dX[0:M, k0:k0+16] over its part of the reduction
+// and writes dW[k0:k0+16, its columns] chunk by chunk.  The W read stream and
+// the dW write stream (4N bytes per row) then overlap on every CU, where two
+// launches in turn ran them one after the other.  With one split (K >= 4096
+// gives 256 such blocks) dX needs no partial sums; with more, the fp32
+// partials go to part[s][m][k] and are added in split order by
+// k_dx_smallm_reduce.
+//
+// Per chunk of 256 reduction columns n (a ring of kRsSlots slots in LDS, all
+// by DMA: W[k0:k0+16, chunk] and dY[0:16MB, chunk], 512 B per row):
+//   dX: wave w takes the chunk's 32-deep steps 2w, 2w+1 (one W fragment, MB
+//       dY fragments, MB MFMAs each); the four waves' sums are added in wave
+//       order at the end.
+//   dW: wave w takes the chunk's 16-column blocks 4w .. 4w+3: one MFMA per
+//       block and 32 rows of M (the X fragments are read once per block),
+//       passes the 16 x 64 fp32 result through 4 KiB of LDS of its own and
+//       stores four 4-row x 256-byte segments.
+// The waits count the wave's vector-memory operations (DMA and stores, which
+// the counter retires in issue order) issued after the chunk's DMA, so a
+// chunk's stores never wait for later DMA and vice versa.  All LDS accesses in
+// the loop are inline asm: the compiler would otherwise treat them as aliasing
+// the DMA in flight and wait for all of it.
+constexpr int kRsRows = 16;                  // W / dW rows per block
+constexpr int kRsCH = 256;                   // reduction columns per chunk
+constexpr int kRsRowBytes = kRsCH * 2;       // 512 B per LDS row
+constexpr int kRsWBytes = kRsRows * kRsRowBytes;
+constexpr int kRsXBytes = 4096;              // X[0:128, k0:k0+16], 32 B per row
+constexpr int kRsStage = 4096;               // per wave: 16 rows x 64 fp32
+template <int MB> constexpr int rs_slot() { return kRsWBytes + 16 * MB * kRsRowBytes; }
+template <int MB> constexpr int rs_slots() { return MB >= 4 ? 3 : 5; }
+template <int MB> constexpr int rs_ring() { return rs_slots<MB>() * rs_slot<MB>(); }
+template <int MB> constexpr int rs_lds() { return rs_ring<MB>() + kRsXBytes + 4 * kRsStage; }
+constexpr int kRsMaxM = 64;
+
+// 16-byte chunk c of LDS row r sits at c ^ rs_swz(r): the 16 rows a fragment
+// row read serves hit 16 different bank groups, and the rows {0..3, 8..11}
+// (or {4..7, 12..15}) that half a transposing read serves hit 8 different
+// 32-byte segments.
+__device__ __forceinline__ int rs_swz(int r) { return (((r & 3) | (((r >> 3) & 1) << 2)) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ int rs_off(int r, int c) { return r * kRsRowBytes + ((c ^ rs_swz(r)) << 4); }
+
+// s_waitcnt vmcnt(n) for a run-time n (clamped to 63: waiting longer is safe)
+__device__ __forceinline__ void vm_wait(int n) {
+    switch (n > 63 ? 63 : n) {
+#define LB_VMW(i)                                              \
+    case i: asm volatile("s_waitcnt vmcnt(" #i ")" ::: "memory"); break;
+    LB_VMW(0) LB_VMW(1) LB_VMW(2) LB_VMW(3) LB_VMW(4) LB_VMW(5) LB_VMW(6) LB_VMW(7)
+    LB_VMW(8) LB_VMW(9) LB_VMW(10) LB_VMW(11) LB_VMW(12) LB_VMW(13) LB_VMW(14) LB_VMW(15)
+    LB_VMW(16) LB_VMW(17) LB_VMW(18) LB_VMW(19) LB_VMW(20) LB_VMW(21) LB_VMW(22) LB_VMW(23)
+    LB_VMW(24) LB_VMW(25) LB_VMW(26) LB_VMW(27) LB_VMW(28) LB_VMW(29) LB_VMW(30) LB_VMW(31)
+    LB_VMW(32) LB_VMW(33) LB_VMW(34) LB_VMW(35) LB_VMW(36) LB_VMW(37) LB_VMW(38) LB_VMW(39)
+    LB_VMW(40) LB_VMW(41) LB_VMW(42) LB_VMW(43) LB_VMW(44) LB_VMW(45) LB_VMW(46) LB_VMW(47)
+    LB_VMW(48) LB_VMW(49) LB_VMW(50) LB_VMW(51) LB_VMW(52) LB_VMW(53) LB_VMW(54) LB_VMW(55)
+    LB_VMW(56) LB_VMW(57) LB_VMW(58) LB_VMW(59) LB_VMW(60) LB_VMW(61) LB_VMW(62)
+    default: asm volatile("s_waitcnt vmcnt(63)" ::: "memory"); break;
+#undef LB_VMW
+    }
+}
+
+__device__ __forceinline__ void lds_write16(LDS char *p, const f32x4_t &v) {
+    asm volatile("ds_write_b128 %0, %1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ f32x4_t lds_read16(const LDS char *p) {
+    f32x4_t v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(p));
+    return v;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_f(f32x4_t (&v)[N]) {
+    static_assert(N == 4, "four staged quads per round");
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3])::"memory");
+}
+template <int MW>
+__device__ __forceinline__ void lgkm_wait_tr_n(bf16x4_t (&t)[MW][2]) {
+    if constexpr (MW == 1)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0][0]), "+v"(t[0][1])::"memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1])::"memory");
+}
+// A buffer offset (below 2^31) marked out of range when !ok: bit 31 set puts
+// it past any descriptor size used here.  Written as arithmetic, not a
+// select, so the compiler emits no branch around the memory instruction (a
+// branch would skip the zero-filling DMA or add store instructions).
+__device__ __forceinline__ uint32_t oob_unless(bool ok, uint32_t off) {
+    return off | ((uint32_t)!ok << 31);
+}
+
+// Wait until at most N of this wave's LDS reads are in flight, with the two
+// dX steps' fragments (or two column blocks' transposed halves) threaded
+// through the asm so that no MFMA that reads them moves above the wait.
+template <int MB, int N>
+__device__ __forceinline__ void rs_wait_dx(bf16x8_t (&w)[2], bf16x8_t (&g)[2][MB]) {
+    static_assert(N <= 15, "lgkmcnt is a 4-bit counter");
+    if constexpr (MB == 2)
+        asm volatile("s_waitcnt lgkmcnt(%[n])"
+                     : "+v"(w[0]), "+v"(w[1]), "+v"(g[0][0]), "+v"(g[0][1]), "+v"(g[1][0]), "+v"(g[1][1])
+                     : [n] "n"(N)
+                     : "memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(%[n])"
+                     : "+v"(w[0]), "+v"(w[1]), "+v"(g[0][0]), "+v"(g[0][1]), "+v"(g[0][2]), "+v"(g[0][3]),
+                       "+v"(g[1][0]), "+v"(g[1][1]), "+v"(g[1][2]), "+v"(g[1][3])
+                     : [n] "n"(N)
+                     : "memory");
+}
+template <int MW, int N>
+__device__ __forceinline__ void rs_wait_tr(bf16x4_t (&a)[MW][2], bf16x4_t (&b)[MW][2]) {
+    static_assert(N <= 15, "lgkmcnt is a 4-bit counter");
+    if constexpr (MW == 1)
+        asm volatile("s_waitcnt lgkmcnt(%[n])"
+                     : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(b[0][0]), "+v"(b[0][1])
+                     : [n] "n"(N)
+                     : "memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(%[n])"
+                     : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[1][0]), "+v"(a[1][1]), "+v"(b[0][0]), "+v"(b[0][1]),
+                       "+v"(b[1][0]), "+v"(b[1][1])
+                     : [n] "n"(N)
+                     : "memory");
+}
+// 16-byte store through a buffer descriptor, non-temporal: an offset past the
+// descriptor's size writes nothing, so every lane issues the instruction
+__device__ __forceinline__ void store16_nt(__amdgpu_buffer_rsrc_t rs, uint32_t off, const f32x4_t &v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rs, (int)off, 0, 2);
+}
+
+struct FusedParams {
+    const uint16_t *X, *W, *G; // X[M,K], W[K,N], dY[M,N]
+    uint16_t *dX;              // [M,K] bf16
+    float *dW;                 // [K,N] fp32
+    float *part;               // split partials [splits][M][K] (splits > 1)
+    int64_t M, K, N;
+    int64_t split_len;         // reduction columns per split (a multiple of kRsCH)
+    int splits;
+};
+
+template <int MB>
+__device__ __forceinline__ void fused_small_block(const FusedParams &p, int b, LDS char *smem) {
+    // the dW reduction reads dY in 32-row steps: the slot holds at least 32 rows
+    static_assert(MB == 2 || MB == 4, "16 MB rows of dY per slot, 32 or 64");
+    constexpr int kS = rs_slots<MB>();
+    constexpr int kSlot = rs_slot<MB>();
+    constexpr int kMW = MB >= 4 ? 2 : 1;      // 32-row steps of the dW reduction over m
+    constexpr int kWInst = kRsWBytes / 1024 / 4;          // W DMA instructions per wave per chunk
+    constexpr int kGInst = 16 * MB * kRsRowBytes / 1024 / 4; // dY DMA instructions per wave per chunk
+    constexpr int kPerChunk = kWInst + kGInst;
+    const int64_t M = p.M, K = p.K, N = p.N;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int s = b % p.splits;
+    const int64_t k0 = (int64_t)(b / p.splits) * kRsRows;
+    const int64_t n_beg = (int64_t)s * p.split_len;
+    const int64_t n_end = min(N, n_beg + p.split_len);
+    const int nc = (int)((n_end - n_beg + kRsCH - 1) / kRsCH);
+    LDS char *const xs = smem + rs_ring<MB>();
+    LDS char *const stage = xs + kRsXBytes + w * kRsStage;
+
+    // offsets are 32-bit (2KN, 2MN, 2MK < 2^31); rows or columns out of range read zero
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.W, (uint32_t)(2 * K * N));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.G, (uint32_t)(2 * M * N));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X, (uint32_t)(2 * M * K));
+    // dW rows k0 .. k0+15 (a 64N-byte window, so 32-bit offsets); rows past K
+    // lie past the descriptor's size and are not written
+    const __amdgpu_buffer_rsrc_t rdw = make_rsrc(p.dW + k0 * N, (uint32_t)(4 * min<int64_t>(kRsRows, K - k0) * N));
+    auto issue = [&](int j) { // chunk j into slot j % kS
+        LDS char *slot = smem + (j % kS) * kSlot;
+        const int64_t c0 = n_beg + (int64_t)j * kRsCH;
+#pragma unroll
+        for (int i = 0; i < kWInst; ++i) {
+            const int q = w * kWInst + i; // 1 KiB = LDS rows 2q, 2q+1
+            const int r = 2 * q + (lane >> 5);
+            const int64_t n = c0 + 8 * ((lane & 31) ^ rs_swz(r));
+            const bool ok = k0 + r < K && n < n_end;
+            dma16_nt(rw, slot + q * 1024, oob_unless(ok, (uint32_t)(2 * ((k0 + r) * N + n))));
+        }
+#pragma unroll
+        for (int i = 0; i < kGInst; ++i) {
+            const int q = w * kGInst + i;
+            const int r = 2 * q + (lane >> 5);
+            const int64_t n = c0 + 8 * ((lane & 31) ^ rs_swz(r));
+            const bool ok = r < M && n < n_end;
+            dma16(rg, slot + kRsWBytes + q * 1024, oob_unless(ok, (uint32_t)(2 * (r * N + n))));
+        }
+    };
+    {   // X[0:M, k0:k0+16]: wave w's instruction covers rows 32w .. 32w+31
+        const int r = 32 * w + (lane >> 1);
+        const int64_t k = k0 + 8 * (lane & 1);
+        dma16(rx, xs + w * 1024, oob_unless(r < M && k < K, (uint32_t)(2 * (r * K + k))));
+    }
+    for (int j = 0; j < kS - 1 && j < nc; ++j)
+        issue(j);
+
+    f32x4_t accx[MB];
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+        accx[j] = f32x4_t{};
+    bf16x8_t xf[kMW];
+    const int g = lane >> 4, sl = lane & 15;
+    for (int jc = 0; jc < nc; ++jc) {
+        // issued after chunk jc's DMA: the DMA of chunks jc+1 .. jc+kS-2 (those
+        // that exist) and the stores of the last min(jc, kS-1) chunks
+        vm_wait(kPerChunk * max(0, min(jc + kS - 2, nc - 1) - jc) + 4 * min(jc, kS - 1));
+        slab_barrier(); // every wave's DMA of chunk jc landed; chunk jc-1's slot is free
+        if (jc + kS - 1 < nc)
+            issue(jc + kS - 1);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        const LDS char *slot = smem + (jc % kS) * kSlot;
+        const LDS char *gs = slot + kRsWBytes;
+        if (jc == 0) { // the X fragments (A side of dW), rows 32rr + 8g .. +7, column k0 + sl
+#pragma unroll
+            for (int rr = 0; rr < kMW; ++rr) {
+                const int row = 32 * rr + 8 * g + (sl >> 2);
+                const bf16x4_t lo = read_tr<0>(xs + row * 32 + 8 * (sl & 3));
+                const bf16x4_t hi = read_tr<0>(xs + (row + 4) * 32 + 8 * (sl & 3));
+                xf[rr] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+        // All of the chunk's fragment reads go out first, in the order they are
+        // used (LDS reads return in order): dX's, then dW's for column blocks
+        // 0, 1, then 2, 3 of the wave; each group of MFMAs waits only for its own.
+        // dX: steps 2w, 2w+1 (32 columns each); lane: dX[16j + l%16][k0 + 4(l/16) .. +3]
+        bf16x8_t wf[2], gf[2][MB];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int c = 4 * (2 * w + u) + g; // this lane's 16-byte chunk of the step
+            wf[u] = read_rc<0>(slot + rs_off(sl, c));
+#pragma unroll
+            for (int j = 0; j < MB; ++j)
+                gf[u][j] = read_rc<0>(gs + rs_off(16 * j + sl, c));
+        }
+        // dW: column blocks 4w .. 4w+3; lane: dW[k0 + l%16][16nb + 4(l/16) .. +3]
+        bf16x4_t tr[4][kMW][2];
+        auto read_w = [&](int t) {
+            const int col = 16 * (4 * w + t) + 4 * (sl & 3);
+#pragma unroll
+            for (int rr = 0; rr < kMW; ++rr)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = 32 * rr + 8 * g + 4 * h + (sl >> 2);
+                    tr[t][rr][h] = read_tr<0>(gs + rs_off(row, col >> 3) + (col & 7) * 2);
+                }
+        };
+        read_w(0);
+        read_w(1);
+        rs_wait_dx<MB, 4 * kMW>(wf, gf); // all but the 2 x 2 kMW reads of blocks 0, 1
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int j = 0; j < MB; ++j)
+                accx[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], gf[u][j], accx[j], 0, 0, 0);
+        read_w(2);
+        read_w(3);
+        f32x4_t accw[4];
+        auto mfma_w = [&](int t) {
+            accw[t] = f32x4_t{};
+#pragma unroll
+            for (int rr = 0; rr < kMW; ++rr)
+                accw[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_shufflevector(tr[t][rr][0], tr[t][rr][1], 0, 1, 2, 3, 4, 5, 6, 7), xf[rr], accw[t], 0, 0,
+                    0);
+        };
+        rs_wait_tr<kMW, 4 * kMW>(tr[0], tr[1]); // blocks 0, 1 landed; 2, 3 may be in flight
+        mfma_w(0);
+        mfma_w(1);
+        rs_wait_tr<kMW, 0>(tr[2], tr[3]);
+        mfma_w(2);
+        mfma_w(3);
+        // through the wave's staging area: row k (16), 16-byte chunk c at c ^ k
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            lds_write16(stage + sl * 256 + (((4 * t + g) ^ sl) << 4), accw[t]);
+        f32x4_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = 4 * u + g;
+            v[u] = lds_read16(stage + r * 256 + ((sl ^ r) << 4));
+        }
+        lgkm_wait_f(v);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        const int64_t nb0 = n_beg + (int64_t)jc * kRsCH + 64 * w + 4 * sl;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) // N % 8 == 0: nb0 .. nb0+3 all in range
+            store16_nt(rdw, oob_unless(nb0 < n_end, (uint32_t)(4 * ((4 * u + g) * N + nb0))), v[u]);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // dX: the four waves' partial sums, added in wave order; the ring is reused
+    // once every DMA has landed and every wave is past the loop
+    vm_wait(0);
+    slab_barrier();
+    LDS float *red = reinterpret_cast<LDS float *>(smem);
+    constexpr int M16 = 16 * MB;
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+        *reinterpret_cast<LDS f32x4_t *>(red + ((w * M16 + 16 * j + sl) * 16 + 4 * g)) = accx[j];
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < M16 * 4) {
+        const int m = t >> 2, kq = t & 3;
+        f32x4_t a = *reinterpret_cast<const LDS f32x4_t *>(red + (m * 16 + 4 * kq));
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww)
+            a += *reinterpret_cast<const LDS f32x4_t *>(red + ((ww * M16 + m) * 16 + 4 * kq));
+        const int64_t k = k0 + 4 * kq;
+        if (m < M && k < K) { // K % 8 == 0: k .. k+3 all in range
+            if (p.splits == 1) {
+                const u32x2_t pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+                *reinterpret_cast<u32x2_t *>(p.dX + m * K + k) = pk;
+            } else {
+                *reinterpret_cast<f32x4_t *>(p.part + ((int64_t)s * M + m) * K + k) = a;
+            }
+        }
+    }
+}
+
+template <int MB>
+__global__ __launch_bounds__(256, 1) void k_lin_bwd_fused_small(FusedParams p) {
+    static_assert(rs_lds<MB>() <= 160 * 1024, "LDS");
+    static_assert(4 * 16 * MB * 16 * 4 <= rs_ring<MB>(), "the dX sums fit in the ring");
+    __shared__ __attribute__((aligned(1024))) char smem_raw[rs_lds<MB>()];
+    fused_small_block<MB>(p, blockIdx.x, (LDS char *)smem_raw);
+}
+
+// ------------------------------------------------------------------------
 // SIMT fallback: any alignment, any sizes; fp32 or bf16 operands.
 // ------------------------------------------------------------------------
 struct SimtJob {
@@ -1203,6 +1534,59 @@ TileJob make_tile_job(int kind, const void *a, const void *b, void *c, int64_t I
     return j;
 }
 
+// Both products for M <= 64 in one launch (plus, with several splits of the
+// reduction, the launch that adds the dX partials in split order).
+bool fused_small_eligible(const LinBwdArgs &a, bool need_dx, bool need_dw) {
+    // dW rows of one block are addressed through a 64N-byte buffer window
+    return need_dx && need_dw && a.M >= 1 && a.M <= kRsMaxM && a.N > 0 && 64 * a.N < ((int64_t)1 << 31);
+}
+
+hipError_t launch_fused_small(const LinBwdArgs &a, hipStream_t s) {
+    FusedParams fp{};
+    fp.X = static_cast<const uint16_t *>(a.X);
+    fp.W = static_cast<const uint16_t *>(a.W);
+    fp.G = static_cast<const uint16_t *>(a.dY);
+    fp.dX = static_cast<uint16_t *>(a.dX);
+    fp.dW = a.dW;
+    fp.M = a.M;
+    fp.K = a.K;
+    fp.N = a.N;
+    // splits of the reduction: toward 256 blocks (one per CU), each a whole
+    // number of chunks, at most kDxsMaxSplits, partials within the workspace
+    const int64_t rblocks = (a.K + kRsRows - 1) / kRsRows;
+    const int64_t chunks = (a.N + kRsCH - 1) / kRsCH;
+    int64_t splits = std::min(chunks, std::max<int64_t>(1, (256 + rblocks - 1) / rblocks));
+    splits = std::min<int64_t>(splits, kDxsMaxSplits);
+    splits = a.dx_partial ? std::min(splits, a.dx_partial_floats / (a.M * a.K)) : 1;
+    splits = std::max<int64_t>(splits, 1);
+    const int64_t split_len = (chunks + splits - 1) / splits * kRsCH;
+    splits = (a.N + split_len - 1) / split_len;
+    fp.split_len = split_len;
+    fp.splits = (int)splits;
+    fp.part = a.dx_partial;
+    const int64_t blocks = rblocks * splits;
+    if (blocks > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)blocks);
+    if (a.M <= 32) // rows M .. 31 of the dY slot read zero
+        hipLaunchKernelGGL(k_lin_bwd_fused_small<2>, grid, dim3(256), 0, s, fp);
+    else
+        hipLaunchKernelGGL(k_lin_bwd_fused_small<4>, grid, dim3(256), 0, s, fp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1)
+        return e;
+    SmallParams sp{};
+    sp.dX = fp.dX;
+    sp.part = fp.part;
+    sp.M = a.M;
+    sp.K = a.K;
+    sp.N = a.N;
+    sp.splits = (int)splits;
+    const int64_t quads = a.M * a.K / 4;
+    hipLaunchKernelGGL(k_dx_smallm_reduce, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, sp);
+    return hipGetLastError();
+}
+
 hipError_t launch_simt(const LinBwdArgs &a, bool need_dx, bool need_dw, hipStream_t s) {
     SimtParams p{};
     int nj = 0;
@@ -1252,7 +1636,7 @@ const char *lin_bwd_path_refusal(const LinBwdArgs &a) {
     const bool need_dw = a.dW != nullptr && a.K > 0 && a.N > 0;
     if (!need_dx && !need_dw)
         return nullptr;
-    if (a.path != PATH_TILE && a.path != PATH_SMALL_M)
+    if (a.path != PATH_TILE && a.path != PATH_SMALL_M && a.path != PATH_FUSED_SMALL_M)
         return "unknown path";
     if (!mfma_eligible(a, need_dx, need_dw))
         return "the MFMA kernels need bf16 operands, K and N multiples of 8, 16-byte aligned pointers "
@@ -1263,6 +1647,9 @@ const char *lin_bwd_path_refusal(const LinBwdArgs &a) {
         if (need_dw && a.M > kSmallMaxM)
             return "the small-M dW kernel takes M <= 256";
     }
+    if (a.path == PATH_FUSED_SMALL_M && !fused_small_eligible(a, need_dx, need_dw))
+        return "the fused small-M kernel computes both products (dX and dW requested), with "
+               "1 <= M <= 64, N > 0 and 64 N < 2^31";
     return nullptr;
 }
 
@@ -1276,6 +1663,12 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
 
     // the small-M kernels skip the empty sums (N = 0 for dX, M = 0 for dW),
     // which the tile kernel writes as zeros
+    // the fused small-M kernel runs when asked for: measured against the two
+    // launches below it was 5% slower at K = N = 4096 (M = 1 .. 32) and 20-25%
+    // slower with K or N = 16384; its one 140 KiB block per CU leaves each
+    // chunk's LDS round trips and barrier unhidden
+    if (a.path == PATH_FUSED_SMALL_M)
+        return launch_fused_small(a, s);
     bool small_dx = need_dx && a.N > 0 && a.M <= kSmallMaxDxM;
     bool small_dw = need_dw && a.M > 0 && a.M <= kSmallMaxM;
     if (a.path == PATH_TILE)

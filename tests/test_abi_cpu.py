@@ -230,10 +230,13 @@ def test_softmax_bwd_binding_checks():
         lb.softmax_bwd(p.t(), p.t())
 
 
-@pytest.mark.parametrize("path", [-1, 4, 99])
+@pytest.mark.parametrize("path", [-1, 5, 99])
 def test_set_lin_bwd_path_rejects_unknown_values(path):
-    assert lb.library().lb_set_lin_bwd_path(path) == -1
-    assert "LB_PATH" in lb.lb_last_error()
+    try:
+        assert lb.library().lb_set_lin_bwd_path(path) == -1
+        assert "LB_PATH" in lb.lb_last_error()
+    finally:
+        lb.library().lb_set_lin_bwd_path(lb.LB_PATH_AUTO)
 
 
 # (path, M, K, N, dtype, X, W, dY, dX, dW): forced paths that cannot run the call are refused
@@ -251,6 +254,9 @@ ODD = ctypes.c_void_p(4098)
     (lb.LB_PATH_TILE, 1 << 17, 1 << 14, 8, 1, (P16, P32, P48, P64, NULL)),  # dX of 4 GiB
     (lb.LB_PATH_SMALL_M, 1025, 64, 64, 1, (P16, P32, P48, P64, NULL)),   # dX: M <= 1024 only
     (lb.LB_PATH_SMALL_M, 257, 64, 64, 1, (P16, P32, P48, NULL, P64)),    # dW: M <= 256 only
+    (lb.LB_PATH_FUSED_SMALL_M, 65, 64, 64, 1, (P16, P32, P48, P64, P16)),  # M <= 64 only
+    (lb.LB_PATH_FUSED_SMALL_M, 32, 64, 64, 1, (P16, P32, P48, P64, NULL)),  # needs dX and dW
+    (lb.LB_PATH_FUSED_SMALL_M, 32, 64, 1 << 25, 1, (P16, P32, P48, P64, P16)),  # 64 N < 2^31
 ])
 def test_forced_path_refused_on_host(path, M, K, N, dtype, ptrs):
     lib = lb.library()

@@ -23,7 +23,14 @@ from gpu_util import (DB_RELF, DW_RELF, DX_RELF, NORM_ULP, abs_bits, assert_with
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-PATHS = {"tile": lb.LB_PATH_TILE, "small_m": lb.LB_PATH_SMALL_M, "general": lb.LB_PATH_GENERAL}
+PATHS = {"tile": lb.LB_PATH_TILE, "small_m": lb.LB_PATH_SMALL_M, "general": lb.LB_PATH_GENERAL,
+         "fused_small_m": lb.LB_PATH_FUSED_SMALL_M}
+
+
+def runs_on(name, M):
+    """Whether a forced path takes this M with both outputs requested (dW on the small-M
+    path needs M <= 256; the fused path needs M <= 64)."""
+    return not ((name == "small_m" and M > 256) or (name == "fused_small_m" and M > 64))
 
 
 def run_path(case, path, need_dx=True, need_dw=True):
@@ -42,9 +49,11 @@ def int_case(M, K, N, seed):
     return synth.LinearCase(M, K, N, "bf16", mk(M, K), mk(K, N), mk(M, N))
 
 
-# M <= 256 runs every product on every path; 256 < M <= 1024 runs dX only on the small-M path
-CROSS_SHAPES = [(1, 264, 520), (32, 1032, 2056), (64, 520, 264), (100, 264, 1032),
-                (256, 1032, 520), (384, 520, 1032), (1024, 264, 520)]
+# M <= 256 runs every product on every path; 256 < M <= 1024 runs dX only on the small-M
+# path; M <= 64 also on the fused path (K = 264 / 520: a partial last group of 16 rows;
+# N = 264 / 2056: a partial last chunk of 256 columns; N = 520 with K = 264: several splits)
+CROSS_SHAPES = [(1, 264, 520), (17, 4104, 264), (32, 1032, 2056), (48, 264, 4104), (64, 520, 264),
+                (100, 264, 1032), (256, 1032, 520), (384, 520, 1032), (1024, 264, 520)]
 
 
 @pytest.mark.parametrize("M,K,N", CROSS_SHAPES)
@@ -54,7 +63,9 @@ def test_each_path_meets_the_bars(M, K, N):
     aX, aW, aG = (abs_bits(synth.bits(t), "bf16") for t in (case.X, case.W, case.G))
     SX = oracle.lin_bwd(aX, aW, aG, "bf16")
     for name, path in PATHS.items():
-        need_dw = not (name == "small_m" and M > 256)
+        if name == "fused_small_m" and M > 64:
+            continue
+        need_dw = runs_on(name, M)
         dX, dW = run_path(case, path, need_dw=need_dw)
         e = relf(host_f64(dX), rX)
         assert e <= DX_RELF, "%s dX relF %.3g" % (name, e)
@@ -66,13 +77,16 @@ def test_each_path_meets_the_bars(M, K, N):
             assert_within_bound(host_f64(dW), rW, SX[1], M, False, name + " dW", sequential=seq)
 
 
-@pytest.mark.parametrize("M,K,N", [(48, 264, 2056), (200, 1032, 520), (700, 264, 1032)])
+@pytest.mark.parametrize("M,K,N", [(48, 264, 2056), (64, 4096, 1032), (200, 1032, 520),
+                                   (700, 264, 1032)])
 def test_paths_agree_bitwise_on_integer_inputs(M, K, N):
     case = int_case(M, K, N, seed=M)
     outs = {}
     for name, path in PATHS.items():
-        outs[name] = run_path(case, path, need_dw=not (name == "small_m" and M > 256))
-    for name in ("small_m", "general"):
+        if name == "fused_small_m" and M > 64:
+            continue
+        outs[name] = run_path(case, path, need_dw=runs_on(name, M))
+    for name in [n for n in outs if n != "tile"]:
         assert torch.equal(outs[name][0].view(torch.int16), outs["tile"][0].view(torch.int16)), name
         if outs[name][1] is not None:
             assert torch.equal(outs[name][1], outs["tile"][1]), name
