@@ -383,15 +383,15 @@ def hold_queue(ms):
 
 def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
     """lin_bwd alone at one shape; rotates over buffer sets larger than the 256 MB MALL.
-    The timed calls are queued behind a sleep kernel (hold_queue), so each call's HIP
-    events measure the GPU's time for it."""
+    The timed calls are queued behind a sleep kernel (hold_queue), so that the events
+    around them measure the GPU's time, not the host's launch latency."""
     import torch
 
     import linear_layer_backward_bwd_amd as lb
     import synth
     dev = "cuda"
     one = 2 * (M * K + K * N + M * N) + 2 * M * K + 4 * K * N
-    nsets = max(1, min(16, -(-rotate_bytes // one)))
+    nsets = max(1, min(16, -(-rotate_bytes // one)))     # one set when it exceeds the MALL anyway
     sets = []
     for i in range(nsets):
         c = synth.linear_case(M, K, N, "bf16", seed=seed + i, device=dev)
@@ -400,14 +400,28 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
     for i in range(warmup):
         c, dX, dW = sets[i % nsets]
         lb.lin_bwd(c.X, c.W, c.G, dX, dW)
-    timer = Timer(["lin_bwd"])
+    # back to back: one event pair around `steps` calls queued behind a sleep kernel
+    timer = Timer(["batch"])
+    _sync()
+    hold_queue(steps * 0.1 + 2.0)
+
+    def calls():
+        for i in range(steps):
+            c, dX, dW = sets[i % nsets]
+            lb.lin_bwd(c.X, c.W, c.G, dX, dW)
+    timer.run("batch", calls)
+    timer.collect()
+    ms = timer.ms["batch"] / steps
+    # the same calls with an event pair around each (the event commands between
+    # consecutive calls add their own time)
+    per = Timer(["lin_bwd"])
     _sync()
     hold_queue(steps * 0.1 + 2.0)
     for i in range(steps):
         c, dX, dW = sets[i % nsets]
-        timer.run("lin_bwd", lambda: lb.lin_bwd(c.X, c.W, c.G, dX, dW))
-    timer.collect()
-    ms = timer.ms["lin_bwd"] / steps
+        per.run("lin_bwd", lambda: lb.lin_bwd(c.X, c.W, c.G, dX, dW))
+    per.collect()
+    ms_events = per.ms["lin_bwd"] / steps
     fl = lin_bwd_flops(M, K, N)
     tf = fl / (ms * 1e-3) / 1e12
     q = lin_bwd_min_bytes(M, K, N)
@@ -425,7 +439,10 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
             "bytes_alg": q,
             "intensity_pages": round(roofs["intensity_pages"], 2),
             "intensity_actual": round(roofs["intensity_actual"], 2),
-            "rotating_sets": nsets, "timing": "GPU time per call, calls queued behind a sleep kernel",
+            "ms_with_event_pair_per_call": round(ms_events, 5),
+            "rotating_sets": nsets,
+            "timing": "GPU time per call: `steps` calls back to back behind a sleep kernel, one "
+                      "event pair around them all",
             "traffic": recorded_traffic(kernel, "lin_bwd_M%d_K%d_N%d" % (M, K, N))}
 
 
@@ -670,6 +687,9 @@ def main(argv=None):
         out["also"] = {
             "lin_bwd_M32_K4096_N4096": bench_linear(32, 4096, 4096, 50, 5, args.seed),
             "lin_bwd_M2048_K4096_N4096": bench_linear(2048, 4096, 4096, 50, 5, args.seed),
+            # the down projection at 65536 tokens: X and dX of 2 GiB each
+            "lin_bwd_M65536_K16384_N4096": bench_linear(65536, 16384, 4096, 3, 1, args.seed,
+                                                        rotate_bytes=0),
             "adamw_2p28_f16": bench_adamw(1 << 28, 10, 2, args.seed),
             "grad_norm_adamw_ex_2p28_f16": bench_clipped_step(1 << 28, 10, 2, args.seed),
             "bias_grad_block": bench_bias(20, 3, args.seed),

@@ -89,7 +89,6 @@ struct TileJob {
     void *c;           // output, row-major [I, J], leading dim J
     int64_t I, J, R;   // output rows, cols, reduction length
     int64_t lda, ldb;  // leading dims of a and b in elements
-    uint32_t a_bytes, b_bytes; // operand sizes (each < 2 GiB on this path)
     int tiles_i, tiles_j, ntiles;
     int kind;          // JOB_DX: RC operands, bf16 out; JOB_DW: OC operands, fp32 out
     // k rotation (slabs): the tile at (ti, tj) walks the slabs starting at
@@ -113,6 +112,29 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, LDS char *dst, 
 // The same for data read once: the non-temporal cache policy (aux bit 1).
 __device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t rs, LDS char *dst, uint32_t off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS void *)dst, 16, (int)off, 0, 0, 2);
+}
+
+// A buffer offset (below 2^31) marked out of range when !ok: bit 31 set puts
+// it past any descriptor size used here.  Written as arithmetic, not a
+// select, so the compiler emits no branch around the memory instruction (a
+// branch would skip a zero-filling DMA, or duplicate a store).
+__device__ __forceinline__ uint32_t oob_unless(bool ok, uint32_t off) {
+    return off | ((uint32_t)!ok << 31);
+}
+
+// Output stores (never re-read by the kernel that writes them): 16 bytes
+// through a buffer descriptor, so that out-of-range lanes are dropped by the
+// hardware without a branch, non-temporal.  (A store-only probe wrote 64 MiB
+// faster with the sc1 policy than non-temporal, 10.2 vs 11.1 us, but in the
+// kernels sc1 was slower: M = 2048 123.7 vs 119.1 us, the block's projections
+// 1390 vs 1413 TFLOP/s, M = 32 24.3 vs 22.7 us, A/B in one process.)
+#ifndef LB_OUT_AUX
+#define LB_OUT_AUX 2 // nt
+#endif
+template <typename T>
+__device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t rs, uint32_t off, const T &v) {
+    static_assert(sizeof(T) == 16, "16-byte stores");
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rs, (int)off, 0, LB_OUT_AUX);
 }
 
 // Per-lane DMA source offsets of an OC slab, fixed for a tile.  Instruction p
@@ -314,13 +336,16 @@ __device__ __forceinline__ void store_quadrant(const f32x4_t (&acc)[kFrags][kFra
                 v[q] = *reinterpret_cast<const LDS u32x4_t *>(reg + r * 256 + ((k ^ (r & 15)) << 4));
             }
             __builtin_amdgcn_sched_barrier(0); // all eight reads before the first store
+            // the round's 32 rows from column jb0 on; rows past I lie past the size
+            const int64_t i0 = ib + 32 * h;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<uint16_t *>(jb.c) + i0 * jb.J + jb0,
+                                                        (uint32_t)(2 * max<int64_t>(0, min<int64_t>(32, jb.I - i0)) * jb.J));
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int r = 4 * q + (lane >> 4);
-                const int k = lane & 15;
-                const int64_t i = ib + 32 * h + r, j = jb0 + 8 * k;
-                if (FULL || (i < jb.I && j < jb.J)) // J % 8 == 0: j..j+7 all in range
-                    __builtin_nontemporal_store(v[q], reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(jb.c) + i * jb.J + j));
+                const int k = lane & 15; // J % 8 == 0: columns j..j+7 all in or all out
+                const uint32_t off = (uint32_t)(2 * (r * jb.J + 8 * k));
+                store_out(rs, FULL ? off : oob_unless(jb0 + 8 * k < jb.J, off), v[q]);
             }
         }
     } else {
@@ -341,13 +366,15 @@ __device__ __forceinline__ void store_quadrant(const f32x4_t (&acc)[kFrags][kFra
                 v[q] = *reinterpret_cast<const LDS f32x4_t *>(reg + r * 512 + ((k ^ r) << 4));
             }
             __builtin_amdgcn_sched_barrier(0); // all eight reads before the first store
+            const int64_t i0 = ib + 16 * x;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<float *>(jb.c) + i0 * jb.J + jb0,
+                                                        (uint32_t)(4 * max<int64_t>(0, min<int64_t>(16, jb.I - i0)) * jb.J));
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int r = 2 * q + (lane >> 5);
                 const int k = lane & 31;
-                const int64_t i = ib + 16 * x + r, j = jb0 + 4 * k;
-                if (FULL || (i < jb.I && j < jb.J))
-                    __builtin_nontemporal_store(v[q], reinterpret_cast<f32x4_t *>(static_cast<float *>(jb.c) + i * jb.J + j));
+                const uint32_t off = (uint32_t)(4 * (r * jb.J + 4 * k));
+                store_out(rs, FULL ? off : oob_unless(jb0 + 4 * k < jb.J, off), v[q]);
             }
         }
     }
@@ -382,16 +409,16 @@ __device__ __forceinline__ int frag_off_rcp(int ob, int lane, int h) {
 }
 // DMA instruction p of wave w fills pair rows 8q .. 8q+7, q = 8w + p; lane l
 // fetches logical chunk (l & 7) ^ swz_rcp(row) of row 8q + l/8.  Offset
-// relative to the pair's first r; rows outside the operand (or, for the
-// partial last pair, r >= R) read zero.
+// relative to the tile's first operand row and the pair's first r (so it
+// stays below 2^31 for operands of any size: 256 rows of ld < 2^22); rows
+// outside the operand (or, for the partial last pair, r >= R) read zero.
 __device__ __forceinline__ uint32_t dma_rcp_off(int p, int64_t ld, int64_t O, int64_t o0, int w, int lane,
                                                 int64_t k0 = 0, int64_t R = -1) {
     const int row = (w * kDmaPerOpPair + p) * 8 + (lane >> 3);
     const int lc = (lane & 7) ^ swz_rcp(row);
-    const int64_t o = o0 + row;
     const int64_t k = k0 + 8 * lc;
-    const bool ok = o < O && (R < 0 || k < R);
-    return ok ? (uint32_t)((o * ld + (R < 0 ? 0 : k0) + 8 * lc) * 2) : kOOB;
+    const bool ok = o0 + row < O && (R < 0 || k < R);
+    return oob_unless(ok, (uint32_t)((row * ld + (R < 0 ? 0 : k0) + 8 * lc) * 2));
 }
 
 // dX tile.  Slab t lives in pair t/2, ring slot (t/2)%2, half t%2.  During
@@ -444,6 +471,11 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
     // rotation of the reduction order (see TileJob), in whole pairs
     const int rotp = ptail || npair == 0 ? 0 : ((jb.rot * ((tj >> 1) & 3)) >> 1) % npair;
     LDS char *const wdst = smem + w * kDmaPerOpPair * 1024;
+    // the tile's operand rows: windows of at most 256 rows (2 * 256 * ld < 2^31)
+    const uint16_t *const a_t = jb.a + i0 * jb.lda;
+    const uint16_t *const b_t = jb.b + j0 * jb.ldb;
+    const uint32_t a_win = (uint32_t)(2 * min<int64_t>(kTile, jb.I - i0) * jb.lda);
+    const uint32_t b_win = (uint32_t)(2 * min<int64_t>(kTile, jb.J - j0) * jb.ldb);
 
     struct PairSrc {
         __amdgpu_buffer_rsrc_t a, b;
@@ -458,8 +490,8 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
         q += rotp;
         q = q >= npair ? q - npair : q;
         const int64_t k0 = (int64_t)q * 64;
-        r.a = make_rsrc(jb.a + k0, jb.a_bytes - (uint32_t)(2 * k0));
-        r.b = make_rsrc(jb.b + k0, jb.b_bytes - (uint32_t)(2 * k0));
+        r.a = make_rsrc(a_t + k0, a_win - (uint32_t)(2 * k0));
+        r.b = make_rsrc(b_t + k0, b_win - (uint32_t)(2 * k0));
         return r;
     };
     auto dma = [&](const PairSrc &src, int q, int op, int p, bool tail) {
@@ -467,9 +499,9 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
         if (tail) {
             const int64_t k0 = (int64_t)q * 64;
             if (op == 0)
-                dma16(make_rsrc(jb.a, jb.a_bytes), st, dma_rcp_off(p, jb.lda, jb.I, i0, w, lane, k0, R));
+                dma16(make_rsrc(a_t, a_win), st, dma_rcp_off(p, jb.lda, jb.I, i0, w, lane, k0, R));
             else
-                dma16(make_rsrc(jb.b, jb.b_bytes), st, dma_rcp_off(p, jb.ldb, jb.J, j0, w, lane, k0, R));
+                dma16(make_rsrc(b_t, b_win), st, dma_rcp_off(p, jb.ldb, jb.J, j0, w, lane, k0, R));
         } else {
             dma16(op == 0 ? src.a : src.b, st, op == 0 ? va[p] : vb[p]);
         }
@@ -626,9 +658,10 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
         }
         s += rot;
         s = s >= nslab ? s - nslab : s;
-        const int64_t r0 = (int64_t)s * kBK;
-        r.a = make_rsrc(jb.a + s * step_a, (uint32_t)(2 * (jb.R - r0) * jb.lda));
-        r.b = make_rsrc(jb.b + s * step_b, (uint32_t)(2 * (jb.R - r0) * jb.ldb));
+        // the slab's rows only (32 rows of ld < 2^25: below 2^31 bytes)
+        const int64_t rows = min<int64_t>(kBK, jb.R - (int64_t)s * kBK);
+        r.a = make_rsrc(jb.a + s * step_a, (uint32_t)(2 * rows * jb.lda));
+        r.b = make_rsrc(jb.b + s * step_b, (uint32_t)(2 * rows * jb.ldb));
         return r;
     };
     // DMA instruction p of operand op for slab s
@@ -844,7 +877,7 @@ __device__ __forceinline__ void dw_small_block(const SmallParams &p, int b, LDS 
     auto issue = [&](int s) { // slab s into slot s % 2: 5 DMA instructions per wave
         LDS char *slot = smem + (s & 1) * kDwsSlot;
         const int64_t r0 = 32 * (int64_t)s;
-        const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.G + r0 * N, (uint32_t)(2 * (M - r0) * N));
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.G + r0 * N, (uint32_t)(2 * min<int64_t>(32, M - r0) * N));
 #pragma unroll
         for (int q = 0; q < kDmaPerOp; ++q)
             dma16(rg, slot + (w * kDmaPerOp + q) * 1024, dma_oc_off(q, N, N, n0, w, lane));
@@ -895,7 +928,11 @@ __device__ __forceinline__ void dw_small_block(const SmallParams &p, int b, LDS 
     }
 
     // epilogue: round q covers columns 64q .. 64q+63 of the wave's 16 rows;
-    // 16-byte chunk c of staging row r sits at chunk c ^ r
+    // 16-byte chunk c of staging row r sits at chunk c ^ r.  The wave's rows
+    // are one buffer window from column n0 on (rows past K lie past its size).
+    const int64_t kw = k0 + 16 * w;
+    const __amdgpu_buffer_rsrc_t rdw =
+        make_rsrc(p.dW + kw * N + n0, (uint32_t)(4 * max<int64_t>(0, min<int64_t>(16, K - kw)) * N));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
@@ -907,9 +944,8 @@ __device__ __forceinline__ void dw_small_block(const SmallParams &p, int b, LDS 
         for (int t = 0; t < 4; ++t) {
             const int r = 4 * t + g, c = sl;
             const f32x4_t v = *reinterpret_cast<const LDS f32x4_t *>(stage + r * 256 + ((c ^ r) << 4));
-            const int64_t k = k0 + 16 * w + r, n = n0 + 64 * q + 4 * c;
-            if (k < K && n < N) // N % 8 == 0: n .. n+3 all in range
-                __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t *>(p.dW + k * N + n));
+            const int nl = 64 * q + 4 * c; // N % 8 == 0: n .. n+3 all in range or all out
+            store_out(rdw, oob_unless(n0 + nl < N, (uint32_t)(4 * (r * N + nl))), v);
         }
     }
 }
@@ -979,8 +1015,9 @@ __device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS 
     const int nc = (int)((n_end - n_beg + kCH - 1) / kCH);
     // W rows from k0 on, and dY; offsets are 32-bit (2KN, 2MN < 2^31) and
     // rows or columns out of range read zero through kOOB
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.W + k0 * N, (uint32_t)(2 * (K - k0) * N));
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.G + m0 * N, (uint32_t)(2 * (M - m0) * N));
+    // windows: the block's 64 rows of W and 16 MB rows of dY (offsets below 2^31 for N < 2^22)
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.W + k0 * N, (uint32_t)(2 * min<int64_t>(64, K - k0) * N));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.G + m0 * N, (uint32_t)(2 * min<int64_t>(16 * MB, M - m0) * N));
     const int lrow = lane / kCPR, lchunk = lane % kCPR; // this lane's row and chunk within an instruction
     auto issue = [&](int j) { // chunk j into slot j % kS
         const int64_t c0 = n_beg + (int64_t)j * kCH;
@@ -1193,14 +1230,6 @@ __device__ __forceinline__ void lgkm_wait_tr_n(bf16x4_t (&t)[MW][2]) {
     else
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1])::"memory");
 }
-// A buffer offset (below 2^31) marked out of range when !ok: bit 31 set puts
-// it past any descriptor size used here.  Written as arithmetic, not a
-// select, so the compiler emits no branch around the memory instruction (a
-// branch would skip the zero-filling DMA or add store instructions).
-__device__ __forceinline__ uint32_t oob_unless(bool ok, uint32_t off) {
-    return off | ((uint32_t)!ok << 31);
-}
-
 // Wait until at most N of this wave's LDS reads are in flight, with the two
 // dX steps' fragments (or two column blocks' transposed halves) threaded
 // through the asm so that no MFMA that reads them moves above the wait.
@@ -1234,11 +1263,6 @@ __device__ __forceinline__ void rs_wait_tr(bf16x4_t (&a)[MW][2], bf16x4_t (&b)[M
                      : [n] "n"(N)
                      : "memory");
 }
-// 16-byte store through a buffer descriptor, non-temporal: an offset past the
-// descriptor's size writes nothing, so every lane issues the instruction
-__device__ __forceinline__ void store16_nt(__amdgpu_buffer_rsrc_t rs, uint32_t off, const f32x4_t &v) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rs, (int)off, 0, 2);
-}
 
 struct FusedParams {
     const uint16_t *X, *W, *G; // X[M,K], W[K,N], dY[M,N]
@@ -1271,8 +1295,8 @@ __device__ __forceinline__ void fused_small_block(const FusedParams &p, int b, L
     LDS char *const xs = smem + rs_ring<MB>();
     LDS char *const stage = xs + kRsXBytes + w * kRsStage;
 
-    // offsets are 32-bit (2KN, 2MN, 2MK < 2^31); rows or columns out of range read zero
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.W, (uint32_t)(2 * K * N));
+    // offsets are 32-bit (16 rows of W, and 2MN, 2MK < 2^31); rows or columns out of range read zero
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.W + k0 * N, (uint32_t)(2 * min<int64_t>(kRsRows, K - k0) * N));
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.G, (uint32_t)(2 * M * N));
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X, (uint32_t)(2 * M * K));
     // dW rows k0 .. k0+15 (a 64N-byte window, so 32-bit offsets); rows past K
@@ -1287,7 +1311,7 @@ __device__ __forceinline__ void fused_small_block(const FusedParams &p, int b, L
             const int r = 2 * q + (lane >> 5);
             const int64_t n = c0 + 8 * ((lane & 31) ^ rs_swz(r));
             const bool ok = k0 + r < K && n < n_end;
-            dma16_nt(rw, slot + q * 1024, oob_unless(ok, (uint32_t)(2 * ((k0 + r) * N + n))));
+            dma16_nt(rw, slot + q * 1024, oob_unless(ok, (uint32_t)(2 * (r * N + n))));
         }
 #pragma unroll
         for (int i = 0; i < kGInst; ++i) {
@@ -1398,7 +1422,7 @@ __device__ __forceinline__ void fused_small_block(const FusedParams &p, int b, L
         const int64_t nb0 = n_beg + (int64_t)jc * kRsCH + 64 * w + 4 * sl;
 #pragma unroll
         for (int u = 0; u < 4; ++u) // N % 8 == 0: nb0 .. nb0+3 all in range
-            store16_nt(rdw, oob_unless(nb0 < n_end, (uint32_t)(4 * ((4 * u + g) * N + nb0))), v[u]);
+            store_out(rdw, oob_unless(nb0 < n_end, (uint32_t)(4 * ((4 * u + g) * N + nb0))), v[u]);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -1521,11 +1545,6 @@ TileJob make_tile_job(int kind, const void *a, const void *b, void *c, int64_t I
     j.R = R;
     j.lda = lda;
     j.ldb = ldb;
-    // RC operands have I (resp. J) rows of ld elements; OC operands have R rows
-    const int64_t a_rows = kind == JOB_DX ? I : R;
-    const int64_t b_rows = kind == JOB_DX ? J : R;
-    j.a_bytes = (uint32_t)(a_rows * lda * 2);
-    j.b_bytes = (uint32_t)(b_rows * ldb * 2);
     j.tiles_i = ceil_div(I, kTile);
     j.tiles_j = ceil_div(J, kTile);
     j.ntiles = j.tiles_i * j.tiles_j;
@@ -1534,13 +1553,41 @@ TileJob make_tile_job(int kind, const void *a, const void *b, void *c, int64_t I
     return j;
 }
 
-// Both products for M <= 64 in one launch (plus, with several splits of the
-// reduction, the launch that adds the dX partials in split order).
-bool fused_small_eligible(const LinBwdArgs &a, bool need_dx, bool need_dw) {
-    // dW rows of one block are addressed through a 64N-byte buffer window
-    return need_dx && need_dw && a.M >= 1 && a.M <= kRsMaxM && a.N > 0 && 64 * a.N < ((int64_t)1 << 31);
+// Which MFMA kernel can run which product.  Every kernel reads 16-byte chunks
+// of bf16 rows (K and N multiples of 8, 16-byte aligned pointers) through
+// buffer descriptors with 32-bit offsets, 2^31 and beyond meaning "out of
+// range"; each descriptor covers only the rows its block reads (a tile's 256
+// operand rows, a 32-row slab, a block's rows of W), so operands and outputs
+// may be larger than 2 GiB as long as each such window stays below 2 GiB.
+struct Eligible {
+    bool tile_dx, tile_dw;   // the 256x256 tile kernel
+    bool small_dx, small_dw; // split-reduction dX (M <= 1024), small-tile dW (M <= 256)
+    bool fused;              // both products in one launch (M <= 64)
+};
+
+Eligible eligible(const LinBwdArgs &a, bool need_dx, bool need_dw) {
+    const int64_t lim = (int64_t)1 << 31;
+    const bool rows8 = a.bf16 && (a.K % 8 == 0) && (a.N % 8 == 0);
+    // output windows: 32 rows of dX (2K bytes each), 16 of dW (4N); slabs of
+    // 32 rows of X (2K) and dY (2N)
+    const bool win = 64 * a.K < lim && 64 * a.N < lim;
+    const bool dx_ok = rows8 && win && is_aligned16(a.dX) && (a.N == 0 || (is_aligned16(a.dY) && is_aligned16(a.W)));
+    const bool dw_ok = rows8 && win && is_aligned16(a.dW) && (a.M == 0 || (is_aligned16(a.X) && is_aligned16(a.dY)));
+    Eligible e;
+    // dX reads 256 rows of dY or W (2N bytes each) per tile / row group
+    e.tile_dx = dx_ok && 512 * a.N < lim;
+    e.tile_dw = dw_ok;
+    e.small_dx = e.tile_dx && a.M <= kSmallMaxDxM;
+    // the small-tile dW kernel addresses X (M <= 256 rows) as a whole
+    e.small_dw = dw_ok && a.M >= 1 && a.M <= kSmallMaxM && 2 * a.M * a.K < lim;
+    // the fused kernel addresses X and dY (M <= 64 rows) as wholes
+    e.fused = need_dx && need_dw && dx_ok && dw_ok && a.M >= 1 && a.M <= kRsMaxM && a.N > 0 &&
+              2 * a.M * a.K < lim && 2 * a.M * a.N < lim;
+    return e;
 }
 
+// Both products for M <= 64 in one launch (plus, with several splits of the
+// reduction, the launch that adds the dX partials in split order).
 hipError_t launch_fused_small(const LinBwdArgs &a, hipStream_t s) {
     FusedParams fp{};
     fp.X = static_cast<const uint16_t *>(a.X);
@@ -1614,19 +1661,6 @@ hipError_t launch_simt(const LinBwdArgs &a, bool need_dx, bool need_dw, hipStrea
     return hipGetLastError();
 }
 
-// The MFMA kernels read 16-byte chunks of bf16 rows (K and N multiples of 8,
-// 16-byte aligned pointers) through buffer descriptors whose 32-bit offsets
-// mark "out of range" with 2^31: each operand must be smaller than 2 GiB.
-bool mfma_eligible(const LinBwdArgs &a, bool need_dx, bool need_dw) {
-    bool vec = a.bf16 && (a.K % 8 == 0) && (a.N % 8 == 0);
-    if (need_dx)
-        vec = vec && is_aligned16(a.dX) && (a.N == 0 || (is_aligned16(a.dY) && is_aligned16(a.W)));
-    if (need_dw)
-        vec = vec && is_aligned16(a.dW) && (a.M == 0 || (is_aligned16(a.X) && is_aligned16(a.dY)));
-    const int64_t lim = (int64_t)1 << 31;
-    return vec && 2 * a.M * a.K < lim && 2 * a.K * a.N < lim && 2 * a.M * a.N < lim;
-}
-
 } // namespace
 
 const char *lin_bwd_path_refusal(const LinBwdArgs &a) {
@@ -1638,18 +1672,20 @@ const char *lin_bwd_path_refusal(const LinBwdArgs &a) {
         return nullptr;
     if (a.path != PATH_TILE && a.path != PATH_SMALL_M && a.path != PATH_FUSED_SMALL_M)
         return "unknown path";
-    if (!mfma_eligible(a, need_dx, need_dw))
-        return "the MFMA kernels need bf16 operands, K and N multiples of 8, 16-byte aligned pointers "
-               "and operands smaller than 2 GiB";
+    const Eligible e = eligible(a, need_dx, need_dw);
+    static const char *kNeed = "the MFMA kernels need bf16 operands, K and N multiples of 8, 16-byte aligned "
+                               "pointers, K and N below 2^25 and, for dX, N below 2^22";
+    if (a.path == PATH_TILE && ((need_dx && !e.tile_dx) || (need_dw && !e.tile_dw)))
+        return kNeed;
     if (a.path == PATH_SMALL_M) {
-        if (need_dx && a.M > kSmallMaxDxM)
-            return "the small-M dX kernel takes M <= 1024";
-        if (need_dw && a.M > kSmallMaxM)
-            return "the small-M dW kernel takes M <= 256";
+        if (need_dx && !e.small_dx)
+            return a.M > kSmallMaxDxM ? "the small-M dX kernel takes M <= 1024" : kNeed;
+        if (need_dw && !e.small_dw)
+            return a.M > kSmallMaxM ? "the small-M dW kernel takes M <= 256" : kNeed;
     }
-    if (a.path == PATH_FUSED_SMALL_M && !fused_small_eligible(a, need_dx, need_dw))
-        return "the fused small-M kernel computes both products (dX and dW requested), with "
-               "1 <= M <= 64, N > 0 and 64 N < 2^31";
+    if (a.path == PATH_FUSED_SMALL_M && !e.fused)
+        return "the fused small-M kernel computes both products (dX and dW requested), with bf16 operands, "
+               "K and N multiples of 8, 16-byte aligned pointers, 1 <= M <= 64 and N > 0";
     return nullptr;
 }
 
@@ -1658,26 +1694,35 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
     const bool need_dw = a.dW != nullptr && a.K > 0 && a.N > 0;
     if (!need_dx && !need_dw)
         return hipSuccess;
-    if (a.path == PATH_GENERAL || !mfma_eligible(a, need_dx, need_dw))
+    if (a.path == PATH_GENERAL)
         return launch_simt(a, need_dx, need_dw, s);
-
-    // the small-M kernels skip the empty sums (N = 0 for dX, M = 0 for dW),
-    // which the tile kernel writes as zeros
     // the fused small-M kernel runs when asked for: measured against the two
     // launches below it was 5% slower at K = N = 4096 (M = 1 .. 32) and 20-25%
     // slower with K or N = 16384; its one 140 KiB block per CU leaves each
     // chunk's LDS round trips and barrier unhidden
-    if (a.path == PATH_FUSED_SMALL_M)
+    const Eligible e = eligible(a, need_dx, need_dw);
+    if (a.path == PATH_FUSED_SMALL_M && e.fused)
         return launch_fused_small(a, s);
-    bool small_dx = need_dx && a.N > 0 && a.M <= kSmallMaxDxM;
-    bool small_dw = need_dw && a.M > 0 && a.M <= kSmallMaxM;
-    if (a.path == PATH_TILE)
-        small_dx = small_dw = false;
+    // per product: the small-M kernel (not for the empty sums, N = 0 for dX and
+    // M = 0 for dW, which the tile kernel writes as zeros), else the tile
+    // kernel, else the element-wise kernel
+    const bool small_ok = a.path != PATH_TILE;
+    const bool small_dx = need_dx && a.N > 0 && small_ok && e.small_dx;
+    const bool small_dw = need_dw && small_ok && e.small_dw;
+    const bool tile_dx = need_dx && !small_dx && e.tile_dx;
+    const bool tile_dw = need_dw && !small_dw && e.tile_dw;
+    const bool simt_dx = need_dx && !small_dx && !tile_dx;
+    const bool simt_dw = need_dw && !small_dw && !tile_dw;
+    if (simt_dx || simt_dw) {
+        hipError_t e2 = launch_simt(a, simt_dx, simt_dw, s);
+        if (e2 != hipSuccess)
+            return e2;
+    }
     MfmaParams p{};
     int nj = 0;
     TileJob jx{}, jw{};
     bool have_x = false, have_w = false;
-    if (need_dx && !small_dx) {
+    if (tile_dx) {
         jx = make_tile_job(JOB_DX, a.dY, a.W, a.dX, a.M, a.K, a.N, a.N, a.N);
         // Rows of both RC operands are 2N bytes apart.  When that is a multiple
         // of 32 KiB, the same k of every row maps to one small group of L2 sets:
@@ -1693,7 +1738,7 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
             jx.rot = 32;
         have_x = true;
     }
-    if (need_dw && !small_dw) {
+    if (tile_dw) {
         jw = make_tile_job(JOB_DW, a.X, a.dY, a.dW, a.K, a.N, a.M, a.K, a.N);
         have_w = true;
     }

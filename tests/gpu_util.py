@@ -53,9 +53,10 @@ class Guarded:
         self.t.fill_(float("nan"))
 
     def check_guards(self):
-        host = self.buf.cpu()
-        assert bool((host[:self.lo] == self.canary).all()), "write before the output buffer"
-        assert bool((host[self.lo + self.n:] == self.canary).all()), "write past the output buffer"
+        before = self.buf[:self.lo].cpu()
+        after = self.buf[self.lo + self.n:].cpu()
+        assert bool((before == self.canary).all()), "write before the output buffer"
+        assert bool((after == self.canary).all()), "write past the output buffer"
 
 
 def relf(a, ref):

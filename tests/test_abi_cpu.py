@@ -251,7 +251,8 @@ ODD = ctypes.c_void_p(4098)
     (lb.LB_PATH_TILE, 64, 60, 64, 1, (P16, P32, P48, P64, NULL)),        # K not a multiple of 8
     (lb.LB_PATH_TILE, 64, 64, 68, 1, (P16, P32, P48, NULL, P64)),        # N not a multiple of 8
     (lb.LB_PATH_TILE, 64, 64, 64, 1, (P16, P32, ODD, P64, NULL)),        # misaligned dY
-    (lb.LB_PATH_TILE, 1 << 17, 1 << 14, 8, 1, (P16, P32, P48, P64, NULL)),  # dX of 4 GiB
+    (lb.LB_PATH_TILE, 64, 64, 1 << 22, 1, (P16, P32, P48, P64, NULL)),   # dX: 256 rows of 2N bytes >= 2 GiB
+    (lb.LB_PATH_TILE, 64, 1 << 25, 64, 1, (P16, P32, P48, NULL, P64)),   # dW: a 32-row slab of X >= 2 GiB
     (lb.LB_PATH_SMALL_M, 1025, 64, 64, 1, (P16, P32, P48, P64, NULL)),   # dX: M <= 1024 only
     (lb.LB_PATH_SMALL_M, 257, 64, 64, 1, (P16, P32, P48, NULL, P64)),    # dW: M <= 256 only
     (lb.LB_PATH_FUSED_SMALL_M, 65, 64, 64, 1, (P16, P32, P48, P64, P16)),  # M <= 64 only

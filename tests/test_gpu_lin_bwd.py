@@ -19,15 +19,16 @@ DEV = "cuda"
 TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
-def run(case, need_dx=True, need_dw=True, stream=None, offset=0):
+def run(case, need_dx=True, need_dw=True, stream=None, offset=0, path=lb.LB_PATH_AUTO):
     X, W, G = (t.to(DEV) for t in (case.X, case.W, case.G))
     gx = Guarded(case.M, case.K, TDT[case.dtype], offset=offset) if need_dx else None
     gw = Guarded(case.K, case.N, torch.float32, offset=offset) if need_dw else None
-    if stream is not None:
-        with torch.cuda.stream(stream):
+    with lb.lin_bwd_path(path):
+        if stream is not None:
+            with torch.cuda.stream(stream):
+                lb.lin_bwd(X, W, G, gx.t if gx else None, gw.t if gw else None)
+        else:
             lb.lin_bwd(X, W, G, gx.t if gx else None, gw.t if gw else None)
-    else:
-        lb.lin_bwd(X, W, G, gx.t if gx else None, gw.t if gw else None)
     torch.cuda.synchronize()
     for g in (gx, gw):
         if g is not None:
@@ -351,14 +352,44 @@ def test_rotated_dx_reduction_integer_inputs_are_exact():
     assert torch.equal(dX.cpu(), torch.from_numpy(rX.astype(np.float32)).to(torch.bfloat16))
 
 
-def test_operand_of_2gib_takes_the_general_path():
-    """W of exactly 2 GiB (32768 x 32768 bf16) is past the 32-bit buffer offsets of the MFMA
-    kernels, so lin_bwd runs the general kernel: sampled entries against the oracle, and the
-    4 GiB dW written without touching the guard words around it."""
-    case = synth.linear_case(8, 32768, 32768, "bf16", x_std=1.0, w_std=0.02, g_std=1e-4, seed=31)
-    dX, dW = run(case)
+def _rows_check(case, dX, dW, rows, seed):
+    """Whole sampled rows of dX and dW against the oracle: the bars over the sample and the
+    per-element bound of every entry."""
+    Xb, Wb, Gb = synth.bits(case.X), synth.bits(case.W), synth.bits(case.G)
+    aX, aW, aG = (abs_bits(b, "bf16") for b in (Xb, Wb, Gb))
+    rng = np.random.default_rng(seed)
+    r = np.unique(np.concatenate([rng.integers(0, case.M, rows), [0, case.M - 1]]))
+    got = host_f64(dX[torch.from_numpy(r).to(dX.device)])
+    ref = oracle.dx_rows(Gb, Wb, "bf16", r)
+    assert relf(got, ref) <= DX_RELF, "dX rows relF %.3g" % relf(got, ref)
+    assert_within_bound(got, ref, oracle.dx_rows(aG, aW, "bf16", r), case.N, True, "dX")
+    r = np.unique(np.concatenate([rng.integers(0, case.K, rows), [0, case.K - 1]]))
+    got = host_f64(dW[torch.from_numpy(r).to(dW.device)])
+    ref = oracle.dw_rows(Xb, Gb, "bf16", r)
+    assert relf(got, ref) <= DW_RELF, "dW rows relF %.3g" % relf(got, ref)
+    assert_within_bound(got, ref, oracle.dw_rows(aX, aG, "bf16", r), case.M, False, "dW")
+
+
+# Operands and outputs of 2 GiB and more stay on the MFMA kernels: every buffer
+# descriptor covers only the rows its block reads or writes.  The path is forced,
+# so a call that could not run there would be refused, not moved to the
+# element-wise kernel.
+#   (8, 32768, 32768)    W 2 GiB, dW 4 GiB: split-reduction dX and small-tile dW
+#   (1040, 8, 2^20 + 8)  dY > 2 GiB: both products on the tile kernel
+#   (65536, 16384, 8)    X 2 GiB and dX 2 GiB: the tile kernel
+#   (1040, 32768, 32768) W 2 GiB, dW 4 GiB: the tile kernel
+BIG_SHAPES = [(8, 32768, 32768), (1040, 8, (1 << 20) + 8), (65536, 16384, 8), (1040, 32768, 32768)]
+
+
+@pytest.mark.parametrize("M,K,N", BIG_SHAPES)
+def test_operands_of_2gib_and_more_stay_on_the_mfma_kernels(M, K, N):
+    case = synth.linear_case(M, K, N, "bf16", x_std=1.0, w_std=0.02, g_std=1e-4, seed=31 + M)
+    dX, dW = run(case, path=lb.LB_PATH_SMALL_M if M <= 256 else lb.LB_PATH_TILE)
     assert not torch.isnan(dX).any() and not torch.isnan(dW).any()
-    _sampled_check(case, dX, dW, 256, 31)
+    if M * K * N <= (1 << 34):
+        check_full_with_bounds(case, dX, dW, bound_rows=32)
+    else:
+        _rows_check(case, dX, dW, 32, M)
 
 
 @pytest.mark.parametrize("proj", range(4))
