@@ -411,9 +411,8 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
             lb.lin_bwd(c.X, c.W, c.G, dX, dW)
     timer.run("batch", calls)
     timer.collect()
-    ms = timer.ms["batch"] / steps
-    # the same calls with an event pair around each (the event commands between
-    # consecutive calls add their own time)
+    ms_b2b = timer.ms["batch"] / steps
+    # the same calls with an event pair around each: the per-call figure
     per = Timer(["lin_bwd"])
     _sync()
     hold_queue(steps * 0.1 + 2.0)
@@ -421,7 +420,7 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
         c, dX, dW = sets[i % nsets]
         per.run("lin_bwd", lambda: lb.lin_bwd(c.X, c.W, c.G, dX, dW))
     per.collect()
-    ms_events = per.ms["lin_bwd"] / steps
+    ms = per.ms["lin_bwd"] / steps
     fl = lin_bwd_flops(M, K, N)
     tf = fl / (ms * 1e-3) / 1e12
     q = lin_bwd_min_bytes(M, K, N)
@@ -439,10 +438,11 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
             "bytes_alg": q,
             "intensity_pages": round(roofs["intensity_pages"], 2),
             "intensity_actual": round(roofs["intensity_actual"], 2),
-            "ms_with_event_pair_per_call": round(ms_events, 5),
+            "ms_back_to_back": round(ms_b2b, 5),
             "rotating_sets": nsets,
-            "timing": "GPU time per call: `steps` calls back to back behind a sleep kernel, one "
-                      "event pair around them all",
+            "timing": "GPU time per call: calls queued behind a sleep kernel, an event pair around "
+                      "each (ms); the same calls with one event pair around them all "
+                      "(ms_back_to_back)",
             "traffic": recorded_traffic(kernel, "lin_bwd_M%d_K%d_N%d" % (M, K, N))}
 
 
