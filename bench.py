@@ -690,6 +690,9 @@ def main(argv=None):
             # the down projection at 65536 tokens: X and dX of 2 GiB each
             "lin_bwd_M65536_K16384_N4096": bench_linear(65536, 16384, 4096, 3, 1, args.seed,
                                                         rotate_bytes=0),
+            # N not a multiple of 8: the call runs on zero-padded copies of dY, W and dW
+            "lin_bwd_M16384_K4096_N4100": bench_linear(16384, 4096, 4100, 5, 2, args.seed,
+                                                       rotate_bytes=0),
             "adamw_2p28_f16": bench_adamw(1 << 28, 10, 2, args.seed),
             "grad_norm_adamw_ex_2p28_f16": bench_clipped_step(1 << 28, 10, 2, args.seed),
             "bias_grad_block": bench_bias(20, 3, args.seed),

@@ -65,8 +65,15 @@ extern "C" {
  *
  * Sizes: 0 <= M, K, N < 2^31.  With M = 0 the sums are empty and dW is filled
  * with zeros; with N = 0 dX is filled with zeros; K = 0 writes nothing.
- * Any pointer alignment and any sizes are accepted; 16-byte aligned pointers
- * with K and N multiples of 8 take the vectorised kernels.
+ * Any pointer alignment and any sizes are accepted.  bf16 calls run on the
+ * MFMA kernels, which read rows in 16-byte chunks: a bf16 call whose K or N is
+ * not a multiple of 8, or whose pointers are not 16-byte aligned, first copies
+ * the operands that need it into zero-padded buffers (rows of a multiple of 8
+ * elements, 16-byte aligned), runs the padded problem and copies dX and dW
+ * back.  Those buffers are allocated on the calling thread's stream
+ * (hipMallocAsync) and released behind the call's last kernel (hipFreeAsync);
+ * if that allocation fails, the call takes the element-wise kernel instead
+ * (a forced path returns LB_EHIP).  fp32 calls take the element-wise kernel.
  * For bf16 with 1 <= M <= 1024 (decode-like and small batches), dX sums over
  * n in several blocks whose fp32 partial sums go to the library-owned
  * workspace of the calling thread's stream and are added in a fixed order
@@ -114,7 +121,11 @@ int lin_bwd_ex(const void *X, const void *W, const void *dY, void *dX, float *dW
  * thread: calls that overlap on a device race (unlike lin_bwd_ex, whose
  * workspace is per stream), so the caller keeps them in one stream order.
  * The first call on a device looks up the array's device address
- * (hipGetSymbolAddress); LB_EHIP if that fails.
+ * (hipGetSymbolAddress); LB_EHIP if that fails.  One exception to "the same
+ * kernels": a bf16 call with K or N not a multiple of 8 or with unaligned
+ * pointers, which lin_bwd_ex runs on padded copies it allocates, takes the
+ * element-wise kernel here (the same bars, not the same bits), and a forced
+ * MFMA path refuses it (LB_EINVAL).
  */
 int lin_bwd_ex_noalloc(const void *X, const void *W, const void *dY, void *dX, float *dW,
                        float *db, int64_t M, int64_t K, int64_t N, int dtype);

@@ -141,6 +141,10 @@ int lin_bwd_impl(const char *name, const void *X, const void *W, const void *dY,
     a.N = N;
     a.bf16 = dtype == LB_BF16;
     a.path = tl_path;
+    // ragged or unaligned bf16 calls run on padded copies allocated on the
+    // stream, which the no-allocation entry point cannot do: there they take
+    // the element-wise kernel
+    a.may_stage = !no_alloc;
     if (const char *why = lb::lin_bwd_path_refusal(a))
         return fail(LB_EINVAL, "%s: the forced kernel path (%d) cannot run this call: %s", name, tl_path, why);
     float *dx_partial = nullptr, *bias_partial = nullptr;

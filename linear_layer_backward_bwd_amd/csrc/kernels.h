@@ -64,6 +64,10 @@ struct LinBwdArgs {
     float *dx_partial;
     int64_t dx_partial_floats;
     int path = PATH_AUTO; // a LinPath
+    // bf16 calls with K or N not a multiple of 8, or with unaligned pointers,
+    // may run on zero-padded copies allocated on the stream (false: they take
+    // the element-wise kernel, nothing is allocated)
+    bool may_stage = true;
 };
 
 constexpr int64_t kDxPartialFloats = 1 << 23; // 32 MiB of dX partials

@@ -29,7 +29,10 @@
 //                    k_dx_smallm_reduce.
 //   k_dw_smallm      dW for M <= 256: bound by writing the fp32 output at small M;
 //                    small tiles, several per CU, so stores overlap other tiles' loads.
-//   k_lin_bwd_simt   any dtype / alignment / shape: fp32 path and ragged bf16 shapes.
+//   k_lin_bwd_fused_small  both products for M <= 64 in one launch (on request).
+//   k_repack         zero-padded copies for bf16 calls whose K or N is not a
+//                    multiple of 8 or whose pointers are not 16-byte aligned.
+//   k_lin_bwd_simt   any dtype / alignment / shape: the fp32 path.
 #include "device.h"
 #include "kernels.h"
 
@@ -1528,6 +1531,48 @@ __global__ __launch_bounds__(256) void k_lin_bwd_simt(SimtParams p) {
 }
 
 // ------------------------------------------------------------------------
+// Ragged or unaligned bf16 operands
+// ------------------------------------------------------------------------
+// The MFMA kernels read rows in 16-byte chunks, so K and N must be multiples
+// of 8 and the pointers 16-byte aligned.  Other bf16 calls run on zero-padded
+// copies: the padded problem (M, K8, N8) has the same sums (zero columns add
+// nothing), its extra output rows and columns are dropped when dX and dW are
+// copied back.  k_repack copies a row-major matrix into another with a
+// different row length, writing zero where the source has no entry.  A thread
+// moves 16 bytes of one destination row: its source elements are loaded one
+// by one (a ragged source row has no 16-byte alignment) but all before any
+// store, so each thread keeps 16 bytes of loads in flight; the store is one
+// 16-byte vector when the destination rows allow it.  Grid: x over 16-byte
+// chunks of a row, y over rows (a block-stride loop beyond 65535 rows).
+template <typename T>
+__global__ __launch_bounds__(256) void k_repack(const T *src, int64_t src_rows, int64_t src_cols, T *dst,
+                                                int64_t dst_rows, int64_t dst_cols, bool dst_vec) {
+    constexpr int V = 16 / sizeof(T);
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
+    if (c0 >= dst_cols)
+        return;
+    for (int64_t r = blockIdx.y; r < dst_rows; r += gridDim.y) {
+        const T *s = src + r * src_cols;
+        T *d = dst + r * dst_cols;
+        T v[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            v[j] = r < src_rows && c0 + j < src_cols ? s[c0 + j] : T(0);
+        if (dst_vec) { // dst_cols % V == 0 and dst 16-byte aligned: c0 .. c0+V-1 in range
+            u32x4v q;
+            __builtin_memcpy(&q, v, 16);
+            *reinterpret_cast<u32x4v *>(d + c0) = q;
+        } else {
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                if (c0 + j < dst_cols)
+                    d[c0 + j] = v[j];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
 // host-side dispatch
 // ------------------------------------------------------------------------
 inline bool is_aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -1661,6 +1706,110 @@ hipError_t launch_simt(const LinBwdArgs &a, bool need_dx, bool need_dw, hipStrea
     return hipGetLastError();
 }
 
+// Which buffers a bf16 call has to copy before the MFMA kernels can take it
+// (none: it runs as it is).  K8, N8: K and N rounded up to multiples of 8.
+struct Staging {
+    bool any;
+    bool g, w, x, dx, dw; // padded copies of dY [M,N8], W [K8,N8], X [M,K8]; dX [M,K8], dW [K8,N8]
+    int64_t K8, N8;
+};
+
+Staging staging(const LinBwdArgs &a, bool need_dx, bool need_dw) {
+    Staging st{};
+    if (!a.bf16 || !a.may_stage || a.path == PATH_GENERAL || a.M <= 0 || a.K <= 0 || a.N <= 0 ||
+        (!need_dx && !need_dw))
+        return st;
+    st.K8 = (a.K + 7) / 8 * 8;
+    st.N8 = (a.N + 7) / 8 * 8;
+    const bool kr = st.K8 != a.K, nr = st.N8 != a.N;
+    st.g = nr || !is_aligned16(a.dY);
+    st.w = need_dx && (kr || nr || !is_aligned16(a.W));
+    st.x = need_dw && (kr || !is_aligned16(a.X));
+    st.dx = need_dx && (kr || !is_aligned16(a.dX));
+    st.dw = need_dw && (kr || nr || !is_aligned16(a.dW));
+    st.any = st.g || st.w || st.x || st.dx || st.dw;
+    return st;
+}
+
+// The padded call as the MFMA dispatch sees it; `base` holds the copies (with
+// base == nullptr only the pointers' alignment is meaningful: for the checks).
+LinBwdArgs padded_call(const LinBwdArgs &a, const Staging &st, bool need_dx, bool need_dw, char *base,
+                       int64_t (&off)[5]) {
+    char *const b = base ? base : reinterpret_cast<char *>(256);
+    LinBwdArgs in = a;
+    in.K = st.K8;
+    in.N = st.N8;
+    in.may_stage = false;
+    in.dY = st.g ? b + off[0] : a.dY;
+    in.W = st.w ? b + off[1] : a.W;
+    in.X = st.x ? b + off[2] : a.X;
+    in.dX = need_dx ? (st.dx ? b + off[3] : a.dX) : nullptr;
+    in.dW = need_dw ? (st.dw ? reinterpret_cast<float *>(b + off[4]) : a.dW) : nullptr;
+    return in;
+}
+
+// Byte offsets of the copies in one allocation (256-byte aligned); returns the total.
+int64_t staging_layout(const LinBwdArgs &a, const Staging &st, int64_t (&off)[5]) {
+    const int64_t bytes[5] = {st.g ? 2 * a.M * st.N8 : 0, st.w ? 2 * st.K8 * st.N8 : 0, st.x ? 2 * a.M * st.K8 : 0,
+                              st.dx ? 2 * a.M * st.K8 : 0, st.dw ? 4 * st.K8 * st.N8 : 0};
+    int64_t total = 0;
+    for (int i = 0; i < 5; ++i) {
+        off[i] = total;
+        total += (bytes[i] + 255) / 256 * 256;
+    }
+    return total;
+}
+
+template <typename T>
+hipError_t repack(const void *src, int64_t src_rows, int64_t src_cols, void *dst, int64_t dst_rows,
+                  int64_t dst_cols, hipStream_t s) {
+    constexpr int V = 16 / sizeof(T);
+    const int64_t per_block = 256 * V;
+    const dim3 grid((unsigned)((dst_cols + per_block - 1) / per_block), (unsigned)std::min<int64_t>(dst_rows, 65535));
+    const bool vec = dst_cols % V == 0 && is_aligned16(dst);
+    hipLaunchKernelGGL(k_repack<T>, grid, dim3(256), 0, s, static_cast<const T *>(src), src_rows, src_cols,
+                       static_cast<T *>(dst), dst_rows, dst_cols, vec);
+    return hipGetLastError();
+}
+
+hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_dw, hipStream_t s);
+
+// Pads, runs the padded call, copies dX / dW back; the copies live in one
+// stream-ordered allocation released behind the last kernel.  When that
+// allocation fails, an automatic call takes the element-wise kernel instead
+// and a forced path returns the error.
+hipError_t launch_staged(const LinBwdArgs &a, const Staging &st, bool need_dx, bool need_dw, hipStream_t s) {
+    int64_t off[5];
+    const int64_t total = staging_layout(a, st, off);
+    void *base = nullptr;
+    hipError_t ea = hipMallocAsync(&base, (size_t)total, s);
+    if (ea == hipSuccess && !is_aligned16(base))
+        ea = hipErrorInvalidValue;
+    if (ea != hipSuccess) {
+        if (base)
+            (void)hipFreeAsync(base, s);
+        (void)hipGetLastError();
+        return a.path == PATH_AUTO ? launch_simt(a, need_dx, need_dw, s) : ea;
+    }
+    char *const b = static_cast<char *>(base);
+    hipError_t e = hipSuccess;
+    if (st.g)
+        e = repack<uint16_t>(a.dY, a.M, a.N, b + off[0], a.M, st.N8, s);
+    if (e == hipSuccess && st.w)
+        e = repack<uint16_t>(a.W, a.K, a.N, b + off[1], st.K8, st.N8, s);
+    if (e == hipSuccess && st.x)
+        e = repack<uint16_t>(a.X, a.M, a.K, b + off[2], a.M, st.K8, s);
+    const LinBwdArgs in = padded_call(a, st, need_dx, need_dw, b, off);
+    if (e == hipSuccess)
+        e = launch_lin_bwd_aligned(in, need_dx, need_dw, s);
+    if (e == hipSuccess && st.dx)
+        e = repack<uint16_t>(b + off[3], a.M, st.K8, a.dX, a.M, a.K, s);
+    if (e == hipSuccess && st.dw)
+        e = repack<float>(b + off[4], st.K8, st.N8, a.dW, a.K, a.N, s);
+    const hipError_t ef = hipFreeAsync(base, s);
+    return e != hipSuccess ? e : ef;
+}
+
 } // namespace
 
 const char *lin_bwd_path_refusal(const LinBwdArgs &a) {
@@ -1672,9 +1821,14 @@ const char *lin_bwd_path_refusal(const LinBwdArgs &a) {
         return nullptr;
     if (a.path != PATH_TILE && a.path != PATH_SMALL_M && a.path != PATH_FUSED_SMALL_M)
         return "unknown path";
-    const Eligible e = eligible(a, need_dx, need_dw);
-    static const char *kNeed = "the MFMA kernels need bf16 operands, K and N multiples of 8, 16-byte aligned "
-                               "pointers, K and N below 2^25 and, for dX, N below 2^22";
+    // a ragged or unaligned call runs padded: judge the padded call
+    const Staging st = staging(a, need_dx, need_dw);
+    int64_t off[5] = {0, 0, 0, 0, 0};
+    const Eligible e = st.any ? eligible(padded_call(a, st, need_dx, need_dw, nullptr, off), need_dx, need_dw)
+                              : eligible(a, need_dx, need_dw);
+    static const char *kNeed = "the MFMA kernels need bf16 operands (K and N multiples of 8 and 16-byte aligned "
+                               "pointers, or a call that may copy its operands padded), K and N below 2^25 and, "
+                               "for dX, N below 2^22";
     if (a.path == PATH_TILE && ((need_dx && !e.tile_dx) || (need_dw && !e.tile_dw)))
         return kNeed;
     if (a.path == PATH_SMALL_M) {
@@ -1696,6 +1850,15 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
         return hipSuccess;
     if (a.path == PATH_GENERAL)
         return launch_simt(a, need_dx, need_dw, s);
+    const Staging st = staging(a, need_dx, need_dw);
+    if (st.any)
+        return launch_staged(a, st, need_dx, need_dw, s);
+    return launch_lin_bwd_aligned(a, need_dx, need_dw, s);
+}
+
+namespace {
+
+hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_dw, hipStream_t s) {
     // the fused small-M kernel runs when asked for: measured against the two
     // launches below it was 5% slower at K = N = 4096 (M = 1 .. 32) and 20-25%
     // slower with K or N = 16384; its one 140 KiB block per CU leaves each
@@ -1840,4 +2003,5 @@ hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s) {
     return hipSuccess;
 }
 
+} // namespace
 } // namespace lb

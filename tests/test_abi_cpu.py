@@ -248,9 +248,6 @@ ODD = ctypes.c_void_p(4098)
 @pytest.mark.parametrize("path,M,K,N,dtype,ptrs", [
     (lb.LB_PATH_TILE, 64, 64, 64, 0, (P16, P32, P48, P64, NULL)),        # fp32 operands
     (lb.LB_PATH_SMALL_M, 64, 64, 64, 0, (P16, P32, P48, NULL, P64)),
-    (lb.LB_PATH_TILE, 64, 60, 64, 1, (P16, P32, P48, P64, NULL)),        # K not a multiple of 8
-    (lb.LB_PATH_TILE, 64, 64, 68, 1, (P16, P32, P48, NULL, P64)),        # N not a multiple of 8
-    (lb.LB_PATH_TILE, 64, 64, 64, 1, (P16, P32, ODD, P64, NULL)),        # misaligned dY
     (lb.LB_PATH_TILE, 64, 64, 1 << 22, 1, (P16, P32, P48, P64, NULL)),   # dX: 256 rows of 2N bytes >= 2 GiB
     (lb.LB_PATH_TILE, 64, 1 << 25, 64, 1, (P16, P32, P48, NULL, P64)),   # dW: a 32-row slab of X >= 2 GiB
     (lb.LB_PATH_SMALL_M, 1025, 64, 64, 1, (P16, P32, P48, P64, NULL)),   # dX: M <= 1024 only
@@ -267,6 +264,44 @@ def test_forced_path_refused_on_host(path, M, K, N, dtype, ptrs):
         assert lib.lin_bwd(X, W, dY, dX, dW, M, K, N, dtype) == -1
         assert "forced kernel path" in lb.lb_last_error()
         assert lib.lin_bwd_ex(X, W, dY, dX, dW, NULL, M, K, N, dtype) == -1
+    finally:
+        assert lib.lb_set_lin_bwd_path(lb.LB_PATH_AUTO) == 0
+
+
+# bf16 calls with K or N not a multiple of 8, or with unaligned pointers, run on padded
+# copies that the call allocates on its stream: a forced MFMA path takes them (here the
+# call passes the host checks and then fails for want of a GPU), while the no-allocation
+# entry point, which cannot copy, refuses them
+STAGED = [
+    (lb.LB_PATH_TILE, 64, 60, 64, (P16, P32, P48, P64, NULL)),        # K not a multiple of 8
+    (lb.LB_PATH_TILE, 64, 64, 68, (P16, P32, P48, NULL, P64)),        # N not a multiple of 8
+    (lb.LB_PATH_TILE, 64, 64, 64, (P16, P32, ODD, P64, NULL)),        # misaligned dY
+    (lb.LB_PATH_SMALL_M, 32, 4100, 4096, (P16, P32, P48, P64, P16)),  # ragged K, both products
+    (lb.LB_PATH_FUSED_SMALL_M, 32, 4096, 4100, (P16, P32, P48, P64, P16)),
+]
+
+
+@pytest.mark.parametrize("path,M,K,N,ptrs", STAGED)
+def test_forced_path_takes_ragged_calls_through_padded_copies(path, M, K, N, ptrs):
+    lib = lb.library()
+    X, W, dY, dX, dW = ptrs
+    assert lib.lb_set_lin_bwd_path(path) == 0
+    try:
+        lib.lin_bwd(X, W, dY, dX, dW, M, K, N, 1)
+        assert "forced kernel path" not in lb.lb_last_error()
+        assert lib.lin_bwd_ex_noalloc(X, W, dY, dX, dW, NULL, M, K, N, 1) == -1
+        assert "forced kernel path" in lb.lb_last_error()
+    finally:
+        assert lib.lb_set_lin_bwd_path(lb.LB_PATH_AUTO) == 0
+
+
+def test_staged_call_still_refuses_what_the_padded_call_cannot_run():
+    """K = 2^25 - 4 pads to 2^25: a 32-row slab of the padded X is 2 GiB."""
+    lib = lb.library()
+    assert lib.lb_set_lin_bwd_path(lb.LB_PATH_TILE) == 0
+    try:
+        assert lib.lin_bwd(P16, P32, P48, NULL, P64, 64, (1 << 25) - 4, 64, 1) == -1
+        assert "forced kernel path" in lb.lb_last_error()
     finally:
         assert lib.lb_set_lin_bwd_path(lb.LB_PATH_AUTO) == 0
 

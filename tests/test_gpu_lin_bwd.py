@@ -59,7 +59,7 @@ SHAPES = [
     (65, 128, 384),
     # small-M dX path (M <= 64), with the MFMA dW path
     (64, 384, 520), (32, 1024, 1032), (17, 40, 8), (1, 264, 72), (48, 8, 1000),
-    # sizes not multiples of 8: SIMT path
+    # sizes not multiples of 8: zero-padded copies on the MFMA kernels
     (33, 100, 70), (5, 7, 3), (70, 9, 130),
 ]
 
