@@ -112,6 +112,52 @@ def test_with_dx_dw_equals_lin_bwd():
     check(db.cpu().numpy(), c.G, "bf16")
 
 
+# db requested together with dW (and dX or not), on the shapes where dW runs on the tile
+# kernel (M > 256): partial last slab (M % 32), partial tile columns (N % 256), one and
+# several tile columns.
+@pytest.mark.parametrize("M,K,N,with_dx", [(300, 264, 1032, True), (1100, 520, 776, False),
+                                           (4097, 264, 520, True), (2048, 4096, 4096, True),
+                                           (257, 8, 8, False), (1000, 1024, 16, True)])
+def test_db_with_dw(M, K, N, with_dx):
+    c = synth.linear_case(M, K, N, "bf16", seed=M + N, device=DEV)
+    dW = torch.empty(K, N, device=DEV)
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device=DEV) if with_dx else None
+    db = Guarded(1, N, torch.float32)
+    lb.lin_bwd_ex(c.X, c.W, c.G, dX, dW, db.t.view(N))
+    torch.cuda.synchronize()
+    db.check_guards()
+    check(db.t.view(N).cpu().numpy(), c.G, "bf16")
+    # and db requested alone
+    alone = torch.empty(N, device=DEV)
+    lb.lin_bwd_ex(None, None, c.G, db=alone)
+    torch.cuda.synchronize()
+    check(alone.cpu().numpy(), c.G, "bf16")
+
+
+def test_db_with_dw_integer_inputs_exact():
+    rng = np.random.default_rng(77)
+    M, K, N = 5000, 264, 4104
+    mk = lambda *sh: torch.tensor(rng.integers(-3, 4, size=sh), dtype=torch.float32).to(torch.bfloat16)
+    c = synth.LinearCase(M, K, N, "bf16", mk(M, K), mk(K, N), mk(M, N))
+    dW = torch.empty(K, N, device=DEV)
+    db = torch.empty(N, device=DEV)
+    lb.lin_bwd_ex(c.X.to(DEV), c.W.to(DEV), c.G.to(DEV), None, dW, db)
+    torch.cuda.synchronize()
+    ref = oracle.bias_grad(synth.bits(c.G), "bf16")
+    assert np.array_equal(db.cpu().numpy(), ref.astype(np.float32))
+
+
+def test_db_with_dw_block_projections():
+    """The block's four projections (M = 16384) with dW and db: every column of db."""
+    cases, _ = synth.block_case(seed=0, device=DEV)
+    for c in cases:
+        dW = torch.empty(c.K, c.N, device=DEV)
+        db = torch.empty(c.N, device=DEV)
+        lb.lin_bwd_ex(c.X, c.W, c.G, None, dW, db)
+        torch.cuda.synchronize()
+        check(db.cpu().numpy(), c.G, "bf16")
+
+
 def bits_t(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
