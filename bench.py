@@ -381,6 +381,50 @@ def hold_queue(ms):
     torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
 
 
+def plain_stream_floor(read_bytes, write_bytes, calls=40, rotate_bytes=768 << 20):
+    """GPU time per launch of the calibration read kernel over `read_bytes` and of the
+    write kernel over `write_bytes` (16-byte vectors, one per thread), cold: each call on
+    the next of enough buffers to exceed the 256 MB last-level cache, queued behind a
+    sleep kernel, an event pair around each call; medians.  Their sum is what two plain
+    streaming kernels need to move the bytes of a memory-bound call on this part."""
+    import ctypes
+
+    import torch
+    if not os.path.exists(CALIB_PATH):
+        raise RuntimeError("%s is not built (python -m linear_layer_backward_bwd_amd.build)" % CALIB_PATH)
+    lib = ctypes.CDLL(CALIB_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.calib_read.argtypes = [vp, i64, vp, vp]
+    lib.calib_write.argtypes = [vp, i64, ctypes.c_uint32, vp]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    word = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {}
+    for name, nbytes in (("read", read_bytes), ("write", write_bytes)):
+        nbytes = (nbytes + 15) // 16 * 16
+        nb = max(4, -(-rotate_bytes // nbytes))
+        bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda") for _ in range(nb)]
+        if name == "read":
+            fn = lambda i: lib.calib_read(bufs[i % nb].data_ptr(), nbytes, word.data_ptr(), stream)
+        else:
+            fn = lambda i: lib.calib_write(bufs[i % nb].data_ptr(), nbytes, 0x3f800000, stream)
+        for i in range(4):
+            assert fn(i) == 0
+        _sync()
+        hold_queue(calls * 0.05 + 2.0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * calls)]
+        for i in range(calls):
+            ev[2 * i].record()
+            assert fn(i) == 0
+            ev[2 * i + 1].record()
+        _sync()
+        t = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(calls))
+        out[name + "_ms"] = round(t[len(t) // 2], 5)
+        del bufs
+        torch.cuda.empty_cache()
+    out["sum_ms"] = round(out["read_ms"] + out["write_ms"], 5)
+    return out
+
+
 def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
     """lin_bwd alone at one shape; rotates over buffer sets larger than the 256 MB MALL.
     The timed calls are queued behind a sleep kernel (hold_queue), so that the events
@@ -425,6 +469,13 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
     tf = fl / (ms * 1e-3) / 1e12
     q = lin_bwd_min_bytes(M, K, N)
     roofs = lin_bwd_roofs(M, K, N)
+    floor = None
+    if roofs["pages"] < PEAK_BF16_TFLOPS:   # memory-bound: what plain streaming kernels need
+        floor = plain_stream_floor(2 * (M * K + K * N + M * N), 2 * M * K + 4 * K * N)
+        floor["floor_over_ms"] = round(floor["sum_ms"] / ms, 4)
+        floor["what"] = ("the calibration read kernel over the bytes the call reads (bf16 X, W, dY) "
+                         "plus the write kernel over the bytes it writes (bf16 dX, fp32 dW), cold, "
+                         "an event pair around each launch, medians")
     kernel = "k_dw_smallm" if M <= 64 else "k_lin_bwd_mfma"
     return {"M": M, "K": K, "N": N, "ms": round(ms, 5), "tflops": round(tf, 1),
             "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
@@ -443,7 +494,8 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
             "timing": "GPU time per call: calls queued behind a sleep kernel, an event pair around "
                       "each (ms); the same calls with one event pair around them all "
                       "(ms_back_to_back)",
-            "traffic": recorded_traffic(kernel, "lin_bwd_M%d_K%d_N%d" % (M, K, N))}
+            "traffic": recorded_traffic(kernel, "lin_bwd_M%d_K%d_N%d" % (M, K, N)),
+            **({"plain_stream_floor": floor} if floor else {})}
 
 
 def bench_adamw(n, steps, warmup, seed):
@@ -701,8 +753,8 @@ def main(argv=None):
         for key in ("lin_bwd_M32_K4096_N4096", "lin_bwd_M2048_K4096_N4096"):
             out["also"][key]["frac_of_measured_mfma_peak"] = round(
                 out["also"][key]["tflops"] / cal["mfma_bf16_tflops"], 4)
-        out["also"]["lin_bwd_M32_K4096_N4096"]["frac_of_measured_copy_alg"] = round(
-            out["also"]["lin_bwd_M32_K4096_N4096"]["gbps_alg"] / cal["copy_gbps"], 4)
+        m32 = out["also"]["lin_bwd_M32_K4096_N4096"]
+        m32["frac_of_measured_copy_alg"] = round(m32["gbps_alg"] / cal["copy_gbps"], 4)
         a2 = out["also"]["adamw_2p28_f16"]
         a2["frac_of_measured_copy"] = round(a2["gbps"] / cal["copy_gbps"], 4)
         a2["frac_of_measured_adamw_mix_stream"] = round(a2["gbps"] / cal["adamw_mix_stream_gbps"], 4)

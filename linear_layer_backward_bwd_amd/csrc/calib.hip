@@ -11,6 +11,7 @@
 //
 //   calib_copy     dst = src, one 16-byte vector per thread over an exact grid
 //   calib_read     reads a buffer once (16-byte vectors), writes nothing in practice
+//   calib_write    writes a buffer once (16-byte vectors), reads nothing
 //   calib_stream   the fused AdamW pass's traffic without its arithmetic: per
 //                  element reads a 16-bit g and fp32 W, m, v, writes W, m, v
 //                  (26 B per element), one element per thread, non-temporal
@@ -44,6 +45,12 @@ __global__ __launch_bounds__(kThreads) void k_read(const u32x4_t *src, int64_t n
     // a value no input produces in practice: keeps the loads, writes nothing
     if (x == 0x9e3779b9u)
         out[0] = x;
+}
+
+__global__ __launch_bounds__(kThreads) void k_write(u32x4_t *dst, int64_t n16, uint32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n16)
+        dst[i] = u32x4_t{v, v, v, (uint32_t)i};
 }
 
 __global__ __launch_bounds__(kThreads) void k_stream(float *W, const uint16_t *g, float *m, float *v, int64_t n) {
@@ -125,6 +132,15 @@ int calib_read(const void *src, int64_t bytes, uint32_t *out, void *stream) {
     if (bytes % 16 || grid_for(bytes / 16, grid) != hipSuccess)
         return -1;
     hipLaunchKernelGGL(k_read, grid, dim3(kThreads), 0, (hipStream_t)stream, (const u32x4_t *)src, bytes / 16, out);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// dst: `bytes` bytes (a multiple of 16), 16-byte aligned; filled with a pattern.
+int calib_write(void *dst, int64_t bytes, uint32_t value, void *stream) {
+    dim3 grid;
+    if (bytes % 16 || grid_for(bytes / 16, grid) != hipSuccess)
+        return -1;
+    hipLaunchKernelGGL(k_write, grid, dim3(kThreads), 0, (hipStream_t)stream, (u32x4_t *)dst, bytes / 16, value);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
