@@ -262,6 +262,7 @@ class Timer:
         self.names = names
         self.ms = {n: 0.0 for n in names}
         self.count = {n: 0 for n in names}
+        self.samples = {n: [] for n in names}
         self.pending = []
 
     def run(self, name, fn):
@@ -276,8 +277,10 @@ class Timer:
     def collect(self):
         _sync()
         for name, a, b in self.pending:
-            self.ms[name] += a.elapsed_time(b)
+            t = a.elapsed_time(b)
+            self.ms[name] += t
             self.count[name] += 1
+            self.samples[name].append(t)
         self.pending = []
 
 
@@ -326,7 +329,9 @@ def bench_block(steps, warmup, seed):
     per_proj = []
     for c in cases:
         ms = timer.ms[c.name] / steps
+        t = sorted(timer.samples[c.name])
         per_proj.append({"name": c.name, "M": c.M, "K": c.K, "N": c.N, "ms": round(ms, 4),
+                         "ms_median": round(t[len(t) // 2], 4), "ms_min": round(t[0], 4),
                          "tflops": round(flops[c.name] / (ms * 1e-3) / 1e12, 1)})
     ms_step = wall / steps * 1e3
     result = {
@@ -465,6 +470,20 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
         per.run("lin_bwd", lambda: lb.lin_bwd(c.X, c.W, c.G, dX, dW))
     per.collect()
     ms = per.ms["lin_bwd"] / steps
+    cold = sorted(per.samples["lin_bwd"])
+    # warm: the same calls on one buffer set, whose inputs the last-level cache then holds
+    warm_median = None
+    if nsets > 1:
+        warm = Timer(["lin_bwd"])
+        c0, dX0, dW0 = sets[0]
+        lb.lin_bwd(c0.X, c0.W, c0.G, dX0, dW0)
+        _sync()
+        hold_queue(steps * 0.1 + 2.0)
+        for i in range(steps):
+            warm.run("lin_bwd", lambda: lb.lin_bwd(c0.X, c0.W, c0.G, dX0, dW0))
+        warm.collect()
+        ws = sorted(warm.samples["lin_bwd"])
+        warm_median = ws[len(ws) // 2]
     fl = lin_bwd_flops(M, K, N)
     tf = fl / (ms * 1e-3) / 1e12
     q = lin_bwd_min_bytes(M, K, N)
@@ -489,11 +508,15 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
             "bytes_alg": q,
             "intensity_pages": round(roofs["intensity_pages"], 2),
             "intensity_actual": round(roofs["intensity_actual"], 2),
+            "ms_median": round(cold[len(cold) // 2], 5), "ms_min": round(cold[0], 5),
+            "warm_ms_median": None if warm_median is None else round(warm_median, 5),
             "ms_back_to_back": round(ms_b2b, 5),
             "rotating_sets": nsets,
-            "timing": "GPU time per call: calls queued behind a sleep kernel, an event pair around "
-                      "each (ms); the same calls with one event pair around them all "
-                      "(ms_back_to_back)",
+            "timing": "GPU time per call, cold (inputs rotate over buffer sets larger than the "
+                      "last-level cache): calls queued behind a sleep kernel, an event pair around "
+                      "each (ms = mean, ms_median, ms_min); the same calls with one event pair "
+                      "around them all (ms_back_to_back); warm_ms_median: the same per-call "
+                      "timing on one buffer set",
             "traffic": recorded_traffic(kernel, "lin_bwd_M%d_K%d_N%d" % (M, K, N)),
             **({"plain_stream_floor": floor} if floor else {})}
 
