@@ -121,7 +121,9 @@ int lin_bwd_ex(const void *X, const void *W, const void *dY, void *dX, float *dW
  * thread: calls that overlap on a device race (unlike lin_bwd_ex, whose
  * workspace is per stream), so the caller keeps them in one stream order.
  * The first call on a device looks up the array's device address
- * (hipGetSymbolAddress); LB_EHIP if that fails.  One exception to "the same
+ * (hipGetSymbolAddress); LB_EHIP if that fails.  For HIP graph capture, make
+ * that first call before capturing; the calls then record kernel launches
+ * only (no allocation, no memset).  One exception to "the same
  * kernels": a bf16 call with K or N not a multiple of 8 or with unaligned
  * pointers, which lin_bwd_ex runs on padded copies it allocates, takes the
  * element-wise kernel here (the same bars, not the same bits), and a forced
