@@ -1821,7 +1821,7 @@ const char *lin_bwd_path_refusal(const LinBwdArgs &a) {
         return nullptr;
     if (a.path != PATH_TILE && a.path != PATH_SMALL_M && a.path != PATH_FUSED_SMALL_M)
         return "unknown path";
-    // a ragged or unaligned call runs padded: judge the padded call
+    // a ragged or unaligned call runs padded: check the padded call
     const Staging st = staging(a, need_dx, need_dw);
     int64_t off[5] = {0, 0, 0, 0, 0};
     const Eligible e = st.any ? eligible(padded_call(a, st, need_dx, need_dw, nullptr, off), need_dx, need_dw)
