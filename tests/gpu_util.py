@@ -102,16 +102,6 @@ def adamw_ok(gpu, ref):
     return bool(ok.all()), worst
 
 
-def sample_positions(rows, cols, count, seed):
-    """Random (row, col) pairs plus the four corners and the last row/col edges."""
-    rng = np.random.default_rng(seed)
-    r = rng.integers(0, rows, count)
-    c = rng.integers(0, cols, count)
-    edge_r = np.array([0, 0, rows - 1, rows - 1] + [rows - 1] * 16 + list(rng.integers(0, rows, 16)))
-    edge_c = np.array([0, cols - 1, 0, cols - 1] + list(rng.integers(0, cols, 16)) + [cols - 1] * 16)
-    return np.concatenate([r, edge_r]), np.concatenate([c, edge_c])
-
-
 # ---- per-element error bounds of the GEMM outputs -------------------------------------
 #
 # A kernel adds the R products of an entry in fp32: 32 at a time inside one MFMA, then into
