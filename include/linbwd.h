@@ -70,10 +70,13 @@ extern "C" {
  * not a multiple of 8, or whose pointers are not 16-byte aligned, first copies
  * the operands that need it into zero-padded buffers (rows of a multiple of 8
  * elements, 16-byte aligned), runs the padded problem and copies dX and dW
- * back.  Those buffers are allocated on the calling thread's stream
- * (hipMallocAsync) and released behind the call's last kernel (hipFreeAsync);
- * if that allocation fails, the call takes the element-wise kernel instead
- * (a forced path returns LB_EHIP).  fp32 calls take the element-wise kernel.
+ * back.  Those buffers come from a library-owned stream-ordered memory pool
+ * of the current device (hipMallocFromPoolAsync on the calling thread's
+ * stream, released behind the call's last kernel with hipFreeAsync); the pool
+ * keeps the memory it has mapped across synchronisations, up to the largest
+ * such call's copies, until lb_shutdown().  If the allocation fails, the call
+ * takes the element-wise kernel instead (a forced path returns LB_EHIP).
+ * fp32 calls take the element-wise kernel.
  * For bf16 with 1 <= M <= 1024 (decode-like and small batches), dX sums over
  * n in several blocks whose fp32 partial sums go to the library-owned
  * workspace of the calling thread's stream and are added in a fixed order

@@ -76,6 +76,16 @@ hipError_t workspace(Workspace &out) {
     return hipSuccess;
 }
 
+// ---- memory pool for the padded copies of ragged or unaligned calls --------
+// One stream-ordered pool per device, created on first use, that keeps what
+// it holds across synchronisations (release threshold: never).  The device's
+// default pool gives its memory back at every synchronisation, and the next
+// allocation then maps it again: a ragged call with a synchronisation after
+// it took 335 us instead of 89 (M = 32) and 339 instead of 215 (M = 2048).
+// lb_shutdown() destroys the pools.
+std::mutex pool_mutex;
+std::map<int, hipMemPool_t> pool_by_device;
+
 // ---- static scratch for lin_bwd_ex_noalloc ----------------------------------
 // The temporaries of lin_bwd_ex (small-M dX split partials, then the bias row
 // partials) for callers that cannot allocate, in a file-scope device array of
@@ -231,6 +241,37 @@ int adamw_impl(const char *name, lb::GradType gt, float *W, const void *g, float
 
 } // namespace
 
+namespace lb {
+hipError_t staging_pool(hipMemPool_t *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    std::lock_guard<std::mutex> lock(pool_mutex);
+    auto it = pool_by_device.find(dev);
+    if (it == pool_by_device.end()) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        e = hipMemPoolCreate(&pool, &props);
+        if (e != hipSuccess)
+            return e;
+        uint64_t keep = UINT64_MAX;
+        e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) {
+            (void)hipMemPoolDestroy(pool);
+            return e;
+        }
+        it = pool_by_device.emplace(dev, pool).first;
+    }
+    *out = it->second;
+    return hipSuccess;
+}
+} // namespace lb
+
 extern "C" {
 
 int lin_bwd_ex(const void *X, const void *W, const void *dY, void *dX, float *dW, float *db, int64_t M,
@@ -384,6 +425,17 @@ int lb_shutdown(void) {
             first = e;
     }
     ws_by_stream.clear();
+    {
+        std::lock_guard<std::mutex> plock(pool_mutex);
+        for (const auto &kv : pool_by_device) {
+            hipError_t e = hipSetDevice(kv.first);
+            if (e == hipSuccess)
+                e = hipMemPoolDestroy(kv.second);
+            if (e != hipSuccess && first == hipSuccess)
+                first = e;
+        }
+        pool_by_device.clear();
+    }
     const hipError_t e = hipSetDevice(cur);
     if (first == hipSuccess)
         first = e;

@@ -73,6 +73,10 @@ struct LinBwdArgs {
 constexpr int64_t kDxPartialFloats = 1 << 23; // 32 MiB of dX partials
 
 
+// The current device's pool for the padded copies of ragged or unaligned
+// calls (it keeps its memory across synchronisations; lb_shutdown frees it).
+hipError_t staging_pool(hipMemPool_t *out);
+
 // Chooses kernels by dtype, alignment and M (or a.path); enqueues 1-3 launches.
 hipError_t launch_lin_bwd(const LinBwdArgs &a, hipStream_t s);
 

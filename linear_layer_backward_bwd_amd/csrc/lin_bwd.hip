@@ -1775,14 +1775,18 @@ hipError_t repack(const void *src, int64_t src_rows, int64_t src_cols, void *dst
 hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_dw, hipStream_t s);
 
 // Pads, runs the padded call, copies dX / dW back; the copies live in one
-// stream-ordered allocation released behind the last kernel.  When that
+// stream-ordered allocation from the library's pool, released behind the last
+// kernel.  When that
 // allocation fails, an automatic call takes the element-wise kernel instead
 // and a forced path returns the error.
 hipError_t launch_staged(const LinBwdArgs &a, const Staging &st, bool need_dx, bool need_dw, hipStream_t s) {
     int64_t off[5];
     const int64_t total = staging_layout(a, st, off);
     void *base = nullptr;
-    hipError_t ea = hipMallocAsync(&base, (size_t)total, s);
+    hipMemPool_t pool = nullptr;
+    hipError_t ea = staging_pool(&pool);
+    if (ea == hipSuccess)
+        ea = hipMallocFromPoolAsync(&base, (size_t)total, pool, s);
     if (ea == hipSuccess && !is_aligned16(base))
         ea = hipErrorInvalidValue;
     if (ea != hipSuccess) {

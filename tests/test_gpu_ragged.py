@@ -139,3 +139,15 @@ def test_staged_calls_back_to_back_on_a_side_stream():
         lb.lin_bwd(X, W, G, dX2, dW2)
         torch.cuda.synchronize()
         assert torch.equal(dX, dX2) and torch.equal(dW, dW2)
+
+
+def test_padded_copies_after_shutdown():
+    """lb_shutdown() destroys the pool of the padded copies; the next ragged call makes a new
+    one and gives the same bits."""
+    case = synth.linear_case(300, 517, 263, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=29)
+    before = run(case, "auto")
+    torch.cuda.synchronize()
+    lb.lb_shutdown()
+    after = run(case, "auto")
+    assert torch.equal(before[0], after[0]) and torch.equal(before[1], after[1])
+    check(case, *after, bound_rows=16)
