@@ -536,8 +536,10 @@ def bench_adamw(n, steps, warmup, seed):
                                                  case.b2, case.eps, case.wd, 1 + i % 10, case.inv_scale))
     timer.collect()
     ms = timer.ms["adamw"] / steps
+    t = sorted(timer.samples["adamw"])
     gbps = ADAMW_BYTES_16BIT_GRAD * n / (ms * 1e-3) / 1e9
-    return {"n": n, "grad": "f16", "ms": round(ms, 4), "gbps": round(gbps, 1),
+    return {"n": n, "grad": "f16", "ms": round(ms, 4), "ms_median": round(t[len(t) // 2], 4),
+            "ms_min": round(t[0], 4), "steps": steps, "warmup": warmup, "gbps": round(gbps, 1),
             "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
             "gparams_per_s": round(n / (ms * 1e-3) / 1e9, 2),
             "traffic": recorded_traffic("k_adamw", "adamw_2p28_f16")}
@@ -768,8 +770,10 @@ def main(argv=None):
             # N not a multiple of 8: the call runs on zero-padded copies of dY, W and dW
             "lin_bwd_M16384_K4096_N4100": bench_linear(16384, 4096, 4100, 5, 2, args.seed,
                                                        rotate_bytes=0),
-            "adamw_2p28_f16": bench_adamw(1 << 28, 10, 2, args.seed),
-            "grad_norm_adamw_ex_2p28_f16": bench_clipped_step(1 << 28, 10, 2, args.seed),
+            # 10 warm-up steps: the first ten or so launches of a long series of these passes
+            # run up to 10% slower than the ones after them, arithmetic or not
+            "adamw_2p28_f16": bench_adamw(1 << 28, 20, 10, args.seed),
+            "grad_norm_adamw_ex_2p28_f16": bench_clipped_step(1 << 28, 20, 10, args.seed),
             "bias_grad_block": bench_bias(20, 3, args.seed),
             "softmax_bwd_attention": bench_softmax(10, 2, args.seed),
         }
