@@ -151,3 +151,20 @@ def test_padded_copies_after_shutdown():
     after = run(case, "auto")
     assert torch.equal(before[0], after[0]) and torch.equal(before[1], after[1])
     check(case, *after, bound_rows=16)
+
+
+@pytest.mark.parametrize("M,K,N", [(0, 100, 70), (0, 4100, 8), (37, 9, 0), (37, 0, 13)])
+def test_empty_sums_with_ragged_sizes(M, K, N):
+    """M = 0: dW is the empty sum (zeros); N = 0: dX is; K = 0 leaves nothing to write.  These
+    calls have nothing to pad and take the element-wise kernel."""
+    X = torch.randn(M, K, device=DEV).to(torch.bfloat16)
+    W = torch.randn(K, N, device=DEV).to(torch.bfloat16)
+    G = torch.randn(M, N, device=DEV).to(torch.bfloat16)
+    dX = torch.full((M, K), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dW = torch.full((K, N), float("nan"), device=DEV)
+    lb.lin_bwd(X, W, G, dX, dW)
+    torch.cuda.synchronize()
+    if M == 0:
+        assert bool((dW == 0).all())
+    if N == 0:
+        assert bool((dX == 0).all())
