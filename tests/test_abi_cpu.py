@@ -319,3 +319,14 @@ def test_forced_path_is_per_thread_and_restored():
         t.join()
         assert lib.lin_bwd(P16, P32, P48, P64, NULL, 64, 64, 64, 0) == -1
     assert seen == [0]
+
+
+def test_c_consumer_compiles_against_the_header():
+    """The native consumer (tests/native/c_abi_consumer.c) builds with gcc against
+    include/linbwd.h and the HIP runtime header alone."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+                        os.path.join(ROOT, "tests", "native", "c_abi_consumer.c")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
