@@ -278,10 +278,14 @@ int lb_set_stream(void *hip_stream);
  *                    (1 <= M <= 64, dX and dW both requested; never chosen
  *                    automatically: slower than the SMALL_M pair on the
  *                    shapes measured)
- * A forced MFMA path (TILE, SMALL_M, FUSED_SMALL_M) needs bf16 operands, K and
- * N multiples of 8, 16-byte aligned pointers and operands below 2 GiB, and
- * the M limits above; a call it cannot run fails with LB_EINVAL before
- * anything is enqueued.  Returns LB_OK, or LB_EINVAL for another value.
+ * A forced MFMA path (TILE, SMALL_M, FUSED_SMALL_M) needs bf16 operands and
+ * the M limits above.  K or N not a multiple of 8, or unaligned pointers, run
+ * on zero-padded copies (see lin_bwd; lin_bwd_ex_noalloc cannot make them and
+ * refuses such calls); the limits of the buffer windows are then those of the
+ * padded call: K, N < 2^25, for dX on the tile kernel N < 2^22, and for the
+ * small-M dW and fused kernels X (and dY) below 2 GiB.  A call the path
+ * cannot run fails with LB_EINVAL before anything is enqueued.  Returns LB_OK,
+ * or LB_EINVAL for another value.
  */
 #define LB_PATH_AUTO 0
 #define LB_PATH_TILE 1
