@@ -1,0 +1,77 @@
+"""Seeded random calls of lin_bwd across the dispatch boundaries: sizes from 1 to a few
+thousand (aligned, ragged, the pages' 4096), every kernel path forced or automatic,
+unaligned inputs and outputs, one product or both.  Each call that its path takes meets
+the oracle's bars over every entry with its outputs' guard bands intact; a forced path
+that cannot run a call refuses it before anything is enqueued.
+
+Every call goes through the C ABI of liblinbwd.so.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_layer_backward_bwd_amd as lb
+import oracle
+import synth
+from gpu_util import DW_RELF, DX_RELF, Guarded, host_f64, relf
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+PATHS = [lb.LB_PATH_AUTO, lb.LB_PATH_TILE, lb.LB_PATH_SMALL_M, lb.LB_PATH_GENERAL, lb.LB_PATH_FUSED_SMALL_M]
+
+
+def draws(seed, count):
+    rng = np.random.default_rng(seed)
+
+    def dim():
+        r = rng.random()
+        if r < 0.3:
+            return int(rng.integers(1, 64))
+        if r < 0.6:
+            return int(rng.integers(64, 600))
+        if r < 0.9:
+            return int(rng.integers(600, 2100))
+        return int(rng.choice([8, 16, 256, 264, 1024, 1032, 2048, 4096, 4100]))
+    out = []
+    while len(out) < count:
+        M, K, N = dim(), dim(), dim()
+        if M * K * N > (1 << 30):
+            continue
+        need_dx = bool(rng.random() < 0.9)
+        need_dw = bool(rng.random() < 0.9) or not need_dx
+        out.append((M, K, N, int(rng.choice(PATHS)), int(rng.choice([0, 0, 0, 1, 3])),
+                    int(rng.choice([0, 0, 0, 1])), need_dx, need_dw, int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,path,off_in,off_out,need_dx,need_dw,seed", draws(2024, 80))
+def test_random_call_meets_the_bars(M, K, N, path, off_in, off_out, need_dx, need_dw, seed):
+    case = synth.linear_case(M, K, N, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=seed)
+
+    def dev(t):
+        flat = torch.empty(t.numel() + off_in, dtype=t.dtype, device=DEV)
+        v = flat[off_in:].view(t.shape)
+        v.copy_(t.to(DEV))
+        return v
+    X, W, G = dev(case.X), dev(case.W), dev(case.G)
+    gx = Guarded(M, K, torch.bfloat16, offset=off_out) if need_dx else None
+    gw = Guarded(K, N, torch.float32, offset=off_out) if need_dw else None
+    with lb.lin_bwd_path(path):
+        try:
+            lb.lin_bwd(X, W, G, gx.t if gx else None, gw.t if gw else None)
+        except RuntimeError as e:
+            assert path != lb.LB_PATH_AUTO and "forced kernel path" in str(e), str(e)
+            for g in (gx, gw):
+                if g is not None:
+                    assert bool(torch.isnan(g.t).all()), "a refused call wrote its output"
+            return
+    torch.cuda.synchronize()
+    for g in (gx, gw):
+        if g is not None:
+            g.check_guards()
+    rX, rW = oracle.lin_bwd(synth.bits(case.X), synth.bits(case.W), synth.bits(case.G), "bf16",
+                            need_dx=need_dx, need_dw=need_dw)
+    if need_dx:
+        assert relf(host_f64(gx.t), rX) <= DX_RELF
+    if need_dw:
+        assert relf(host_f64(gw.t), rW) <= DW_RELF
