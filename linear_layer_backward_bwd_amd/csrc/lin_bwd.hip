@@ -94,8 +94,9 @@ struct TileJob {
     int64_t lda, ldb;  // leading dims of a and b in elements
     int tiles_i, tiles_j, ntiles;
     int kind;          // JOB_DX: RC operands, bf16 out; JOB_DW: OC operands, fp32 out
-    // k rotation (slabs): the tile at (ti, tj) walks the slabs starting at
-    // rot * ((tj / 2) % 4) mod nslab (0 for a ragged RC reduction)
+    // k rotation (slabs), dX (RC) jobs only: the tile at (ti, tj) walks the
+    // slabs starting at rot * ((tj / 2) % 4) mod nslab (0 for a ragged
+    // reduction)
     int rot;
 };
 
@@ -517,14 +518,12 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
         (op == 0 ? an : bn)[xb] = read_rc<off>(smem + fo[op][xb][m & 1]);
     };
     // slab t with t % 4 == TM (compile time); flags as described above (only
-    // odd slabs issue DMAs: the 16 instructions of pair (t+3)/2)
-    auto slab = [&](int t, auto tm, bool dmas, bool tail, bool N, Frags &af, Frags &bf, Frags &an, Frags &bn) {
+    // odd slabs issue DMAs: the 16 instructions of pair (t+3)/2, from `src`)
+    auto slab = [&](int t, auto tm, bool dmas, bool tail, bool N, const PairSrc &src, Frags &af, Frags &bf,
+                    Frags &an, Frags &bn) {
         constexpr int m = decltype(tm)::value;
         constexpr bool odd = m & 1;
         const int q = (t + 3) / 2;
-        PairSrc src{};
-        if (odd && dmas)
-            src = pair_src(q);
         if (odd && N) {
             dma_wait(0);
             slab_barrier();
@@ -569,12 +568,37 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
         using C2 = std::integral_constant<int, 2>;
         using C3 = std::integral_constant<int, 3>;
         int s = 0;
-        // steady state: the pairs issued (s/2 + 2, s/2 + 3) are full ones
-        for (; s / 2 + 4 < npair; s += 4) {
-            slab(s + 0, C0{}, true, false, false, af, bf, an, bn);
-            slab(s + 1, C1{}, true, false, true, an, bn, af, bf);
-            slab(s + 2, C2{}, true, false, false, af, bf, an, bn);
-            slab(s + 3, C3{}, true, false, true, an, bn, af, bf);
+        // steady state: the pairs issued (s/2 + 2, s/2 + 3) are full ones.
+        // Their sources come from a cursor that advances base and window by a
+        // pair (the general pair_src, between two slabs, held up the odd
+        // slab's first MFMA): cq is the rotated index of the next pair fetched.
+        if (npair > 4) {
+            int cq = (2 + rotp) % npair;
+            const uint16_t *ca = a_t + (int64_t)cq * 64, *cb = b_t + (int64_t)cq * 64;
+            uint32_t cwa = a_win - 128u * (uint32_t)cq, cwb = b_win - 128u * (uint32_t)cq;
+            auto next_pair = [&]() {
+                const PairSrc r{make_rsrc(ca, cwa), make_rsrc(cb, cwb)};
+                ++cq;
+                ca += 64;
+                cb += 64;
+                cwa -= 128;
+                cwb -= 128;
+                if (cq == npair) { // the rotated order wraps to the first pair
+                    cq = 0;
+                    ca = a_t;
+                    cb = b_t;
+                    cwa = a_win;
+                    cwb = b_win;
+                }
+                return r;
+            };
+            const PairSrc none{};
+            for (; s / 2 + 4 < npair; s += 4) {
+                slab(s + 0, C0{}, true, false, false, none, af, bf, an, bn);
+                slab(s + 1, C1{}, true, false, true, next_pair(), an, bn, af, bf);
+                slab(s + 2, C2{}, true, false, false, none, af, bf, an, bn);
+                slab(s + 3, C3{}, true, false, true, next_pair(), an, bn, af, bf);
+            }
         }
         auto flags = [&](int t, bool &dmas, bool &tail, bool &N) {
             const bool odd = t & 1;
@@ -589,10 +613,11 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
             flags(s + 1, d1, t1, n1);
             flags(s + 2, d2, t2, n2);
             flags(s + 3, d3, t3, n3);
-            slab(s + 0, C0{}, d0, t0, n0, af, bf, an, bn);
-            slab(s + 1, C1{}, d1, t1, n1, an, bn, af, bf);
-            slab(s + 2, C2{}, d2, t2, n2, af, bf, an, bn);
-            slab(s + 3, C3{}, d3, t3, n3, an, bn, af, bf);
+            const PairSrc none{};
+            slab(s + 0, C0{}, d0, t0, n0, none, af, bf, an, bn);
+            slab(s + 1, C1{}, d1, t1, n1, pair_src((s + 4) / 2), an, bn, af, bf);
+            slab(s + 2, C2{}, d2, t2, n2, none, af, bf, an, bn);
+            slab(s + 3, C3{}, d3, t3, n3, pair_src((s + 6) / 2), an, bn, af, bf);
         }
     }
     mfma_drain();
@@ -602,27 +627,18 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
 // dW tile (OC operands).  Wave w = 2*wm + wn owns the 128x128 quadrant
 // (wm, wn) as 8x8 blocks of 16x16 (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
 // The reduction runs in slabs of 32 through a 4-slot LDS ring; one slab is one
-// k-step of 64 MFMAs per wave.
+// k-step of 64 MFMAs per wave.  The reduction order is never rotated here
+// (rotation is for the dX job's operands only).
 __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS char *smem) {
     static_assert(kDmaPerOp == 4 && kStages == 4, "pipeline below assumes 4 DMAs per operand, 4 stages");
     constexpr int kRPF = 2;                   // ds_read_b64_tr_b16 per fragment
     constexpr int kReads = 2 * kFrags * kRPF; // per wave per slab
     constexpr int kDmaPerSlab = 2 * kDmaPerOp;
-    int ti, tj;
-    tile_coords(jb, t_index, ti, tj);
-    const int64_t i0 = (int64_t)ti * kTile;
-    const int64_t j0 = (int64_t)tj * kTile;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // wave-uniform
     const int wm = w >> 1, wn = w & 1;
 
-    // slab-independent per-lane offsets: DMA sources and LDS fragment addresses
-    uint32_t va[kDmaPerOp], vb[kDmaPerOp];
-#pragma unroll
-    for (int p = 0; p < kDmaPerOp; ++p) {
-        va[p] = dma_oc_off(p, jb.lda, jb.I, i0, w, lane);
-        vb[p] = dma_oc_off(p, jb.ldb, jb.J, j0, w, lane);
-    }
+    // LDS fragment addresses: the same for every tile
     int fo[2][kFrags][kRPF]; // [A/B][block][half]
 #pragma unroll
     for (int x = 0; x < kFrags; ++x)
@@ -632,23 +648,37 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
             fo[1][x][h] = kBOffset + frag_off_oc(wn * 128 + x * 16, lane, h);
         }
 
-    f32x4_t acc[kFrags][kFrags];
-#pragma unroll
-    for (int x = 0; x < kFrags; ++x)
-#pragma unroll
-        for (int y = 0; y < kFrags; ++y)
-            acc[x][y] = f32x4_t{};
-
     const int nslab = (int)((jb.R + kBK - 1) / kBK);
-    // optional rotation of the reduction order (see TileJob)
-    const int rot = nslab == 0 ? 0 : (jb.rot * ((tj >> 1) & 3)) % nslab;
-    // per-slab source advance (elements) of each operand
+    // The slab count is padded to a multiple of the ring size with slabs that
+    // read zero, so every pass of the loops below runs four whole slabs with
+    // compile-time ring slots and no early exit.
+    const int nslab4 = (nslab + kStages - 1) / kStages * kStages;
+    // per-slab source advance (elements) and a full slab's bytes, per operand
+    // (32 rows of ld < 2^25: below 2^31 bytes)
     const int64_t step_a = (int64_t)kBK * jb.lda;
     const int64_t step_b = (int64_t)kBK * jb.ldb;
+    const uint32_t full_a = (uint32_t)(2 * step_a);
+    const uint32_t full_b = (uint32_t)(2 * step_b);
     LDS char *const wdst = smem + w * kDmaPerOp * 1024; // this wave's DMA destinations
 
-    // Buffer descriptors for slab s: the base advances to the slab (scalar work
-    // only) and the size shrinks to the rows left, so rows past R read zero.
+    int ti, tj;
+    tile_coords(jb, t_index, ti, tj);
+    const int64_t i0 = (int64_t)ti * kTile;
+    const int64_t j0 = (int64_t)tj * kTile;
+    // slab-independent per-lane DMA source offsets
+    uint32_t va[kDmaPerOp], vb[kDmaPerOp];
+#pragma unroll
+    for (int p = 0; p < kDmaPerOp; ++p) {
+        va[p] = dma_oc_off(p, jb.lda, jb.I, i0, w, lane);
+        vb[p] = dma_oc_off(p, jb.ldb, jb.J, j0, w, lane);
+    }
+
+    // Buffer descriptors for slab s: the base at the slab's first row, the size
+    // the rows left, so rows past R read zero.  The general form (padding
+    // slabs, a partial last slab) serves the prologue and the last groups;
+    // the steady state advances two pointers by a slab instead (the general
+    // form's 64-bit products, done between two slabs, held up the first MFMA
+    // of every slab).
     struct SlabSrc {
         __amdgpu_buffer_rsrc_t a, b;
     };
@@ -659,17 +689,14 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
             r.b = make_rsrc(jb.b, 0);
             return r;
         }
-        s += rot;
-        s = s >= nslab ? s - nslab : s;
-        // the slab's rows only (32 rows of ld < 2^25: below 2^31 bytes)
         const int64_t rows = min<int64_t>(kBK, jb.R - (int64_t)s * kBK);
         r.a = make_rsrc(jb.a + s * step_a, (uint32_t)(2 * rows * jb.lda));
         r.b = make_rsrc(jb.b + s * step_b, (uint32_t)(2 * rows * jb.ldb));
         return r;
     };
-    // DMA instruction p of operand op for slab s
-    auto dma = [&](const SlabSrc &src, int s, int op, int p) {
-        LDS char *st = wdst + (s % kStages) * kOperandBytes + p * 1024 + op * kBOffset;
+    // DMA instruction p of operand op for a slab in ring slot `slot`
+    auto dma = [&](const SlabSrc &src, int slot, int op, int p) {
+        LDS char *st = wdst + slot * kOperandBytes + p * 1024 + op * kBOffset;
         dma16(op == 0 ? src.a : src.b, st, op == 0 ? va[p] : vb[p]);
     };
     // Read LDS read number j (0 .. kReads-1) of a slab held in ring slot `stage`
@@ -699,33 +726,32 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
     // Slab s (fragments already in af/bf):
     //   if there is a slab s+1: wait for its DMA and barrier.  After the
     //   barrier every wave has its slab-s fragments in registers, so ring slot
-    //   s%4 is free and takes the DMA of slab s+4;
+    //   s%4 is free and takes the DMA (source src) of slab s+4;
     //   64 MFMAs on (af, bf); the LDS reads of slab s+1 into (an, bn) go with
-    //   the first MFMAs, the DMA of slab s+4 with later ones (sched_barrier pins
-    //   the order, so the matrix pipe never waits behind address or memory work).
+    //   the first MFMAs, the DMA with later ones (sched_barrier pins the order,
+    //   so the matrix pipe never waits behind address or memory work).
     //   The last slab reads its successor's ring slot too (stale data, never
     //   used): keeping the reads unconditional lets the transposed halves share
     //   registers with the fragments they form.
-    // wait_n: this wave's DMA instructions issued after slab s+1's.
-    // Called with constant flags in the steady state (inlining folds them away)
-    // and with run-time flags in the few peeled and draining iterations.
-    // stage: the ring slot of slab s, as a compile-time constant (unrolled steady
-    // state) or an int; the next slab's slot is derived the same way.
-    auto next_stage = [](auto st) {
-        if constexpr (std::is_integral_v<decltype(st)>)
-            return (st + 1) % kStages;
-        else
-            return std::integral_constant<int, (decltype(st)::value + 1) % kStages>{};
-    };
+    // wait_n: this wave's DMA instructions issued after the following slab's.
+    // stage: the ring slot of slab s, a compile-time constant; the next slab's
+    // slot is derived from it.
     constexpr int kReadSlot = 1; // MFMA slots per LDS read
     // DMA j after MFMA kDmaSlot0 + kDmaStep*j (33, 37, ..., 61): spaced so the
     // four waves' instructions stay within the CU's address rate (every second
     // MFMA filled the address FIFO; block 1.9% slower)
     constexpr int kDmaSlot0 = 33;
     constexpr int kDmaStep = 4;
-    auto slab = [&](int s, auto stage, bool dmas, bool N, int wait_n, Frags &af, Frags &bf, Frags &an,
-                    Frags &bn) {
-        const SlabSrc src = dmas ? slab_src(s + kStages) : SlabSrc{};
+    f32x4_t acc[kFrags][kFrags];
+#pragma unroll
+    for (int x = 0; x < kFrags; ++x)
+#pragma unroll
+        for (int y = 0; y < kFrags; ++y)
+            acc[x][y] = f32x4_t{};
+    auto slab = [&](auto stage, bool dmas, const SlabSrc &src, bool N, int wait_n, Frags &af, Frags &bf,
+                    Frags &an, Frags &bn) {
+        constexpr int slot = decltype(stage)::value;
+        using Next = std::integral_constant<int, (slot + 1) % kStages>;
         if (N) {
             dma_wait(wait_n);
             slab_barrier();
@@ -738,22 +764,24 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
             mfma16(acc[x][y], bf[y], af[x]);
             __builtin_amdgcn_sched_barrier(0);
             if (i % kReadSlot == 0 && i / kReadSlot < kReads)
-                read_frag(next_stage(stage), i / kReadSlot, tr);
+                read_frag(Next{}, i / kReadSlot, tr);
             if (dmas && i >= kDmaSlot0 && i < kDmaSlot0 + kDmaStep * kDmaPerSlab &&
                 (i - kDmaSlot0) % kDmaStep == 0) {
                 const int d = (i - kDmaSlot0) / kDmaStep;
-                dma(src, s + kStages, d & 1, d >> 1);
+                dma(src, slot, d & 1, d >> 1);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         finish_reads(an, bn, tr);
         __builtin_amdgcn_sched_barrier(0);
     };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    constexpr int kW = 2 * kDmaPerSlab; // steady state: the two slabs after the next may be in flight
+    const SlabSrc none{};
     Frags af, bf, an, bn;
-    // The slab count is padded to a multiple of the ring size with slabs that
-    // read zero, so every pass of the loops below runs four whole slabs with
-    // compile-time ring slots and no early exit.
-    const int nslab4 = (nslab + kStages - 1) / kStages * kStages;
     if (nslab > 0) {
         // prologue: slabs 0..3 fill the ring; wait for slab 0 and read it
         for (int s = 0; s < kStages; ++s) {
@@ -773,27 +801,35 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
                 read_frag(0, j, tr);
             finish_reads(af, bf, tr);
         }
-        // steady state: slabs s+1..s+3 exist and slab s+4 is a full slab, branch free
-        constexpr int kW = 2 * kDmaPerSlab; // slabs s+2 and s+3 may be in flight
         int s = 0;
-        for (; s + 2 * kStages < nslab; s += kStages) {
-            slab(s + 0, std::integral_constant<int, 0>{}, true, true, kW, af, bf, an, bn);
-            slab(s + 1, std::integral_constant<int, 1>{}, true, true, kW, an, bn, af, bf);
-            slab(s + 2, std::integral_constant<int, 2>{}, true, true, kW, af, bf, an, bn);
-            slab(s + 3, std::integral_constant<int, 3>{}, true, true, kW, an, bn, af, bf);
-        }
-        // the rest (last DMAs, then draining), with run-time flags that only gate
-        // DMA issue and barriers
-        auto slab_rt = [&](int t, auto stage, Frags &a, Frags &b, Frags &a2, Frags &b2) {
-            slab(t, stage, t + kStages < nslab4, t + 1 < nslab4,
-                 kDmaPerSlab * ((t + 2 < nslab4) + (t + 3 < nslab4)), a, b, a2, b2);
+        // steady state: slab s+4 is a full slab, branch free; pa / pb point at
+        // the slab the next DMA fetches
+        const uint16_t *pa = jb.a + 4 * step_a;
+        const uint16_t *pb = jb.b + 4 * step_b;
+        auto next_src = [&]() {
+            const SlabSrc r{make_rsrc(pa, full_a), make_rsrc(pb, full_b)};
+            pa += step_a;
+            pb += step_b;
+            return r;
         };
-        for (; s < nslab4; s += kStages) {
-            slab_rt(s + 0, std::integral_constant<int, 0>{}, af, bf, an, bn);
-            slab_rt(s + 1, std::integral_constant<int, 1>{}, an, bn, af, bf);
-            slab_rt(s + 2, std::integral_constant<int, 2>{}, af, bf, an, bn);
-            slab_rt(s + 3, std::integral_constant<int, 3>{}, an, bn, af, bf);
+        for (; s + 2 * kStages < nslab; s += kStages) {
+            slab(C0{}, true, next_src(), true, kW, af, bf, an, bn);
+            slab(C1{}, true, next_src(), true, kW, an, bn, af, bf);
+            slab(C2{}, true, next_src(), true, kW, af, bf, an, bn);
+            slab(C3{}, true, next_src(), true, kW, an, bn, af, bf);
         }
+        // the groups whose DMA targets may be partial or padding slabs
+        for (; s + kStages < nslab4; s += kStages) {
+            slab(C0{}, true, slab_src(s + 4), true, kW, af, bf, an, bn);
+            slab(C1{}, true, slab_src(s + 5), true, kW, an, bn, af, bf);
+            slab(C2{}, true, slab_src(s + 6), true, kW, af, bf, an, bn);
+            slab(C3{}, true, slab_src(s + 7), true, kW, an, bn, af, bf);
+        }
+        // draining: no more DMAs; slab t waits for t+1 while one exists
+        slab(C0{}, false, none, true, kDmaPerSlab * 2, af, bf, an, bn);
+        slab(C1{}, false, none, true, kDmaPerSlab * 1, an, bn, af, bf);
+        slab(C2{}, false, none, true, 0, af, bf, an, bn);
+        slab(C3{}, false, none, false, 0, an, bn, af, bf);
     }
 
     mfma_drain();
