@@ -311,8 +311,10 @@ const char *lb_version(void);
  * stream (the gradient norm's partial sums, lin_bwd_ex's bias partials and
  * lin_bwd's dX partials for bf16 with 1 <= M <= 1024, allocated on first use
  * per device and stream; without this call they are kept until the process
- * ends).  A later call that
- * needs a workspace allocates it again.  No call of this library may be in
+ * ends) and destroys each device's memory pool of lin_bwd's padded copies
+ * (ragged or unaligned bf16 calls).  A later call that needs a workspace or
+ * a pool makes it again.  The static array of lin_bwd_ex_noalloc is not
+ * freed: it lives as long as the process.  No call of this library may be in
  * flight on any device, on any stream, nor may another thread call into the
  * library meanwhile: the caller synchronizes first.  The calling thread's
  * current device is unchanged.  Returns LB_OK, or LB_EHIP
