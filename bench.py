@@ -700,7 +700,7 @@ def main(argv=None):
                          "scaling HBM byte counters; calib = the calibration kernels")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU; --gpus %d is not supported "
+        print("bench.py: one GPU only; --gpus %d is not supported "
               "(the multi-GPU sharding is a design note, not code)" % args.gpus, file=sys.stderr)
         return 2
     import torch
