@@ -269,7 +269,9 @@ int lb_set_stream(void *hip_stream);
  * the kernels can be compared with each other on the same inputs and a
  * caller can pin a choice; every path computes the same sums, rounded once.
  *   LB_PATH_AUTO     chosen by dtype, alignment and M (the default)
- *   LB_PATH_TILE     both products on the 256x256 MFMA tile kernel
+ *   LB_PATH_TILE     both products on the 256x256 MFMA tile kernel (for
+ *                    M <= 1024 with dX's reduction split over several tiles
+ *                    when that shortens the launch)
  *   LB_PATH_SMALL_M  dX on the split-reduction kernel (M <= 1024), dW on the
  *                    small-tile kernel (M <= 256)
  *   LB_PATH_GENERAL  both products on the element-wise kernel

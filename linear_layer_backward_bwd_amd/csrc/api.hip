@@ -176,8 +176,11 @@ int lin_bwd_impl(const char *name, const void *X, const void *W, const void *dY,
             bias_partial = ws.bias_partial;
         }
     }
-    a.dx_partial = dx_partial;
-    a.dx_partial_floats = dx_partial ? lb::kDxPartialFloats : 0;
+    // the dX partials only where every entry point passes them (bf16,
+    // 1 <= M <= 1024), so that lin_bwd and lin_bwd_ex with or without db
+    // choose the same splits and give the same bits
+    a.dx_partial = small_dx ? dx_partial : nullptr;
+    a.dx_partial_floats = a.dx_partial ? lb::kDxPartialFloats : 0;
     hipError_t e = lb::launch_lin_bwd(a, tl_stream);
     if (e != hipSuccess)
         return hip_fail(name, e);

@@ -55,6 +55,7 @@ constexpr int kBOffset = kStages * kOperandBytes;  // all A slabs first, then al
 constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
 constexpr int kDmaPerOp = kBK / 8;                // DMA instructions per wave per operand per slab
 constexpr int kGroupI = 4;                        // tile rows per raster group
+constexpr int kCUs = 256;                         // compute units of the part (8 XCDs x 32)
 constexpr uint32_t kOOB = 0x80000000u;            // buffer offset past num_records: reads 0
 
 #define LDS __attribute__((address_space(3)))
@@ -92,12 +93,20 @@ struct TileJob {
     void *c;           // output, row-major [I, J], leading dim J
     int64_t I, J, R;   // output rows, cols, reduction length
     int64_t lda, ldb;  // leading dims of a and b in elements
-    int tiles_i, tiles_j, ntiles;
+    int tiles_i, tiles_j, ntiles; // ntiles = tiles_i * tiles_j * splits
     int kind;          // JOB_DX: RC operands, bf16 out; JOB_DW: OC operands, fp32 out
     // k rotation (slabs), dX (RC) jobs only: the tile at (ti, tj) walks the
     // slabs starting at rot * ((tj / 2) % 4) mod nslab (0 for a ragged
     // reduction)
     int rot;
+    // dX jobs only: the reduction split into `splits` ranges of split_len
+    // elements (a whole number of 64-element pairs; the last range may be
+    // shorter); with splits > 1 the tiles of range s write fp32 partial sums
+    // to part + s*I*J, which a later launch adds in range order, instead of
+    // bf16 sums to c
+    int splits;
+    int64_t split_len;
+    float *part;
 };
 
 struct MfmaParams {
@@ -283,10 +292,14 @@ __device__ __forceinline__ void slab_barrier() {
 // different XCDs (round-robin dispatch), so first gather each XCD's blocks
 // into one contiguous range of tiles, then raster that range in groups of
 // kGroupI tile rows so concurrently running tiles share operand panels in L2.
-__device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, int &tj) {
+__device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, int &tj, int &sp) {
     int u = t;
     if ((jb.ntiles & 7) == 0)
         u = (t & 7) * (jb.ntiles >> 3) + (t >> 3);
+    // the reduction range: consecutive tiles of an XCD share it (and their panels)
+    const int tps = jb.tiles_i * jb.tiles_j;
+    sp = u / tps;
+    u -= sp * tps;
     const int per_group = kGroupI * jb.tiles_j;
     const int group = u / per_group;
     const int first_i = group * kGroupI;
@@ -313,8 +326,14 @@ __device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, i
 // alternated read, wait, store: one LDS round trip per 1 KiB store, 4.4 us per
 // dX and 4.6-5.4 us per dW tile at M = 2048.)
 constexpr int kEpiBytes = 8192; // per wave
+// An output: row-major [I, J], leading dimension J (bf16 for KIND == JOB_DX,
+// fp32 for JOB_DW).
+struct OutView {
+    void *c;
+    int64_t I, J;
+};
 template <int KIND, bool FULL>
-__device__ __forceinline__ void store_quadrant(const f32x4_t (&acc)[kFrags][kFrags], const TileJob &jb,
+__device__ __forceinline__ void store_quadrant(const f32x4_t (&acc)[kFrags][kFrags], const OutView &jb,
                                                int64_t ib, int64_t jb0, int w, int lane, LDS char *smem) {
     LDS char *const reg = smem + kLdsBytes + w * kEpiBytes;
     if constexpr (KIND == JOB_DX) {
@@ -384,7 +403,7 @@ __device__ __forceinline__ void store_quadrant(const f32x4_t (&acc)[kFrags][kFra
     }
 }
 template <int KIND>
-__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[kFrags][kFrags], const TileJob &jb, int64_t i0,
+__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[kFrags][kFrags], const OutView &jb, int64_t i0,
                                            int64_t j0, int w, int wm, int wn, int lane, LDS char *smem) {
     const int64_t ib = i0 + wm * 128;
     const int64_t jb0 = j0 + wn * 128;
@@ -435,11 +454,12 @@ __device__ __forceinline__ uint32_t dma_rcp_off(int p, int64_t ld, int64_t O, in
 // (the four waves' 64 instructions of 1 KiB over 64 MFMAs); issued every
 // second MFMA, or half of them in the next slab, the address FIFO filled, the
 // waves stalled unevenly and the barrier paid for the skew (block 1.8% slower).
+template <bool SPLIT> // SPLIT: the job's reduction is split (fp32 partials out)
 __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS char *smem) {
     static_assert(kStages * kOperandBytes == 2 * kPairBytes, "two pairs per operand");
     constexpr int kReads = 2 * kFrags; // ds_read_b128 per wave per slab
-    int ti, tj;
-    tile_coords(jb, t_index, ti, tj);
+    int ti, tj, sp;
+    tile_coords(jb, t_index, ti, tj, sp);
     const int64_t i0 = (int64_t)ti * kTile;
     const int64_t j0 = (int64_t)tj * kTile;
     const int lane = threadIdx.x & 63;
@@ -467,7 +487,9 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
         for (int y = 0; y < kFrags; ++y)
             acc[x][y] = f32x4_t{};
 
-    const int64_t R = jb.R;
+    // this tile's reduction range: [kb, kb + R) of the job's (one range unless split)
+    const int64_t kb = (int64_t)sp * jb.split_len;
+    const int64_t R = min<int64_t>(jb.split_len, jb.R - kb);
     const int npair = (int)((R + 63) / 64);
     const int nslab4 = (int)(((R + kBK - 1) / kBK + 3) / 4 * 4); // padded with zero slabs
     const int P = nslab4 / 2;                                     // pairs, padding included
@@ -475,11 +497,12 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
     // rotation of the reduction order (see TileJob), in whole pairs
     const int rotp = ptail || npair == 0 ? 0 : ((jb.rot * ((tj >> 1) & 3)) >> 1) % npair;
     LDS char *const wdst = smem + w * kDmaPerOpPair * 1024;
-    // the tile's operand rows: windows of at most 256 rows (2 * 256 * ld < 2^31)
-    const uint16_t *const a_t = jb.a + i0 * jb.lda;
-    const uint16_t *const b_t = jb.b + j0 * jb.ldb;
-    const uint32_t a_win = (uint32_t)(2 * min<int64_t>(kTile, jb.I - i0) * jb.lda);
-    const uint32_t b_win = (uint32_t)(2 * min<int64_t>(kTile, jb.J - j0) * jb.ldb);
+    // the tile's operand rows from the range's first column: windows of at
+    // most 256 rows (2 * 256 * ld < 2^31), from a_t / b_t to the window's end
+    const uint16_t *const a_t = jb.a + i0 * jb.lda + kb;
+    const uint16_t *const b_t = jb.b + j0 * jb.ldb + kb;
+    const uint32_t a_win = (uint32_t)(2 * (min<int64_t>(kTile, jb.I - i0) * jb.lda - kb));
+    const uint32_t b_win = (uint32_t)(2 * (min<int64_t>(kTile, jb.J - j0) * jb.ldb - kb));
 
     struct PairSrc {
         __amdgpu_buffer_rsrc_t a, b;
@@ -621,7 +644,13 @@ __device__ __forceinline__ void run_tile_rc(const TileJob &jb, int t_index, LDS 
         }
     }
     mfma_drain();
-    store_tile<JOB_DX>(acc, jb, i0, j0, w, wm, wn, lane, smem);
+    // (one epilogue per instantiation: with both behind a run-time branch the
+    // compiler copied the accumulators out of the AGPRs before it and spilled)
+    if constexpr (SPLIT) // fp32 partial sums of range sp
+        store_tile<JOB_DW>(acc, OutView{jb.part + (int64_t)sp * jb.I * jb.J, jb.I, jb.J}, i0, j0, w, wm, wn, lane,
+                           smem);
+    else
+        store_tile<JOB_DX>(acc, OutView{jb.c, jb.I, jb.J}, i0, j0, w, wm, wn, lane, smem);
 }
 
 // dW tile (OC operands).  Wave w = 2*wm + wn owns the 128x128 quadrant
@@ -661,8 +690,8 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
     const uint32_t full_b = (uint32_t)(2 * step_b);
     LDS char *const wdst = smem + w * kDmaPerOp * 1024; // this wave's DMA destinations
 
-    int ti, tj;
-    tile_coords(jb, t_index, ti, tj);
+    int ti, tj, sp;
+    tile_coords(jb, t_index, ti, tj, sp); // one reduction range: sp = 0
     const int64_t i0 = (int64_t)ti * kTile;
     const int64_t j0 = (int64_t)tj * kTile;
     // slab-independent per-lane DMA source offsets
@@ -833,10 +862,13 @@ __device__ __forceinline__ void run_tile_oc(const TileJob &jb, int t_index, LDS 
     }
 
     mfma_drain();
-    store_tile<JOB_DW>(acc, jb, i0, j0, w, wm, wn, lane, smem);
+    store_tile<JOB_DW>(acc, OutView{jb.c, jb.I, jb.J}, i0, j0, w, wm, wn, lane, smem);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
+// One block = one tile of job 0 or job 1.  SPLIT: the dX job (if any) has its
+// reduction split into several ranges (k_lin_bwd_mfma_split).
+template <bool SPLIT>
+__device__ __forceinline__ void lin_bwd_mfma_block(const MfmaParams &p) {
     __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes + 4 * kEpiBytes];
     LDS char *smem = (LDS char *)smem_raw;
     int b = blockIdx.x;
@@ -846,23 +878,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) {
         jb = &p.job[1];
     }
     if (jb->kind == JOB_DX)
-        run_tile_rc(*jb, b, smem);
+        run_tile_rc<SPLIT>(*jb, b, smem);
     else
         run_tile_oc(*jb, b, smem);
 }
+__global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma(MfmaParams p) { lin_bwd_mfma_block<false>(p); }
+__global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma_split(MfmaParams p) { lin_bwd_mfma_block<true>(p); }
 
 // ------------------------------------------------------------------------
 // small M: at M <= 64 both products are bound by HBM, not MFMA: dX streams W
-// (2KN bytes), dW writes the fp32 output (4KN bytes).  Up to M = 1024 the tile
-// kernel would give dX only (M/256)(K/256) tiles, so dX keeps the
-// split-reduction kernel (dW returns to the tile kernel above M = 256).  They
-// run as two launches.  (One launch holding the blocks of both was slower where it
+// (2KN bytes), dW writes the fp32 output (4KN bytes).  Up to M = 256 dX takes
+// the split-reduction kernel below and dW the small-tile kernel, as two
+// launches; from M = 257 to 1024, where dW returns to the tile kernel, dX joins
+// it there with its reduction split over several tiles (the tile kernel with
+// whole reductions would give dX only (M/256)(K/256) long tiles).  (One launch holding the blocks of both was slower where it
 // mattered: the dX blocks took every CU first, the dW blocks then ran at the
 // merged kernel's lower occupancy, and at N = 16384 the mixed read and write
 // streams made it 40% slower than the two launches in turn.)
 // ------------------------------------------------------------------------
 constexpr int kSmallMaxM = 256;   // dW: the small-tile kernel up to this M
-constexpr int kSmallMaxDxM = 1024; // dX: the split-reduction kernel up to this M (row groups above 256)
+constexpr int kSmallMaxDxM = 1024; // dX: split reductions (either kernel) up to this M
 
 struct SmallParams {
     const uint16_t *X, *W, *G; // X[M,K], W[K,N], dY[M,N]
@@ -1631,7 +1666,39 @@ TileJob make_tile_job(int kind, const void *a, const void *b, void *c, int64_t I
     j.ntiles = j.tiles_i * j.tiles_j;
     j.kind = kind;
     j.rot = 0;
+    j.splits = 1;
+    j.split_len = R;
+    j.part = nullptr;
     return j;
+}
+
+// From this M on (up to kSmallMaxDxM), dX takes the tile kernel with a split
+// reduction instead of the small-M kernel when the path is chosen
+// automatically: there dW has left the small-tile kernel, and the split dX
+// tiles share one launch with the dW tiles (measured at K = N = 4096, both
+// products: M = 320 64.1 -> 49.2 us, 512 69.2 -> 57.6, 768 105.0 -> 78.2,
+// 1024 101.4 -> 82.7; M = 1024, K = 16384 377.8 -> 251.9).  At M <= 256 the
+// split tiles were no faster than the small-M kernel for dX alone, and slower
+// with K = 16384 (75.9 vs 66.6 us at M = 256).
+constexpr int64_t kTileSplitMinDxM = kSmallMaxM + 1;
+
+// Reduction ranges for a dX tile job: with few dX tiles (small M) one tile's
+// reduction would outlast the launch, so it is split until one range is no
+// longer than the launch's average per CU (or than a dW tile in the same
+// launch), in powers of two up to kDxsMaxSplits, with every range's fp32
+// partials [M, K] within the workspace.
+int tile_dx_splits(const LinBwdArgs &a, const TileJob &jx, const TileJob *jw) {
+    const int64_t xs = (jx.R + kBK - 1) / kBK; // slabs per dX tile
+    int64_t total = (int64_t)jx.ntiles * xs, other = 0;
+    if (jw) {
+        other = (jw->R + kBK - 1) / kBK;
+        total += (int64_t)jw->ntiles * other;
+    }
+    const int64_t target = std::max((total + kCUs - 1) / kCUs, other);
+    int sx = 1;
+    while (sx < kDxsMaxSplits && (xs + sx - 1) / sx > target && 2 * sx * a.M * a.K <= a.dx_partial_floats)
+        sx *= 2;
+    return sx;
 }
 
 // Which MFMA kernel can run which product.  Every kernel reads 16-byte chunks
@@ -1908,9 +1975,12 @@ hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_d
         return launch_fused_small(a, s);
     // per product: the small-M kernel (not for the empty sums, N = 0 for dX and
     // M = 0 for dW, which the tile kernel writes as zeros), else the tile
-    // kernel, else the element-wise kernel
+    // kernel, else the element-wise kernel.  From M = kTileSplitMinDxM on, dX
+    // takes the tile kernel with its reduction split over several tiles (fp32
+    // partials in the workspace) instead of the small-M kernel.
     const bool small_ok = a.path != PATH_TILE;
-    const bool small_dx = need_dx && a.N > 0 && small_ok && e.small_dx;
+    const bool small_dx = need_dx && a.N > 0 && small_ok && e.small_dx &&
+                          !(a.path == PATH_AUTO && a.M >= kTileSplitMinDxM && a.dx_partial != nullptr);
     const bool small_dw = need_dw && small_ok && e.small_dw;
     const bool tile_dx = need_dx && !small_dx && e.tile_dx;
     const bool tile_dw = need_dw && !small_dw && e.tile_dw;
@@ -1945,6 +2015,15 @@ hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_d
         jw = make_tile_job(JOB_DW, a.X, a.dY, a.dW, a.K, a.N, a.M, a.K, a.N);
         have_w = true;
     }
+    if (have_x && a.dx_partial != nullptr && a.N > 0) {
+        const int sx = tile_dx_splits(a, jx, have_w ? &jw : nullptr);
+        if (sx > 1) {
+            jx.split_len = ((a.N + sx - 1) / sx + 63) / 64 * 64;
+            jx.splits = (int)((a.N + jx.split_len - 1) / jx.split_len);
+            jx.part = a.dx_partial;
+            jx.ntiles *= jx.splits;
+        }
+    }
     // longest reduction first: those tiles start on the first wave of CUs
     if (have_x && have_w) {
         if (jw.R > jx.R) {
@@ -1964,23 +2043,30 @@ hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_d
         const int64_t blocks = (int64_t)p.job[0].ntiles + (nj > 1 ? p.job[1].ntiles : 0);
         if (blocks > 0x7fffffff)
             return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(k_lin_bwd_mfma, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+        if (have_x && jx.splits > 1)
+            hipLaunchKernelGGL(k_lin_bwd_mfma_split, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+        else
+            hipLaunchKernelGGL(k_lin_bwd_mfma, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
-    if (small_dx || small_dw) {
+    // the dX partials of a split tile job are added (in range order) by the
+    // small-M dW launch when there is one, else by a launch of their own
+    const int tile_splits = have_x && jx.splits > 1 ? jx.splits : 1;
+    if (small_dx || small_dw || tile_splits > 1) {
         SmallParams sp{};
         sp.X = static_cast<const uint16_t *>(a.X);
         sp.W = static_cast<const uint16_t *>(a.W);
         sp.G = static_cast<const uint16_t *>(a.dY);
-        sp.dX = small_dx ? static_cast<uint16_t *>(a.dX) : nullptr;
+        sp.dX = small_dx || tile_splits > 1 ? static_cast<uint16_t *>(a.dX) : nullptr;
         sp.dW = small_dw ? a.dW : nullptr;
         sp.M = a.M;
         sp.K = a.K;
         sp.N = a.N;
-        sp.splits = 1;
-        int64_t reduce_quads = 0;
+        sp.splits = tile_splits;
+        sp.part = a.dx_partial;
+        int64_t reduce_quads = tile_splits > 1 ? a.M * a.K / 4 : 0;
         if (small_dx) {
             // splits of the reduction: aim at ~256 blocks (one per CU; a block
             // streams its chunks through its ring), each split a whole number of
