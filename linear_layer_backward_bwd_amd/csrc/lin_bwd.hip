@@ -22,11 +22,14 @@
 //                    One launch runs the tiles of both products; blocks are ordered
 //                    longest reduction first and mapped so that each XCD works on a
 //                    compact group of tiles.
-//   k_dx_smallm      dX for M <= 1024 (decode-like and small batches): streams W
-//                    once per 256-row group, the reduction over n split across
-//                    blocks; the fp32 partials are added in split order by the
-//                    first blocks of k_dw_smallm (M <= 256), else by
-//                    k_dx_smallm_reduce.
+//   k_lin_bwd_mfma_split  the same with dX's reduction split into ranges whose
+//                    tiles write fp32 partials (257 <= M <= 1024, where dX alone
+//                    would give few, long tiles); k_dx_smallm_reduce adds them.
+//   k_dx_smallm      dX for M <= 256 (decode-like and small batches; up to 1024
+//                    on request): streams W once per 256-row group, the reduction
+//                    over n split across blocks; the fp32 partials are added in
+//                    split order by the first blocks of k_dw_smallm (M <= 256),
+//                    else by k_dx_smallm_reduce.
 //   k_dw_smallm      dW for M <= 256: bound by writing the fp32 output at small M;
 //                    small tiles, several per CU, so stores overlap other tiles' loads.
 //   k_lin_bwd_fused_small  both products for M <= 64 in one launch (on request).
