@@ -204,6 +204,7 @@ def calibrate(reps=10):
 
 
 KERNEL_SOURCES = {"k_lin_bwd_mfma": "linear_layer_backward_bwd_amd/csrc/lin_bwd.hip",
+                  "k_lin_bwd_mfma_split": "linear_layer_backward_bwd_amd/csrc/lin_bwd.hip",
                   "k_dw_smallm": "linear_layer_backward_bwd_amd/csrc/lin_bwd.hip",
                   "k_adamw": "linear_layer_backward_bwd_amd/csrc/adamw.hip",
                   "k_norm_partial": "linear_layer_backward_bwd_amd/csrc/grad_norm.hip",
@@ -495,7 +496,8 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
         floor["what"] = ("the calibration read kernel over the bytes the call reads (bf16 X, W, dY) "
                          "plus the write kernel over the bytes it writes (bf16 dX, fp32 dW), cold, "
                          "an event pair around each launch, medians")
-    kernel = "k_dw_smallm" if M <= 64 else "k_lin_bwd_mfma"
+    kernel = ("k_dw_smallm" if M <= 64 else "k_lin_bwd_mfma_split" if 256 < M <= 1024 and N > 0
+              else "k_lin_bwd_mfma")
     return {"M": M, "K": K, "N": N, "ms": round(ms, 5), "tflops": round(tf, 1),
             "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "bound": "hbm" if roofs["pages"] < PEAK_BF16_TFLOPS else "mfma",
@@ -693,7 +695,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the M=32 / M=2048 / 2^28-param AdamW figures")
-    ap.add_argument("--only", choices=["block", "m32", "m2048", "adamw", "clipped", "bias", "softmax",
+    ap.add_argument("--only", choices=["block", "m32", "m1024", "m2048", "adamw", "clipped", "bias", "softmax",
                                        "copycal", "calib"],
                     default=None,
                     help="time one workload only (for profiling); copycal = 1 GiB copies for "
@@ -710,8 +712,8 @@ def main(argv=None):
     import linear_layer_backward_bwd_amd as lb
     lb.library()
 
-    if args.only in ("m32", "m2048"):
-        M = 32 if args.only == "m32" else 2048
+    if args.only in ("m32", "m1024", "m2048"):
+        M = int(args.only[1:])
         print(json.dumps(bench_linear(M, 4096, 4096, args.steps, args.warmup, args.seed)), flush=True)
         return 0
     if args.only == "adamw":
@@ -764,6 +766,8 @@ def main(argv=None):
         out["also"] = {
             "lin_bwd_M32_K4096_N4096": bench_linear(32, 4096, 4096, 50, 5, args.seed),
             "lin_bwd_M2048_K4096_N4096": bench_linear(2048, 4096, 4096, 50, 5, args.seed),
+            # the block's shard on 16 data-parallel ranks: dX with its reduction split over tiles
+            "lin_bwd_M1024_K4096_N4096": bench_linear(1024, 4096, 4096, 50, 5, args.seed),
             # the down projection at 65536 tokens: X and dX of 2 GiB each
             "lin_bwd_M65536_K16384_N4096": bench_linear(65536, 16384, 4096, 3, 1, args.seed,
                                                         rotate_bytes=0),
@@ -777,7 +781,7 @@ def main(argv=None):
             "bias_grad_block": bench_bias(20, 3, args.seed),
             "softmax_bwd_attention": bench_softmax(10, 2, args.seed),
         }
-        for key in ("lin_bwd_M32_K4096_N4096", "lin_bwd_M2048_K4096_N4096"):
+        for key in ("lin_bwd_M32_K4096_N4096", "lin_bwd_M1024_K4096_N4096", "lin_bwd_M2048_K4096_N4096"):
             out["also"][key]["frac_of_measured_mfma_peak"] = round(
                 out["also"][key]["tflops"] / cal["mfma_bf16_tflops"], 4)
         m32 = out["also"]["lin_bwd_M32_K4096_N4096"]
