@@ -50,9 +50,10 @@ def check(case, got, ref):
         assert relf(db.cpu().numpy(), oracle.bias_grad(Gb, "bf16")) <= DB_RELF
 
 
-# (M, K, N): M = 200 sums dX in 16 splits and db in row splits, both through the array;
-# the second call is smaller (M = 40: 4 splits) and reads back only what it wrote
-SHAPES = [(200, 1032, 4104), (40, 520, 1032)]
+# (M, K, N), each call smaller than the one before: M = 600 sums dX in 8 ranges on the tile
+# kernel, M = 200 in 16 splits on the small-M kernel, and db in row splits, all through the
+# array; M = 40 (4 splits) reads back only what it wrote
+SHAPES = [(600, 1032, 4104), (200, 1032, 4104), (40, 520, 1032)]
 
 
 def test_noalloc_matches_lin_bwd_ex_two_calls_in_a_row():
@@ -87,13 +88,16 @@ def test_noalloc_through_the_binding():
         assert torch.equal(a, b)
 
 
-def test_noalloc_replays_of_a_captured_graph():
+@pytest.mark.parametrize("M", [200, 600])
+def test_noalloc_replays_of_a_captured_graph(M):
     """lin_bwd_ex_noalloc captured into a HIP graph (its callers include graph capture),
     replayed on new inputs copied into the captured buffers, with eager work and
     synchronisations between replays; every replay bit for bit equal to lin_bwd_ex run
-    eagerly on the same inputs.  M = 200 sums dX in 16 splits and db in row splits, both
-    through the static array, so each replay reuses what the previous one left there."""
-    M, K, N = 200, 1032, 4104
+    eagerly on the same inputs.  M = 200 sums dX in 16 splits on the small-M kernel, M = 600
+    in 8 ranges on the tile kernel (the split launch and the launch that adds the ranges),
+    and db in row splits, all through the static array, so each replay reuses what the
+    previous one left there."""
+    K, N = 1032, 4104
     cases = [synth.linear_case(M, K, N, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=90 + i)
              for i in range(3)]
     X, W, G = (t.to(DEV) for t in (cases[0].X, cases[0].W, cases[0].G))
