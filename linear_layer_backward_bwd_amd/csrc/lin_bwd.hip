@@ -1684,6 +1684,15 @@ TileJob make_tile_job(int kind, const void *a, const void *b, void *c, int64_t I
 // split tiles were no faster than the small-M kernel for dX alone, and slower
 // with K = 16384 (75.9 vs 66.6 us at M = 256).
 constexpr int64_t kTileSplitMinDxM = kSmallMaxM + 1;
+// Below that, down to this M, both products take the tile kernel (one launch,
+// dX split) when both are requested and K, N >= kTileBothMinKN: there the two
+// small-M launches lost (tile / small-M, whole call: 0.82-1.00 on 11 seeded
+// shapes with K, N >= 2048 between M = 145 and 254, e.g. M = 204, K = 12288,
+// N = 16384 424.6 -> 350.1 us), while with K or N <= 1024, at M <= 128 or for
+// one product alone the small-M kernels stayed as fast or faster (M = 128,
+// K = N = 4096: 35.3 vs 42.3 us).
+constexpr int64_t kTileBothMinM = 160;
+constexpr int64_t kTileBothMinKN = 2048;
 
 // Reduction ranges for a dX tile job: with few dX tiles (small M) one tile's
 // reduction would outlast the launch, so it is split until one range is no
@@ -1980,8 +1989,12 @@ hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_d
     // M = 0 for dW, which the tile kernel writes as zeros), else the tile
     // kernel, else the element-wise kernel.  From M = kTileSplitMinDxM on, dX
     // takes the tile kernel with its reduction split over several tiles (fp32
-    // partials in the workspace) instead of the small-M kernel.
-    const bool small_ok = a.path != PATH_TILE;
+    // partials in the workspace) instead of the small-M kernel; from
+    // kTileBothMinM with large K and N, both products do (both_tile).
+    const bool both_tile = a.path == PATH_AUTO && need_dx && need_dw && a.dx_partial != nullptr &&
+                           a.M >= kTileBothMinM && a.K >= kTileBothMinKN && a.N >= kTileBothMinKN &&
+                           e.tile_dx && e.tile_dw;
+    const bool small_ok = a.path != PATH_TILE && !both_tile;
     const bool small_dx = need_dx && a.N > 0 && small_ok && e.small_dx &&
                           !(a.path == PATH_AUTO && a.M >= kTileSplitMinDxM && a.dx_partial != nullptr);
     const bool small_dw = need_dw && small_ok && e.small_dw;

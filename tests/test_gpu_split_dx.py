@@ -1,4 +1,5 @@
-"""dX on the tile kernel with its reduction split over several tiles (257 <= M <= 1024).
+"""dX on the tile kernel with its reduction split over several tiles (257 <= M <= 1024, and
+160 <= M <= 256 with both products requested and K, N >= 2048).
 
 In that range dW runs on the 256x256 tile kernel, and dX would give only (M/256)(K/256)
 tiles, each over the whole reduction N: the launch would last as long as one such tile.
@@ -56,12 +57,13 @@ def check(case, dX, dW, bound_rows):
         assert_within_bound(hw[rows], rW[rows], oracle.dw_rows(aX, aG, "bf16", rows), case.M, False, "dW")
 
 
-# (M, K, N, need_dw): the first M that takes the split; two and four ranges; ragged K and N
-# (padded copies, then the split); N = 16384, where the rows of dY and W are 32 KiB apart and
-# the tiles start their ranges at rotated pairs (eight ranges of 32 pairs here); M = 1024
-SHAPES = [(257, 256, 8192, True), (300, 1040, 2056, True), (600, 520, 4096, True),
-          (1000, 520, 4100, True), (700, 777, 1030, True), (512, 1024, 16384, False),
-          (1024, 1024, 4096, True)]
+# (M, K, N, need_dw): both products on the tile kernel below M = 257 (large K and N); the
+# first M that takes the split for any K and N; two and four ranges; ragged K and N (padded
+# copies, then the split); N = 16384, where the rows of dY and W are 32 KiB apart and the
+# tiles start their ranges at rotated pairs (eight ranges of 32 pairs here); M = 1024
+SHAPES = [(160, 2048, 2048, True), (200, 2048, 4100, True), (257, 256, 8192, True),
+          (300, 1040, 2056, True), (600, 520, 4096, True), (1000, 520, 4100, True),
+          (700, 777, 1030, True), (512, 1024, 16384, False), (1024, 1024, 4096, True)]
 
 
 @pytest.mark.parametrize("M,K,N,need_dw", SHAPES)
@@ -77,7 +79,8 @@ def int_case(M, K, N, seed):
     return synth.LinearCase(M, K, N, "bf16", mk(M, K), mk(K, N), mk(M, N))
 
 
-@pytest.mark.parametrize("M,K,N", [(600, 264, 4096), (512, 1024, 16384), (1024, 520, 2056)])
+@pytest.mark.parametrize("M,K,N", [(192, 2048, 2056), (600, 264, 4096), (512, 1024, 16384),
+                                   (1024, 520, 2056)])
 def test_split_dx_integer_inputs_bitwise_against_the_element_wise_kernel(M, K, N):
     """Integer inputs in {-2..2}: every partial and every sum is exact in fp32, so the split
     path, the forced tile path and the element-wise kernel all give the same bits."""
