@@ -80,8 +80,9 @@ extern "C" {
  * For bf16 with 1 <= M <= 1024 (decode-like and small batches), dX sums over
  * n in several blocks whose fp32 partial sums go to the library-owned
  * workspace of the calling thread's stream and are added in a fixed order
- * (results repeat bit for bit).  The kernels are chosen by dtype, alignment
- * and M unless lb_set_lin_bwd_path() forces a path.
+ * (results repeat bit for bit).  The kernels are chosen by dtype, alignment,
+ * M, K, N and the outputs requested unless lb_set_lin_bwd_path() forces a
+ * path; every choice computes the same sums, rounded once.
  * Errors: LB_EINVAL for a negative size, a NULL operand that a requested
  * output needs (X for dW; W for dX; dY for either), or a forced kernel path
  * that cannot run the call; LB_EDTYPE for another dtype; LB_EHIP when the
