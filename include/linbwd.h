@@ -20,7 +20,7 @@
  *  - Outputs must not alias inputs or each other.
  *  - Calls enqueued on different streams that write the same memory race.
  *  - The few calls that need temporary device memory (noted below) take it
- *    from a library-owned workspace of about 36.2 MiB per (device, stream)
+ *    from a library-owned workspace of about 68.2 MiB per (device, stream)
  *    pair, allocated on the first such call on that stream and kept until the
  *    process ends or lb_shutdown(): calls on one stream run in order and share
  *    it, calls on different streams use different workspaces and may overlap.
@@ -77,10 +77,11 @@ extern "C" {
  * such call's copies, until lb_shutdown().  If the allocation fails, the call
  * takes the element-wise kernel instead (a forced path returns LB_EHIP).
  * fp32 calls take the element-wise kernel.
- * For bf16 with 1 <= M <= 1024 (decode-like and small batches), dX sums over
- * n in several blocks whose fp32 partial sums go to the library-owned
- * workspace of the calling thread's stream and are added in a fixed order
- * (results repeat bit for bit).  The kernels are chosen by dtype, alignment,
+ * For bf16 with 1 <= M <= 2048 (decode-like and small batches, and batches
+ * too small to fill the GPU with whole dX tiles), dX may sum over n in
+ * several blocks whose fp32 partial sums go to the library-owned workspace of
+ * the calling thread's stream and are added in a fixed order (results repeat
+ * bit for bit).  The kernels are chosen by dtype, alignment,
  * M, K, N and the outputs requested unless lb_set_lin_bwd_path() forces a
  * path; every choice computes the same sums, rounded once.
  * Errors: LB_EINVAL for a negative size, a NULL operand that a requested
@@ -117,7 +118,7 @@ int lin_bwd_ex(const void *X, const void *W, const void *dY, void *dX, float *dW
  * same kernels, splits and summation order, so the same bits), with the same
  * arguments, sizes and errors, but calls no allocating routine: its
  * temporaries (the small-M dX split partials and db's row partials) live in a
- * static device array of 36 MiB (8 Mi + 1 Mi floats) that the library holds on
+ * static device array of 68 MiB (16 Mi + 1 Mi floats) that the library holds on
  * every device it runs on until the process ends.  The kernels size their
  * splits to that array, so no size is refused for want of room.  Nothing in it
  * needs to start at zero: every partial is written before it is read.
@@ -269,9 +270,10 @@ int lb_set_stream(void *hip_stream);
  * the calling thread's later calls (per thread, like the stream), so that
  * the kernels can be compared with each other on the same inputs and a
  * caller can pin a choice; every path computes the same sums, rounded once.
- *   LB_PATH_AUTO     chosen by dtype, alignment and M (the default)
+ *   LB_PATH_AUTO     chosen by dtype, alignment, M, K, N and the outputs
+ *                    requested (the default)
  *   LB_PATH_TILE     both products on the 256x256 MFMA tile kernel (for
- *                    M <= 1024 with dX's reduction split over several tiles
+ *                    M <= 2048 with dX's reduction split over several tiles
  *                    when that shortens the launch)
  *   LB_PATH_SMALL_M  dX on the split-reduction kernel (M <= 1024), dW on the
  *                    small-tile kernel (M <= 256)
@@ -312,7 +314,7 @@ const char *lb_version(void);
 /*
  * lb_shutdown -- frees the library-owned workspaces of every device and
  * stream (the gradient norm's partial sums, lin_bwd_ex's bias partials and
- * lin_bwd's dX partials for bf16 with 1 <= M <= 1024, allocated on first use
+ * lin_bwd's dX partials for bf16 with 1 <= M <= 2048, allocated on first use
  * per device and stream; without this call they are kept until the process
  * ends) and destroys each device's memory pool of lin_bwd's padded copies
  * (ragged or unaligned bf16 calls).  A later call that needs a workspace or

@@ -36,7 +36,8 @@ bool beta_ok(float b) { return b >= 0.0f && b < 1.0f; } // false for NaN
 // Library-owned workspace, allocated on first use for each (device, stream)
 // pair and kept until the process ends or lb_shutdown(): grad_norm's
 // per-block partial sums and flags, lin_bwd_ex's per-split bias partials and
-// the fp32 dX partials of lin_bwd's M <= 1024 path, in separate regions.
+// the fp32 dX partials of lin_bwd's split dX (bf16, M <= 2048), in separate
+// regions.
 // Calls on one stream run in order, so they can share one workspace; calls on
 // two streams of a device get two workspaces and may overlap.
 struct Workspace {
@@ -158,8 +159,8 @@ int lin_bwd_impl(const char *name, const void *X, const void *W, const void *dY,
     if (const char *why = lb::lin_bwd_path_refusal(a))
         return fail(LB_EINVAL, "%s: the forced kernel path (%d) cannot run this call: %s", name, tl_path, why);
     float *dx_partial = nullptr, *bias_partial = nullptr;
-    const bool small_dx = dX && dtype == LB_BF16 && M > 0 && M <= 1024 && K > 0 && N > 0;
-    if ((db && N > 0) || small_dx) {
+    const bool dx_split = dX && dtype == LB_BF16 && M > 0 && M <= lb::kDxSplitMaxM && K > 0 && N > 0;
+    if ((db && N > 0) || dx_split) {
         if (no_alloc) {
             float *p = nullptr;
             hipError_t e = scratch_address(&p);
@@ -177,9 +178,9 @@ int lin_bwd_impl(const char *name, const void *X, const void *W, const void *dY,
         }
     }
     // the dX partials only where every entry point passes them (bf16,
-    // 1 <= M <= 1024), so that lin_bwd and lin_bwd_ex with or without db
-    // choose the same splits and give the same bits
-    a.dx_partial = small_dx ? dx_partial : nullptr;
+    // 1 <= M <= kDxSplitMaxM), so that lin_bwd and lin_bwd_ex with or without
+    // db choose the same splits and give the same bits
+    a.dx_partial = dx_split ? dx_partial : nullptr;
     a.dx_partial_floats = a.dx_partial ? lb::kDxPartialFloats : 0;
     hipError_t e = lb::launch_lin_bwd(a, tl_stream);
     if (e != hipSuccess)

@@ -70,7 +70,12 @@ struct LinBwdArgs {
     bool may_stage = true;
 };
 
-constexpr int64_t kDxPartialFloats = 1 << 23; // 32 MiB of dX partials
+constexpr int64_t kDxPartialFloats = 1 << 24; // 64 MiB of dX partials (split tile ranges, 1 <= M <= 2048)
+// what the small-M dX kernels' splits may use of it (their split counts were
+// measured within this capacity)
+constexpr int64_t kSmallDxPartialFloats = 1 << 23;
+// dX partials are passed to the dispatch for bf16 calls with 1 <= M <= this
+constexpr int64_t kDxSplitMaxM = 2048;
 
 
 // The current device's pool for the padded copies of ragged or unaligned

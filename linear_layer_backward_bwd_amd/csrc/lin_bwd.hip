@@ -23,8 +23,9 @@
 //                    longest reduction first and mapped so that each XCD works on a
 //                    compact group of tiles.
 //   k_lin_bwd_mfma_split  the same with dX's reduction split into ranges whose
-//                    tiles write fp32 partials (257 <= M <= 1024, where dX alone
-//                    would give few, long tiles); k_dx_smallm_reduce adds them.
+//                    tiles write fp32 partials (where few, long dX tiles would
+//                    outlast the launch: M from 257, or 160 with both products and
+//                    K, N >= 2048, up to 2048); k_dx_smallm_reduce adds them.
 //   k_dx_smallm      dX for M <= 256 (decode-like and small batches; up to 1024
 //                    on request): streams W once per 256-row group, the reduction
 //                    over n split across blocks; the fp32 partials are added in
@@ -900,7 +901,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma_split(MfmaParams p
 // streams made it 40% slower than the two launches in turn.)
 // ------------------------------------------------------------------------
 constexpr int kSmallMaxM = 256;   // dW: the small-tile kernel up to this M
-constexpr int kSmallMaxDxM = 1024; // dX: split reductions (either kernel) up to this M
+constexpr int kSmallMaxDxM = 1024; // dX: the small-M kernel up to this M (split tile ranges: kDxSplitMaxM)
 
 struct SmallParams {
     const uint16_t *X, *W, *G; // X[M,K], W[K,N], dY[M,N]
@@ -1695,10 +1696,82 @@ constexpr int64_t kTileBothMinM = 160;
 constexpr int64_t kTileBothMinKN = 2048;
 
 // Reduction ranges for a dX tile job: with few dX tiles (small M) one tile's
-// reduction would outlast the launch, so it is split until one range is no
-// longer than the launch's average per CU (or than a dW tile in the same
-// launch), in powers of two up to kDxsMaxSplits, with every range's fp32
-// partials [M, K] within the workspace.
+// reduction would outlast the launch, so it is split, in powers of two up to
+// kDxsMaxSplits, while a dX tile is longer than the launch's average per CU
+// (or than a dW tile in the same launch), each range keeps at least 8 slabs,
+// and the ranges' fp32 partials [M, K] fit the workspace.  Splitting costs the
+// partials (M*K fp32 per range, written, then read back) and, once the tiles
+// no longer run in one wave (more tiles than CUs), a tile's fixed work per
+// range: so the first split, and any split beyond one wave, needs a tile
+// longer than that target by more than a quarter (at least 8 slabs); and a
+// launch that runs in one wave is split into more than one only where that
+// shortens its scheduled length (launch_span; one wave: at most a sixteenth
+// more tiles than CUs, whose few extra tiles start as the shortest finish).
+// Measured with forced range counts (calls back to back on cold inputs):
+//   M = 1800, K = N = 4096 (tile 6% above the average): 1 range 106.6 us, 2 131.2
+//   M = 1959, K = N = 2048 (tile 3% above a dW tile): 1 44.5, 2 55.5, 4 79.0
+//   M = 200, K = N = 4096 (272 tiles unsplit, 16 dX): 4 49.1, 8 44.3, 16 51.4
+//   M = 1000, K = 520, N = 4104 (one wave): 2 57.9, 4 37.9, 8 31.3, 16 36.0
+//   M = 160, K = N = 2048 (one wave): 2 29.9, 4 23.1, 8 21.7, 16 25.9
+//   M = 2048, K = 1024, N = 16384: 1 356.1, 4 (chosen) 131.9
+//   M = 549, K = 8192, N = 1024 (one wave unsplit, two with 2): 1 31.0, 2 50.7
+//   M = 200, K = 2048, N = 4104 (264 tiles with 16): 8 31.1, 16 27.9
+// A tile's fixed work (first operand round trip, epilogue) in slabs.
+constexpr int64_t kTileFixedSlabs = 4;
+
+// Length, in slabs, of a launch of n0 tiles of l0 slabs then n1 tiles of l1:
+// each tile starts on the CU that frees first and takes its slabs plus the
+// fixed work.  CUs that free at the same time are kept as one group; a launch
+// that would need more groups than tracked counts as endless.
+int64_t launch_span(int64_t n0, int64_t l0, int64_t n1, int64_t l1) {
+    constexpr int kG = 16;
+    int64_t t[kG] = {0}, c[kG] = {kCUs};
+    int g = 1;
+    const int64_t n[2] = {n0, n1}, len[2] = {l0 + kTileFixedSlabs, l1 + kTileFixedSlabs};
+    for (int j = 0; j < 2; ++j) {
+        for (int64_t left = n[j]; left > 0;) {
+            int e = 0;
+            for (int i = 1; i < g; ++i)
+                if (t[i] < t[e])
+                    e = i;
+            const int64_t k = std::min(c[e], left), end = t[e] + len[j];
+            left -= k;
+            c[e] -= k;
+            int f = -1;
+            for (int i = 0; i < g; ++i)
+                if (t[i] == end)
+                    f = i;
+            if (f >= 0) {
+                c[f] += k;
+            } else if (c[e] == 0) {
+                t[e] = end;
+                c[e] = k;
+                continue;
+            } else if (g < kG) {
+                t[g] = end;
+                c[g++] = k;
+            } else {
+                return INT64_MAX;
+            }
+            if (c[e] == 0) {
+                t[e] = t[g - 1];
+                c[e] = c[g - 1];
+                --g;
+            }
+        }
+    }
+    int64_t span = 0;
+    for (int i = 0; i < g; ++i)
+        span = std::max(span, t[i]);
+    return span;
+}
+
+// launch_span of the dX tiles in sx ranges and the dW tiles, longest first
+int64_t split_span(int64_t ntx, int sx, int64_t xs, int64_t wtiles, int64_t ws) {
+    const int64_t lx = (xs + sx - 1) / sx;
+    return lx >= ws ? launch_span(ntx * sx, lx, wtiles, ws) : launch_span(wtiles, ws, ntx * sx, lx);
+}
+
 int tile_dx_splits(const LinBwdArgs &a, const TileJob &jx, const TileJob *jw) {
     const int64_t xs = (jx.R + kBK - 1) / kBK; // slabs per dX tile
     int64_t total = (int64_t)jx.ntiles * xs, other = 0;
@@ -1707,9 +1780,23 @@ int tile_dx_splits(const LinBwdArgs &a, const TileJob &jx, const TileJob *jw) {
         total += (int64_t)jw->ntiles * other;
     }
     const int64_t target = std::max((total + kCUs - 1) / kCUs, other);
+    const int64_t limit = target + std::max<int64_t>(8, target / 4);
+    const int64_t wtiles = jw ? jw->ntiles : 0;
+    const int64_t wave = kCUs + kCUs / 16;
     int sx = 1;
-    while (sx < kDxsMaxSplits && (xs + sx - 1) / sx > target && 2 * sx * a.M * a.K <= a.dx_partial_floats)
+    while (sx < kDxsMaxSplits) {
+        const int64_t cur = (xs + sx - 1) / sx;            // a dX tile's slabs now
+        const int64_t next = (xs + 2 * sx - 1) / (2 * sx); // ... with twice the ranges
+        if (cur <= target || next < 8 || 2 * sx * a.M * a.K > a.dx_partial_floats)
+            break;
+        const bool one_wave = (int64_t)jx.ntiles * 2 * sx + wtiles <= wave;
+        if ((sx == 1 || !one_wave) && cur <= limit)
+            break;
+        if (!one_wave && (int64_t)jx.ntiles * sx + wtiles <= wave &&
+            split_span(jx.ntiles, 2 * sx, xs, wtiles, other) >= split_span(jx.ntiles, sx, xs, wtiles, other))
+            break;
         sx *= 2;
+    }
     return sx;
 }
 
@@ -1764,7 +1851,7 @@ hipError_t launch_fused_small(const LinBwdArgs &a, hipStream_t s) {
     const int64_t chunks = (a.N + kRsCH - 1) / kRsCH;
     int64_t splits = std::min(chunks, std::max<int64_t>(1, (256 + rblocks - 1) / rblocks));
     splits = std::min<int64_t>(splits, kDxsMaxSplits);
-    splits = a.dx_partial ? std::min(splits, a.dx_partial_floats / (a.M * a.K)) : 1;
+    splits = a.dx_partial ? std::min(splits, std::min(a.dx_partial_floats, kSmallDxPartialFloats) / (a.M * a.K)) : 1;
     splits = std::max<int64_t>(splits, 1);
     const int64_t split_len = (chunks + splits - 1) / splits * kRsCH;
     splits = (a.N + split_len - 1) / split_len;
@@ -2042,7 +2129,7 @@ hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_d
     }
     // longest reduction first: those tiles start on the first wave of CUs
     if (have_x && have_w) {
-        if (jw.R > jx.R) {
+        if (jw.R > (jx.splits > 1 ? jx.split_len : jx.R)) {
             p.job[nj++] = jw;
             p.job[nj++] = jx;
         } else {
@@ -2097,7 +2184,7 @@ hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_d
             if (a.dx_partial == nullptr)
                 splits = 1;
             else
-                splits = std::min(splits, a.dx_partial_floats / (a.M * a.K));
+                splits = std::min(splits, std::min(a.dx_partial_floats, kSmallDxPartialFloats) / (a.M * a.K));
             splits = std::max<int64_t>(splits, 1);
             const int64_t split_len = (chunks + splits - 1) / splits * chunk;
             splits = (a.N + split_len - 1) / split_len;

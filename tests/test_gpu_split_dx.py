@@ -1,5 +1,6 @@
-"""dX on the tile kernel with its reduction split over several tiles (257 <= M <= 1024, and
-160 <= M <= 256 with both products requested and K, N >= 2048).
+"""dX on the tile kernel with its reduction split over several tiles (where few, long dX
+tiles would outlast the launch: from M = 257 up to 2048, and from M = 160 with both products
+requested and K, N >= 2048).
 
 In that range dW runs on the 256x256 tile kernel, and dX would give only (M/256)(K/256)
 tiles, each over the whole reduction N: the launch would last as long as one such tile.
@@ -60,10 +61,13 @@ def check(case, dX, dW, bound_rows):
 # (M, K, N, need_dw): both products on the tile kernel below M = 257 (large K and N); the
 # first M that takes the split for any K and N; two and four ranges; ragged K and N (padded
 # copies, then the split); N = 16384, where the rows of dY and W are 32 KiB apart and the
-# tiles start their ranges at rotated pairs (eight ranges of 32 pairs here); M = 1024
+# tiles start their ranges at rotated pairs (eight ranges of 32 pairs here); M = 1024; above
+# 1024 with small K, and (1280, 2048, 8192), whose four ranges of partials (40 MiB) need more
+# than half the workspace
 SHAPES = [(160, 2048, 2048, True), (200, 2048, 4100, True), (257, 256, 8192, True),
           (300, 1040, 2056, True), (600, 520, 4096, True), (1000, 520, 4100, True),
-          (700, 777, 1030, True), (512, 1024, 16384, False), (1024, 1024, 4096, True)]
+          (700, 777, 1030, True), (512, 1024, 16384, False), (1024, 1024, 4096, True),
+          (1100, 264, 8192, True), (1500, 260, 4100, True), (1280, 2048, 8192, True)]
 
 
 @pytest.mark.parametrize("M,K,N,need_dw", SHAPES)
@@ -80,7 +84,7 @@ def int_case(M, K, N, seed):
 
 
 @pytest.mark.parametrize("M,K,N", [(192, 2048, 2056), (600, 264, 4096), (512, 1024, 16384),
-                                   (1024, 520, 2056)])
+                                   (1024, 520, 2056), (1300, 520, 4096)])
 def test_split_dx_integer_inputs_bitwise_against_the_element_wise_kernel(M, K, N):
     """Integer inputs in {-2..2}: every partial and every sum is exact in fp32, so the split
     path, the forced tile path and the element-wise kernel all give the same bits."""
