@@ -2123,6 +2123,8 @@ hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_d
         if (sx > 1) {
             jx.split_len = ((a.N + sx - 1) / sx + 63) / 64 * 64;
             jx.splits = (int)((a.N + jx.split_len - 1) / jx.split_len);
+            if ((int64_t)jx.splits * a.M * a.K > a.dx_partial_floats) // the ranges' partials must fit
+                return hipErrorInvalidValue;
             jx.part = a.dx_partial;
             jx.ntiles *= jx.splits;
         }
