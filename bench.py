@@ -206,6 +206,7 @@ def calibrate(reps=10):
 KERNEL_SOURCES = {"k_lin_bwd_mfma": "linear_layer_backward_bwd_amd/csrc/lin_bwd.hip",
                   "k_lin_bwd_mfma_split": "linear_layer_backward_bwd_amd/csrc/lin_bwd.hip",
                   "k_dw_smallm": "linear_layer_backward_bwd_amd/csrc/lin_bwd.hip",
+                  "k_smallm_pair": "linear_layer_backward_bwd_amd/csrc/lin_bwd.hip",
                   "k_adamw": "linear_layer_backward_bwd_amd/csrc/adamw.hip",
                   "k_norm_partial": "linear_layer_backward_bwd_amd/csrc/grad_norm.hip",
                   "k_bias_partial": "linear_layer_backward_bwd_amd/csrc/bias_grad.hip",
@@ -496,8 +497,9 @@ def bench_linear(M, K, N, steps, warmup, seed, rotate_bytes=768 << 20):
         floor["what"] = ("the calibration read kernel over the bytes the call reads (bf16 X, W, dY) "
                          "plus the write kernel over the bytes it writes (bf16 dX, fp32 dW), cold, "
                          "an event pair around each launch, medians")
-    kernel = ("k_dw_smallm" if M <= 64 else "k_lin_bwd_mfma_split" if 256 < M <= 1024 and N > 0
-              else "k_lin_bwd_mfma")
+    pair = M <= 64 and N <= 8192 and K * N <= (1 << 25 if N <= 4096 else 5 << 22)
+    kernel = ("k_smallm_pair" if pair else "k_dw_smallm" if M <= 64
+              else "k_lin_bwd_mfma_split" if 256 < M <= 1024 and N > 0 else "k_lin_bwd_mfma")
     return {"M": M, "K": K, "N": N, "ms": round(ms, 5), "tflops": round(tf, 1),
             "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "bound": "hbm" if roofs["pages"] < PEAK_BF16_TFLOPS else "mfma",

@@ -276,7 +276,9 @@ int lb_set_stream(void *hip_stream);
  *                    M <= 2048 with dX's reduction split over several tiles
  *                    when that shortens the launch)
  *   LB_PATH_SMALL_M  dX on the split-reduction kernel (M <= 1024), dW on the
- *                    small-tile kernel (M <= 256)
+ *                    small-tile kernel (M <= 256); at M <= 64 with both
+ *                    products and moderate K*N, the blocks of both in one
+ *                    launch
  *   LB_PATH_GENERAL  both products on the element-wise kernel
  *   LB_PATH_FUSED_SMALL_M  both products in one launch in which each block
  *                    streams 16 rows of W and writes the same 16 rows of dW

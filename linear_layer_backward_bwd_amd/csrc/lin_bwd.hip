@@ -33,6 +33,9 @@
 //                    else by k_dx_smallm_reduce.
 //   k_dw_smallm      dW for M <= 256: bound by writing the fp32 output at small M;
 //                    small tiles, several per CU, so stores overlap other tiles' loads.
+//   k_smallm_pair    the blocks of both in one launch, two per CU (M <= 64, N and
+//                    K*N not too large), so W's read stream and dW's write stream
+//                    overlap; the dX partials are then added by k_dx_smallm_reduce.
 //   k_lin_bwd_fused_small  both products for M <= 64 in one launch (on request).
 //   k_repack         zero-padded copies for bf16 calls whose K or N is not a
 //                    multiple of 8 or whose pointers are not 16-byte aligned.
@@ -893,14 +896,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma_split(MfmaParams p
 // small M: at M <= 64 both products are bound by HBM, not MFMA: dX streams W
 // (2KN bytes), dW writes the fp32 output (4KN bytes).  Up to M = 256 dX takes
 // the split-reduction kernel below and dW the small-tile kernel, as two
-// launches; from M = 257 to 1024, where dW returns to the tile kernel, dX joins
-// it there with its reduction split over several tiles (the tile kernel with
-// whole reductions would give dX only (M/256)(K/256) long tiles).  (One launch holding the blocks of both was slower where it
-// mattered: the dX blocks took every CU first, the dW blocks then ran at the
-// merged kernel's lower occupancy, and at N = 16384 the mixed read and write
-// streams made it 40% slower than the two launches in turn.)
+// launches, or at M <= 64 (up to an N and a K*N) as one launch holding the blocks
+// of both (k_smallm_pair); from M = 257, where dW returns to the tile kernel,
+// dX joins it there with its reduction split over several tiles (the tile
+// kernel with whole reductions would give dX only (M/256)(K/256) long tiles).
+// (With dX's 144 KiB ring the one launch lost: the dX blocks took every CU
+// first and the dW blocks ran at the merged kernel's occupancy of one block
+// per CU.  With 72 KiB it wins up to N = 8192 and a dW of 128 MiB; at N = 16384
+// or K = N = 8192 the mixed read and write streams still made it slower than
+// the two launches in turn.)
 // ------------------------------------------------------------------------
 constexpr int kSmallMaxM = 256;   // dW: the small-tile kernel up to this M
+// k_smallm_pair: both products with M up to kPairMaxM, N up to kPairMaxN and
+// K*N up to kPairMaxKN (dW of 128 MiB), or kPairMaxKNWide above N = 4096
+// (measured against the two launches: M = 1 / 32, K = 4096, N = 8192 1.044 /
+// 1.013 of their time, M = 28, K = 2056, N = 8192 0.79, M = 64, K = 8192,
+// N = 4096 0.91; K = N = 8192 1.00 and N = 16384 1.00-1.12)
+constexpr int64_t kPairMaxM = 64;
+constexpr int64_t kPairMaxN = 8192;
+constexpr int64_t kPairMaxKN = 1LL << 25;
+constexpr int64_t kPairMaxKNWide = 5LL << 22;
 constexpr int kSmallMaxDxM = 1024; // dX: the small-M kernel up to this M (split tile ranges: kDxSplitMaxM)
 
 struct SmallParams {
@@ -915,6 +930,7 @@ struct SmallParams {
                                // split b % splits, row group (b / splits) % mgroups, group b / splits / mgroups
     int dw_tiles_n;            // dW block b = (n tile, k tile) (b % dw_tiles_n, b / dw_tiles_n)
     int reduce_blocks;         // dW blocks that also add up dX partials
+    int dx_blocks;             // k_smallm_pair: blocks below this run dX, the rest dW
 };
 
 // dW[k,n] = Σ_m X[m,k]·dY[m,n] for M <= 256: a rank-M product whose cost is
@@ -1050,12 +1066,12 @@ __device__ __forceinline__ void dw_small_block(const SmallParams &p, int b, LDS 
 constexpr int kDxsBK = 64; // dX columns per block
 template <int MB> // reduction elements per chunk: dY's slot stays within LDS
 constexpr int dx_small_chunk() { return MB <= 4 ? 256 : 128; }
-template <int MB>
-constexpr int dx_small_slot() { return (64 + MB * 16) * dx_small_chunk<MB>() * 2; }
-template <int MB> // ring slots: three where they fit in LDS
-constexpr int dx_small_slots() { return 3 * dx_small_slot<MB>() <= 160 * 1024 ? 3 : 2; }
-template <int MB>
-constexpr int dx_small_lds() { return dx_small_slots<MB>() * dx_small_slot<MB>(); }
+template <int MB, int CH = dx_small_chunk<MB>()>
+constexpr int dx_small_slot() { return (64 + MB * 16) * CH * 2; }
+template <int MB, int CH = dx_small_chunk<MB>()> // ring slots: three where they fit in LDS
+constexpr int dx_small_slots() { return 3 * dx_small_slot<MB, CH>() <= 160 * 1024 ? 3 : 2; }
+template <int MB, int CH = dx_small_chunk<MB>(), int S = dx_small_slots<MB, CH>()>
+constexpr int dx_small_lds() { return S * dx_small_slot<MB, CH>(); }
 
 // Wait until at most `c` chunks' DMA (kPerChunk instructions each) are in flight.
 template <int kPerChunk>
@@ -1068,15 +1084,13 @@ __device__ __forceinline__ void dx_chunk_wait(int c) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int MB>
+template <int MB, int kCH = dx_small_chunk<MB>(), int kS = dx_small_slots<MB, kCH>()>
 __device__ __forceinline__ void dx_small_block(const SmallParams &p, int b, LDS char *smem) {
-    constexpr int kCH = dx_small_chunk<MB>();
     constexpr int kRow = 2 * kCH;                // bytes per LDS row
     constexpr int kCPR = kRow / 16;              // 16-byte chunks per row
     constexpr int kRPI = 1024 / kRow;            // rows per DMA instruction
     constexpr int kWSlot = 64 * kRow;            // W part of a slot
-    constexpr int kSlot = dx_small_slot<MB>();
-    constexpr int kS = dx_small_slots<MB>();
+    constexpr int kSlot = dx_small_slot<MB, kCH>();
     constexpr int kWInst = 16 / kRPI;            // W DMA instructions per wave per chunk
     constexpr int kGInst = MB * 16 / kRPI / 4;   // dY DMA instructions per wave per chunk
     constexpr int kPerChunk = kWInst + kGInst;
@@ -1210,6 +1224,26 @@ template <int MB>
 __global__ __launch_bounds__(256) void k_dx_smallm(SmallParams p) {
     __shared__ __attribute__((aligned(1024))) char smem_raw[dx_small_lds<MB>()];
     dx_small_block<MB>(p, blockIdx.x, (LDS char *)smem_raw);
+}
+
+// Both small-M products in one launch (M <= kPairMaxM, N <= kPairMaxN, K*N
+// within kPairMaxKN or kPairMaxKNWide): blocks below dx_blocks run dX blocks
+// with a ring of 128-element chunks, the rest dW blocks.  At 128 elements a
+// dX block needs at most 72 KiB of LDS (96 would leave no room beside it;
+// MB = 4 keeps two slots, 64 KiB), so every CU holds two blocks of either
+// kind: the dX blocks' read stream of W and the dW blocks' write stream of
+// fp32 dW overlap, and the launch boundary between them goes.  Each block computes what it computes in k_dx_smallm /
+// k_dw_smallm, in the same order, so results are the same bits; dX's split
+// partials are added afterwards by k_dx_smallm_reduce.
+template <int MB, int CH, int S>
+__global__ __launch_bounds__(256) void k_smallm_pair(SmallParams p) {
+    constexpr int kDx = dx_small_lds<MB, CH, S>();
+    static_assert(kDx <= 80 * 1024 && kDwsLds <= 80 * 1024, "two blocks fit a CU's LDS");
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kDx > kDwsLds ? kDx : kDwsLds];
+    if ((int)blockIdx.x < p.dx_blocks)
+        dx_small_block<MB, CH, S>(p, blockIdx.x, (LDS char *)smem_raw);
+    else
+        dw_small_block(p, blockIdx.x - p.dx_blocks, (LDS char *)smem_raw);
 }
 
 // dW blocks; with reduce_blocks > 0 the first reduce_blocks blocks also finish
@@ -2196,6 +2230,27 @@ hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_d
             const int64_t blocks = groups * sp.mgroups * splits;
             if (blocks > 0x7fffffff)
                 return hipErrorInvalidConfiguration;
+            if (small_dw && a.M <= kPairMaxM && a.N <= kPairMaxN &&
+                a.K * a.N <= (a.N <= 4096 ? kPairMaxKN : kPairMaxKNWide)) {
+                // both products in one launch (mb <= 4); the dX split partials,
+                // if any, are added by a launch of their own
+                sp.dx_blocks = (int)blocks;
+                sp.dw_tiles_n = ceil_div(a.N, kDwsBN);
+                const int64_t total = blocks + (int64_t)sp.dw_tiles_n * ceil_div(a.K, kDwsBK);
+                if (total > 0x7fffffff)
+                    return hipErrorInvalidConfiguration;
+                const dim3 g2((unsigned)total);
+                switch (mb) {
+                case 1: hipLaunchKernelGGL((k_smallm_pair<1, 128, 3>), g2, dim3(256), 0, s, sp); break;
+                case 2: hipLaunchKernelGGL((k_smallm_pair<2, 128, 3>), g2, dim3(256), 0, s, sp); break;
+                default: hipLaunchKernelGGL((k_smallm_pair<4, 128, 2>), g2, dim3(256), 0, s, sp); break;
+                }
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess || splits == 1)
+                    return e;
+                hipLaunchKernelGGL(k_dx_smallm_reduce, dim3((unsigned)((a.M * a.K / 4 + 255) / 256)), dim3(256), 0, s, sp);
+                return hipGetLastError();
+            }
             const dim3 grid((unsigned)blocks);
             switch (mb) {
             case 1: hipLaunchKernelGGL(k_dx_smallm<1>, grid, dim3(256), 0, s, sp); break;
