@@ -44,7 +44,30 @@ def draws(seed, count):
     return out
 
 
-@pytest.mark.parametrize("M,K,N,path,off_in,off_out,need_dx,need_dw,seed", draws(2024, 80))
+def draws_near_limits(seed, count):
+    """Calls where the dispatch weighs sizes: M <= 64 (both products in one launch up to an N
+    and a K*N, two launches beyond) and 1025 <= M <= 2048 (dX split over tiles where a whole
+    dX tile would outlast the launch), K and N up to 16400, aligned or ragged, automatic path."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        M = int(rng.integers(1, 65)) if len(out) % 2 == 0 else int(rng.integers(1025, 2049))
+        while True:
+            K = int(rng.choice([8, 264, 520, 1032, 2056, 4096, 4100, 8192, 16384])) if rng.random() < 0.6 \
+                else int(rng.integers(1, 16400))
+            N = int(rng.choice([264, 1024, 2056, 4096, 4104, 8192, 8200, 16384])) if rng.random() < 0.6 \
+                else int(rng.integers(1, 16400))
+            if M * K * N <= (1 << 31):
+                break
+        need_dx = bool(rng.random() < 0.85)
+        need_dw = bool(rng.random() < 0.85) or not need_dx
+        out.append((M, K, N, lb.LB_PATH_AUTO, int(rng.choice([0, 0, 0, 1])), 0, need_dx, need_dw,
+                    int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,path,off_in,off_out,need_dx,need_dw,seed",
+                         draws(2024, 80) + draws_near_limits(2025, 40))
 def test_random_call_meets_the_bars(M, K, N, path, off_in, off_out, need_dx, need_dw, seed):
     case = synth.linear_case(M, K, N, "bf16", x_std=1.0, w_std=1.0, g_std=1.0, seed=seed)
 
