@@ -41,6 +41,7 @@
 //                    multiple of 8 or whose pointers are not 16-byte aligned.
 //   k_lin_bwd_simt   any dtype / alignment / shape: the fp32 path.
 #include "device.h"
+#include "dispatch.h"
 #include "kernels.h"
 
 #include <algorithm>
@@ -896,10 +897,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma_split(MfmaParams p
 // small M: at M <= 64 both products are bound by HBM, not MFMA: dX streams W
 // (2KN bytes), dW writes the fp32 output (4KN bytes).  Up to M = 256 dX takes
 // the split-reduction kernel below and dW the small-tile kernel, as two
-// launches, or at M <= 64 (up to an N and a K*N) as one launch holding the blocks
-// of both (k_smallm_pair); from M = 257, where dW returns to the tile kernel,
-// dX joins it there with its reduction split over several tiles (the tile
-// kernel with whole reductions would give dX only (M/256)(K/256) long tiles).
+// launches, or at M <= 64 (up to an N and a K*N: plan::pair_fits) as one
+// launch holding the blocks of both (k_smallm_pair); from M = 257, where dW
+// returns to the tile kernel, dX joins it there with its reduction split over
+// several tiles (the tile kernel with whole reductions would give dX only
+// (M/256)(K/256) long tiles).
 // (With dX's 144 KiB ring the one launch lost: the dX blocks took every CU
 // first and the dW blocks ran at the merged kernel's occupancy of one block
 // per CU.  With 72 KiB it wins up to N = 8192 and a dW of 128 MiB; at N = 16384
@@ -907,15 +909,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_lin_bwd_mfma_split(MfmaParams p
 // the two launches in turn.)
 // ------------------------------------------------------------------------
 constexpr int kSmallMaxM = 256;   // dW: the small-tile kernel up to this M
-// k_smallm_pair: both products with M up to kPairMaxM, N up to kPairMaxN and
-// K*N up to kPairMaxKN (dW of 128 MiB), or kPairMaxKNWide above N = 4096
-// (measured against the two launches: M = 1 / 32, K = 4096, N = 8192 1.044 /
-// 1.013 of their time, M = 28, K = 2056, N = 8192 0.79, M = 64, K = 8192,
-// N = 4096 0.91; K = N = 8192 1.00 and N = 16384 1.00-1.12)
-constexpr int64_t kPairMaxM = 64;
-constexpr int64_t kPairMaxN = 8192;
-constexpr int64_t kPairMaxKN = 1LL << 25;
-constexpr int64_t kPairMaxKNWide = 5LL << 22;
 constexpr int kSmallMaxDxM = 1024; // dX: the small-M kernel up to this M (split tile ranges: kDxSplitMaxM)
 
 struct SmallParams {
@@ -1226,8 +1219,8 @@ __global__ __launch_bounds__(256) void k_dx_smallm(SmallParams p) {
     dx_small_block<MB>(p, blockIdx.x, (LDS char *)smem_raw);
 }
 
-// Both small-M products in one launch (M <= kPairMaxM, N <= kPairMaxN, K*N
-// within kPairMaxKN or kPairMaxKNWide): blocks below dx_blocks run dX blocks
+// Both small-M products in one launch (where plan::pair_fits: M <= 64 and
+// limits on N and K*N): blocks below dx_blocks run dX blocks
 // with a ring of 128-element chunks, the rest dW blocks.  At 128 elements a
 // dX block needs at most 72 KiB of LDS (96 would leave no room beside it;
 // MB = 4 keeps two slots, 64 KiB), so every CU holds two blocks of either
@@ -1729,110 +1722,10 @@ constexpr int64_t kTileSplitMinDxM = kSmallMaxM + 1;
 constexpr int64_t kTileBothMinM = 160;
 constexpr int64_t kTileBothMinKN = 2048;
 
-// Reduction ranges for a dX tile job: with few dX tiles (small M) one tile's
-// reduction would outlast the launch, so it is split, in powers of two up to
-// kDxsMaxSplits, while a dX tile is longer than the launch's average per CU
-// (or than a dW tile in the same launch), each range keeps at least 8 slabs,
-// and the ranges' fp32 partials [M, K] fit the workspace.  Splitting costs the
-// partials (M*K fp32 per range, written, then read back) and, once the tiles
-// no longer run in one wave (more tiles than CUs), a tile's fixed work per
-// range: so the first split, and any split beyond one wave, needs a tile
-// longer than that target by more than a quarter (at least 8 slabs); and a
-// launch that runs in one wave is split into more than one only where that
-// shortens its scheduled length (launch_span; one wave: at most a sixteenth
-// more tiles than CUs, whose few extra tiles start as the shortest finish).
-// Measured with forced range counts (calls back to back on cold inputs):
-//   M = 1800, K = N = 4096 (tile 6% above the average): 1 range 106.6 us, 2 131.2
-//   M = 1959, K = N = 2048 (tile 3% above a dW tile): 1 44.5, 2 55.5, 4 79.0
-//   M = 200, K = N = 4096 (272 tiles unsplit, 16 dX): 4 49.1, 8 44.3, 16 51.4
-//   M = 1000, K = 520, N = 4104 (one wave): 2 57.9, 4 37.9, 8 31.3, 16 36.0
-//   M = 160, K = N = 2048 (one wave): 2 29.9, 4 23.1, 8 21.7, 16 25.9
-//   M = 2048, K = 1024, N = 16384: 1 356.1, 4 (chosen) 131.9
-//   M = 549, K = 8192, N = 1024 (one wave unsplit, two with 2): 1 31.0, 2 50.7
-//   M = 200, K = 2048, N = 4104 (264 tiles with 16): 8 31.1, 16 27.9
-// A tile's fixed work (first operand round trip, epilogue) in slabs.
-constexpr int64_t kTileFixedSlabs = 4;
-
-// Length, in slabs, of a launch of n0 tiles of l0 slabs then n1 tiles of l1:
-// each tile starts on the CU that frees first and takes its slabs plus the
-// fixed work.  CUs that free at the same time are kept as one group; a launch
-// that would need more groups than tracked counts as endless.
-int64_t launch_span(int64_t n0, int64_t l0, int64_t n1, int64_t l1) {
-    constexpr int kG = 16;
-    int64_t t[kG] = {0}, c[kG] = {kCUs};
-    int g = 1;
-    const int64_t n[2] = {n0, n1}, len[2] = {l0 + kTileFixedSlabs, l1 + kTileFixedSlabs};
-    for (int j = 0; j < 2; ++j) {
-        for (int64_t left = n[j]; left > 0;) {
-            int e = 0;
-            for (int i = 1; i < g; ++i)
-                if (t[i] < t[e])
-                    e = i;
-            const int64_t k = std::min(c[e], left), end = t[e] + len[j];
-            left -= k;
-            c[e] -= k;
-            int f = -1;
-            for (int i = 0; i < g; ++i)
-                if (t[i] == end)
-                    f = i;
-            if (f >= 0) {
-                c[f] += k;
-            } else if (c[e] == 0) {
-                t[e] = end;
-                c[e] = k;
-                continue;
-            } else if (g < kG) {
-                t[g] = end;
-                c[g++] = k;
-            } else {
-                return INT64_MAX;
-            }
-            if (c[e] == 0) {
-                t[e] = t[g - 1];
-                c[e] = c[g - 1];
-                --g;
-            }
-        }
-    }
-    int64_t span = 0;
-    for (int i = 0; i < g; ++i)
-        span = std::max(span, t[i]);
-    return span;
-}
-
-// launch_span of the dX tiles in sx ranges and the dW tiles, longest first
-int64_t split_span(int64_t ntx, int sx, int64_t xs, int64_t wtiles, int64_t ws) {
-    const int64_t lx = (xs + sx - 1) / sx;
-    return lx >= ws ? launch_span(ntx * sx, lx, wtiles, ws) : launch_span(wtiles, ws, ntx * sx, lx);
-}
-
-int tile_dx_splits(const LinBwdArgs &a, const TileJob &jx, const TileJob *jw) {
-    const int64_t xs = (jx.R + kBK - 1) / kBK; // slabs per dX tile
-    int64_t total = (int64_t)jx.ntiles * xs, other = 0;
-    if (jw) {
-        other = (jw->R + kBK - 1) / kBK;
-        total += (int64_t)jw->ntiles * other;
-    }
-    const int64_t target = std::max((total + kCUs - 1) / kCUs, other);
-    const int64_t limit = target + std::max<int64_t>(8, target / 4);
-    const int64_t wtiles = jw ? jw->ntiles : 0;
-    const int64_t wave = kCUs + kCUs / 16;
-    int sx = 1;
-    while (sx < kDxsMaxSplits) {
-        const int64_t cur = (xs + sx - 1) / sx;            // a dX tile's slabs now
-        const int64_t next = (xs + 2 * sx - 1) / (2 * sx); // ... with twice the ranges
-        if (cur <= target || next < 8 || 2 * sx * a.M * a.K > a.dx_partial_floats)
-            break;
-        const bool one_wave = (int64_t)jx.ntiles * 2 * sx + wtiles <= wave;
-        if ((sx == 1 || !one_wave) && cur <= limit)
-            break;
-        if (!one_wave && (int64_t)jx.ntiles * sx + wtiles <= wave &&
-            split_span(jx.ntiles, 2 * sx, xs, wtiles, other) >= split_span(jx.ntiles, sx, xs, wtiles, other))
-            break;
-        sx *= 2;
-    }
-    return sx;
-}
+// The host-side sizing decisions (range counts, the launch-length model, the
+// pair limits) live in dispatch.h; its constants must be the kernels'.
+static_assert(plan::kCUs == kCUs && plan::kSlab == kBK && plan::kMaxSplits == kDxsMaxSplits,
+              "dispatch.h sizes the kernels in this file");
 
 // Which MFMA kernel can run which product.  Every kernel reads 16-byte chunks
 // of bf16 rows (K and N multiples of 8, 16-byte aligned pointers) through
@@ -1882,13 +1775,9 @@ hipError_t launch_fused_small(const LinBwdArgs &a, hipStream_t s) {
     // splits of the reduction: toward 256 blocks (one per CU), each a whole
     // number of chunks, at most kDxsMaxSplits, partials within the workspace
     const int64_t rblocks = (a.K + kRsRows - 1) / kRsRows;
-    const int64_t chunks = (a.N + kRsCH - 1) / kRsCH;
-    int64_t splits = std::min(chunks, std::max<int64_t>(1, (256 + rblocks - 1) / rblocks));
-    splits = std::min<int64_t>(splits, kDxsMaxSplits);
-    splits = a.dx_partial ? std::min(splits, std::min(a.dx_partial_floats, kSmallDxPartialFloats) / (a.M * a.K)) : 1;
-    splits = std::max<int64_t>(splits, 1);
-    const int64_t split_len = (chunks + splits - 1) / splits * kRsCH;
-    splits = (a.N + split_len - 1) / split_len;
+    const plan::Split sl = plan::reduction_split(
+        a.N, kRsCH, rblocks, a.M, a.K, a.dx_partial ? std::min(a.dx_partial_floats, kSmallDxPartialFloats) : 0);
+    const int64_t splits = sl.splits, split_len = sl.len;
     fp.split_len = split_len;
     fp.splits = (int)splits;
     fp.part = a.dx_partial;
@@ -2153,10 +2042,12 @@ hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_d
         have_w = true;
     }
     if (have_x && a.dx_partial != nullptr && a.N > 0) {
-        const int sx = tile_dx_splits(a, jx, have_w ? &jw : nullptr);
+        const int sx = plan::tile_dx_splits(a.M, a.K, jx.ntiles, jx.R, have_w ? jw.ntiles : 0, have_w ? jw.R : 0,
+                                            a.dx_partial_floats);
         if (sx > 1) {
-            jx.split_len = ((a.N + sx - 1) / sx + 63) / 64 * 64;
-            jx.splits = (int)((a.N + jx.split_len - 1) / jx.split_len);
+            const plan::Split sl = plan::tile_split_len(a.N, sx);
+            jx.split_len = sl.len;
+            jx.splits = (int)sl.splits;
             if ((int64_t)jx.splits * a.M * a.K > a.dx_partial_floats) // the ranges' partials must fit
                 return hipErrorInvalidValue;
             jx.part = a.dx_partial;
@@ -2214,24 +2105,17 @@ hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_d
             sp.mgroups = (int)((a.M + 16 * mb - 1) / (16 * mb)); // above 256 rows: groups of 256
             const int64_t chunk = mb <= 4 ? dx_small_chunk<4>() : dx_small_chunk<8>();
             const int64_t groups = (a.K + kDxsBK - 1) / kDxsBK;
-            const int64_t chunks = (a.N + chunk - 1) / chunk;
-            int64_t splits = std::min(chunks, std::max<int64_t>(1, (256 + groups * sp.mgroups - 1) / (groups * sp.mgroups)));
-            splits = std::min<int64_t>(splits, kDxsMaxSplits);
-            if (a.dx_partial == nullptr)
-                splits = 1;
-            else
-                splits = std::min(splits, std::min(a.dx_partial_floats, kSmallDxPartialFloats) / (a.M * a.K));
-            splits = std::max<int64_t>(splits, 1);
-            const int64_t split_len = (chunks + splits - 1) / splits * chunk;
-            splits = (a.N + split_len - 1) / split_len;
+            const plan::Split sl =
+                plan::reduction_split(a.N, chunk, groups * sp.mgroups, a.M, a.K,
+                                      a.dx_partial ? std::min(a.dx_partial_floats, kSmallDxPartialFloats) : 0);
+            const int64_t splits = sl.splits, split_len = sl.len;
             sp.split_len = split_len;
             sp.splits = (int)splits;
             sp.part = a.dx_partial;
             const int64_t blocks = groups * sp.mgroups * splits;
             if (blocks > 0x7fffffff)
                 return hipErrorInvalidConfiguration;
-            if (small_dw && a.M <= kPairMaxM && a.N <= kPairMaxN &&
-                a.K * a.N <= (a.N <= 4096 ? kPairMaxKN : kPairMaxKNWide)) {
+            if (small_dw && plan::pair_fits(a.M, a.K, a.N)) {
                 // both products in one launch (mb <= 4); the dX split partials,
                 // if any, are added by a launch of their own
                 sp.dx_blocks = (int)blocks;
