@@ -278,7 +278,8 @@ int lb_set_stream(void *hip_stream);
  *   LB_PATH_SMALL_M  dX on the split-reduction kernel (M <= 1024), dW on the
  *                    small-tile kernel (M <= 256); at M <= 64 with both
  *                    products and moderate K*N, the blocks of both in one
- *                    launch
+ *                    launch; at M <= 16 on small calls, dX blocks that each
+ *                    sum a whole reduction (no partials)
  *   LB_PATH_GENERAL  both products on the element-wise kernel
  *   LB_PATH_FUSED_SMALL_M  both products in one launch in which each block
  *                    streams 16 rows of W and writes the same 16 rows of dW

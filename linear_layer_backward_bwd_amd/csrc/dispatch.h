@@ -156,5 +156,26 @@ inline bool pair_fits(int64_t M, int64_t K, int64_t N) {
     return M >= 1 && M <= kPairMaxM && N >= 1 && N <= kPairMaxN && K * N <= (N <= 4096 ? kPairMaxKN : kPairMaxKNWide);
 }
 
+// dX for M <= 16 without split partials (dx_rows16_block; with dW in one
+// launch) on small calls: K from kRows16MinK (at least 32 blocks of 16 rows),
+// N from kRows16MinN to kRows16MaxN and at most 4K (enough blocks for the
+// reduction's length), K*N up to kRows16MaxKN.  Measured per call against the
+// split kernel and its summing launch, on 90 seeded shapes with M <= 16:
+// within these limits 0.70-1.00 of its time (M = 1, K = N = 1024: 8.8 ->
+// 6.5 us; M = 6, K = 1912, N = 1080, dX alone: 8.8 -> 6.2); outside them
+// 1.04-1.67 (K <= 632 with N >= 3152, K <= 370 with N >= 4600: too few blocks
+// for long reductions; N = 176: a quarter of n is less than one chunk) or
+// mixed for larger K*N (0.90 at M = 8, K = N = 4096; 1.22 at M = 16,
+// K = 1024, N = 4096).
+constexpr int64_t kRows16MaxM = 16;
+constexpr int64_t kRows16MinK = 512;
+constexpr int64_t kRows16MinN = 256;
+constexpr int64_t kRows16MaxN = 4096;
+constexpr int64_t kRows16MaxKN = 1LL << 21;
+inline bool rows16_fits(int64_t M, int64_t K, int64_t N) {
+    return M >= 1 && M <= kRows16MaxM && K >= kRows16MinK && N >= kRows16MinN && N <= kRows16MaxN &&
+           N <= 4 * K && K * N <= kRows16MaxKN;
+}
+
 } // namespace plan
 } // namespace lb

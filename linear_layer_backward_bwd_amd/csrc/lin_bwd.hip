@@ -36,6 +36,9 @@
 //   k_smallm_pair    the blocks of both in one launch, two per CU (M <= 64, N and
 //                    K*N not too large), so W's read stream and dW's write stream
 //                    overlap; the dX partials are then added by k_dx_smallm_reduce.
+//   k_dx_rows16, k_smallm_pair16  the same for M <= 16 on small calls, with dX
+//                    blocks that each sum a whole reduction: no partials and no
+//                    summing launch.
 //   k_lin_bwd_fused_small  both products for M <= 64 in one launch (on request).
 //   k_repack         zero-padded copies for bf16 calls whose K or N is not a
 //                    multiple of 8 or whose pointers are not 16-byte aligned.
@@ -1219,6 +1222,118 @@ __global__ __launch_bounds__(256) void k_dx_smallm(SmallParams p) {
     dx_small_block<MB>(p, blockIdx.x, (LDS char *)smem_raw);
 }
 
+// dX for M <= 16 on small calls (plan::rows16_fits) without split partials,
+// so without the launch that sums them: block b owns dX columns k0 = 16b ..
+// +15 over the whole reduction, and wave w takes the w-th quarter of n in
+// chunks of 128: W's 16 rows come by DMA through a ring of its own (four
+// slots of 16 rows x 256 bytes; 16-byte chunk c of row r at chunk c ^ r),
+// dY's fragments straight from memory into registers three chunks ahead (dY
+// is at most 16 rows and stays in the caches).  Every chunk is issued, the
+// ones past the wave's range reading zero, so the loop has no branches and
+// one wait count.  The four waves' sums are added in wave order through LDS.
+// 64 KiB of LDS: two blocks per CU, beside dW's blocks in k_smallm_pair16.
+constexpr int kR16CH = 128, kR16Row = 256, kR16S = 4, kR16Slot = 16 * kR16Row;
+constexpr int kR16Lds = 4 * kR16S * kR16Slot;
+
+__device__ __forceinline__ bf16x8_t load16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ void dx_rows16_block(const SmallParams &p, int b, LDS char *smem) {
+    constexpr int kPer = 4 + 4; // per chunk: 4 DMA instructions (4 rows x 256 B each), 4 fragment loads
+    static_assert((kR16S - 1) * kPer <= 63, "the chunks in flight fit the vmcnt counter");
+    const int64_t M = p.M, K = p.K, N = p.N;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t k0 = (int64_t)b * 16;
+    const int64_t qn = ((N + 3) / 4 + kR16CH - 1) / kR16CH * kR16CH;
+    const int64_t n_beg = min(N, (int64_t)w * qn), n_end = min(N, n_beg + qn);
+    const int nc = (int)((n_end - n_beg + kR16CH - 1) / kR16CH);
+    const int nc4 = (nc + kR16S - 1) / kR16S * kR16S;
+    LDS char *const ring = smem + w * (kR16S * kR16Slot);
+    // windows: the block's 16 rows of W, all of dY (2MN < 2^31); out-of-range
+    // rows and columns read zero through the window or kOOB
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.W + k0 * N, (uint32_t)(2 * min<int64_t>(16, K - k0) * N));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.G, (uint32_t)(2 * M * N));
+    const int drow = lane >> 4, dchunk = lane & 15; // DMA: row within the instruction, LDS chunk
+    const int sw = lane & 15, q4 = lane >> 4;       // fragments: row, 8-element group
+    bf16x8_t gbuf[kR16S][4];
+    f32x4_t acc = f32x4_t{};
+    auto issue = [&](int j, auto slc) __attribute__((always_inline)) {
+        constexpr int SL = decltype(slc)::value;
+        const int64_t c0 = n_beg + (int64_t)j * kR16CH;
+        LDS char *slot = ring + SL * kR16Slot;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * i + drow;
+            const int64_t n = c0 + 8 * (dchunk ^ r);
+            dma16_nt(rw, slot + i * 1024, oob_unless(k0 + r < K && n < n_end, (uint32_t)(2 * (r * N + n))));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t n = c0 + 32 * u + 8 * q4;
+            gbuf[SL][u] = load16(rg, oob_unless(sw < M && n < n_end, (uint32_t)(2 * (sw * N + n))));
+        }
+    };
+    // chunk j from slot SL, after issuing chunk j + 3 into the slot chunk j - 1 used
+    auto step = [&](int j, auto slc) __attribute__((always_inline)) {
+        constexpr int SL = decltype(slc)::value;
+        issue(j + kR16S - 1, std::integral_constant<int, (SL + kR16S - 1) % kR16S>{});
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kR16S - 1) * kPer) : "memory");
+        const LDS char *slot = ring + SL * kR16Slot;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            bf16x8_t wf[1], gf[1];
+            wf[0] = read_rc<0>(slot + sw * kR16Row + (((4 * u + q4) ^ sw) << 4));
+            gf[0] = gbuf[SL][u];
+            lgkm_wait_wg<1, 1>(wf, gf);
+            // lane l: dX[m = l%16][k0 + 4(l/16) .. +3]
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[0], gf[0], acc, 0, 0, 0);
+        }
+    };
+    issue(0, std::integral_constant<int, 0>{});
+    issue(1, std::integral_constant<int, 1>{});
+    issue(2, std::integral_constant<int, 2>{});
+    for (int jc = 0; jc < nc4; jc += kR16S) {
+        step(jc, std::integral_constant<int, 0>{});
+        step(jc + 1, std::integral_constant<int, 1>{});
+        step(jc + 2, std::integral_constant<int, 2>{});
+        step(jc + 3, std::integral_constant<int, 3>{});
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // the last (zero-reading) DMA into the ring too
+    LDS f32x4_t *const sums = (LDS f32x4_t *)smem;
+    __syncthreads(); // every wave is done with its ring
+    sums[w * 64 + lane] = acc;
+    __syncthreads();
+    if (w != 0)
+        return;
+    f32x4_t t = sums[lane];
+#pragma unroll
+    for (int v = 1; v < 4; ++v)
+        t += sums[v * 64 + lane];
+    const int64_t k = k0 + 4 * q4; // K % 8 == 0: k .. k+3 all in range or all out
+    if (sw < M && k < K) {
+        const u32x2_t pk = {pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
+        *reinterpret_cast<u32x2_t *>(p.dX + sw * K + k) = pk;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_dx_rows16(SmallParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kR16Lds];
+    dx_rows16_block(p, blockIdx.x, (LDS char *)smem_raw);
+}
+
+// both products for the same calls: blocks below dx_blocks run dx_rows16_block,
+// the rest k_dw_smallm's blocks (LDS: the larger of the two, two blocks per CU)
+__global__ __launch_bounds__(256) void k_smallm_pair16(SmallParams p) {
+    static_assert(kR16Lds <= 80 * 1024 && kDwsLds <= 80 * 1024, "two blocks fit a CU's LDS");
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kR16Lds > kDwsLds ? kR16Lds : kDwsLds];
+    if ((int)blockIdx.x < p.dx_blocks)
+        dx_rows16_block(p, blockIdx.x, (LDS char *)smem_raw);
+    else
+        dw_small_block(p, blockIdx.x - p.dx_blocks, (LDS char *)smem_raw);
+}
+
 // Both small-M products in one launch (where plan::pair_fits: M <= 64 and
 // limits on N and K*N): blocks below dx_blocks run dX blocks
 // with a ring of 128-element chunks, the rest dW blocks.  At 128 elements a
@@ -2115,6 +2230,21 @@ hipError_t launch_lin_bwd_aligned(const LinBwdArgs &a, bool need_dx, bool need_d
             const int64_t blocks = groups * sp.mgroups * splits;
             if (blocks > 0x7fffffff)
                 return hipErrorInvalidConfiguration;
+            if (plan::rows16_fits(a.M, a.K, a.N)) {
+                // no split partials: dX alone, or dX and dW in one launch
+                sp.splits = 1;
+                sp.part = nullptr;
+                sp.dx_blocks = (int)((a.K + 15) / 16);
+                int64_t total = sp.dx_blocks;
+                if (small_dw) {
+                    sp.dw_tiles_n = ceil_div(a.N, kDwsBN);
+                    total += (int64_t)sp.dw_tiles_n * ceil_div(a.K, kDwsBK);
+                    hipLaunchKernelGGL(k_smallm_pair16, dim3((unsigned)total), dim3(256), 0, s, sp);
+                } else {
+                    hipLaunchKernelGGL(k_dx_rows16, dim3((unsigned)total), dim3(256), 0, s, sp);
+                }
+                return hipGetLastError();
+            }
             if (small_dw && plan::pair_fits(a.M, a.K, a.N)) {
                 // both products in one launch (mb <= 4); the dX split partials,
                 // if any, are added by a launch of their own

@@ -5,6 +5,7 @@
 //   tlen N sx                     -> ranges and range length for sx
 //   red N chunk units M K cap     -> small-M kernel splits and split length
 //   pair M K N                    -> 1 if both small-M products share a launch
+//   r16 M K N                     -> 1 if dX sums whole reductions at small M
 #include "dispatch.h"
 
 #include <cstdio>
@@ -36,6 +37,10 @@ int main() {
             if (std::scanf("%lld %lld %lld", v, v + 1, v + 2) != 3)
                 return 2;
             std::printf("%d\n", lb::plan::pair_fits(v[0], v[1], v[2]) ? 1 : 0);
+        } else if (!std::strcmp(op, "r16")) {
+            if (std::scanf("%lld %lld %lld", v, v + 1, v + 2) != 3)
+                return 2;
+            std::printf("%d\n", lb::plan::rows16_fits(v[0], v[1], v[2]) ? 1 : 0);
         } else {
             return 2;
         }

@@ -2,8 +2,8 @@
 CPU: the launch-length model against a plain tile-by-tile simulation, the dX range counts
 against the fastest counts measured on the GPU with the count forced (the sweeps listed in
 dispatch.h), the invariants every range count must keep (partials within the workspace,
-ranges of whole 64-element pairs covering the reduction), and the limits of the one-launch
-small-M pair.
+ranges of whole 64-element pairs covering the reduction), the limits of the one-launch
+small-M pair and of the small-M dX that sums whole reductions (no split partials).
 """
 import heapq
 import os
@@ -130,5 +130,15 @@ def test_small_m_pair_limits(probe):
              ((28, 2056, 8192), 1), ((32, 4096, 8192), 0), ((32, 1024, 8200), 0), ((12, 8192, 8192), 0),
              ((48, 2048, 16384), 0), ((16, 16384, 2048), 1), ((64, 8, 264), 1)]
     got = probe(["pair %d %d %d" % c for c, _ in cases])
+    for (c, want), (g,) in zip(cases, got):
+        assert g == want, c
+
+
+def test_small_m_whole_reduction_limits(probe):
+    cases = [((16, 1024, 2048), 1), ((17, 1024, 2048), 0), ((1, 1024, 1024), 1), ((16, 2056, 1024), 0),
+             ((8, 4096, 4096), 0), ((16, 512, 2048), 1), ((16, 512, 2056), 0), ((16, 512, 4096), 0),
+             ((4, 4096, 256), 1), ((4, 4096, 248), 0), ((4, 504, 2016), 0), ((3, 16, 8), 0),
+             ((16, 8, 262144), 0)]
+    got = probe(["r16 %d %d %d" % c for c, _ in cases])
     for (c, want), (g,) in zip(cases, got):
         assert g == want, c

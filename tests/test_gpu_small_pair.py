@@ -14,6 +14,11 @@ dX and dW kernels compute, in the same order, so these tests check:
 * both sides of the N = 8192 limit, ragged K and N, every row-block width (M <= 16, <= 32,
   <= 64), and a wide N beside a K*N above the wide limit (two launches there).
 
+For M <= 16 on small calls (K >= 512, 256 <= N <= min(4096, 4K), K*N <= 2^21) the dX blocks
+sum a whole reduction each instead (16 W rows per block, the four waves' quarter sums added in
+order), with no partials and no summing launch, both in the one-launch pair and for dX alone,
+so the same checks hold there.
+
 Outputs sit between NaN-poisoned guard bands that must stay intact.  Every call goes
 through the C ABI of liblinbwd.so.
 """
@@ -35,7 +40,11 @@ DEV = "cuda"
 # groups, one dW row of tiles)
 SHAPES = [(1, 4096, 4096), (16, 1024, 2048), (17, 2048, 1024), (32, 4096, 4096), (40, 520, 1032),
           (64, 4096, 4096), (64, 1040, 8192), (32, 1024, 8200), (5, 4100, 4100), (24, 64, 8192),
-          (28, 2056, 8192), (8, 4096, 8192), (64, 8, 264)]
+          (28, 2056, 8192), (8, 4096, 8192), (64, 8, 264),
+          # M <= 16 on small calls: dX without partials; at and just past the K*N and N limits;
+          # ragged (padded copies first); a tiny call just outside
+          (1, 1024, 1024), (13, 520, 2056), (9, 1030, 1030), (16, 2048, 1024), (16, 2056, 1024),
+          (4, 1024, 2048), (4, 512, 2056), (6, 4096, 256), (3, 16, 8)]
 
 
 def run(case, need_dx=True, need_dw=True, path=lb.LB_PATH_AUTO):
@@ -73,7 +82,8 @@ def test_pair_matches_the_oracle_and_the_single_product_calls(M, K, N):
     assert torch.equal(dW, dW1)
 
 
-@pytest.mark.parametrize("M,K,N", [(32, 4096, 4096), (64, 1032, 8192), (9, 520, 2056)])
+@pytest.mark.parametrize("M,K,N", [(32, 4096, 4096), (64, 1032, 8192), (9, 520, 2056), (16, 1024, 2048),
+                                   (1, 8, 264), (5, 2048, 512)])
 def test_pair_integer_inputs_bitwise_against_the_element_wise_kernel(M, K, N):
     """Integer inputs in {-2..2}: every product and sum is exact in fp32, so the one-launch
     pair, the forced small-M path and the element-wise kernel give the same bits."""
