@@ -56,8 +56,9 @@ def lin_bwd_tiled_bytes(M, K, N, tile=256, cus_per_xcd=32, xcds=8):
     """HBM bytes the MFMA tile kernel must move for lin_bwd at large M, as a model.
 
     Operands: the kernel's tile order (tiles of each XCD gathered into one range and
-    rastered in groups of 4 tile rows; dX tiles start their reduction at one of four
-    rotated slabs when rows are a multiple of 32 KiB apart) with each XCD running 32
+    rastered in groups of 4 tile rows, 2 for a job with rotated starts; dX tiles start
+    their reduction at one of four rotated slabs when rows are a multiple of 32 KiB
+    apart) with each XCD running 32
     tiles at a time.  A panel (the 256 operand rows or columns that one tile row or
     column reads over the whole reduction) is counted once per group of 32 concurrent
     tiles that reads it from the same starting slab, i.e. the tiles share lines in the
@@ -76,9 +77,10 @@ def lin_bwd_tiled_bytes(M, K, N, tile=256, cus_per_xcd=32, xcds=8):
                 a, b = set(), set()
                 for t in seq[c:c + cus_per_xcd]:
                     u = (t & 7) * (n >> 3) + (t >> 3) if n % 8 == 0 else t
-                    per_group = 4 * tj_n
-                    first_i = (u // per_group) * 4
-                    rows = min(ti_n - first_i, 4)
+                    gi = 2 if rot else 4
+                    per_group = gi * tj_n
+                    first_i = (u // per_group) * gi
+                    rows = min(ti_n - first_i, gi)
                     in_group = u % per_group
                     ti, tj = first_i + in_group % rows, in_group // rows
                     start = (rot * ((tj >> 1) & 3)) % nslab if nslab else 0

@@ -66,6 +66,7 @@ constexpr int kBOffset = kStages * kOperandBytes;  // all A slabs first, then al
 constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KiB
 constexpr int kDmaPerOp = kBK / 8;                // DMA instructions per wave per operand per slab
 constexpr int kGroupI = 4;                        // tile rows per raster group
+constexpr int kGroupIRot = 2;                     // ... for a job whose reduction starts are rotated
 constexpr int kCUs = 256;                         // compute units of the part (8 XCDs x 32)
 constexpr uint32_t kOOB = 0x80000000u;            // buffer offset past num_records: reads 0
 
@@ -303,6 +304,11 @@ __device__ __forceinline__ void slab_barrier() {
 // different XCDs (round-robin dispatch), so first gather each XCD's blocks
 // into one contiguous range of tiles, then raster that range in groups of
 // kGroupI tile rows so concurrently running tiles share operand panels in L2.
+// A job with rotated reduction starts (rows 32 KiB apart) takes groups of
+// kGroupIRot rows: measured on M = 16384, N = 16384 (K = 4096) dX alone 1307
+// -> 1407 TFLOP/s, both products 1414 -> 1439, and N = 32768 1349 -> 1428;
+// level (within 0.5%) at M <= 8192 or K = 1024; the same bits.  For all jobs
+// two-row groups made the QKV and down projections 1-1.6% slower.
 __device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, int &tj, int &sp) {
     int u = t;
     if ((jb.ntiles & 7) == 0)
@@ -311,10 +317,11 @@ __device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, i
     const int tps = jb.tiles_i * jb.tiles_j;
     sp = u / tps;
     u -= sp * tps;
-    const int per_group = kGroupI * jb.tiles_j;
+    const int gi = jb.rot != 0 ? kGroupIRot : kGroupI;
+    const int per_group = gi * jb.tiles_j;
     const int group = u / per_group;
-    const int first_i = group * kGroupI;
-    const int rows = min(jb.tiles_i - first_i, kGroupI);
+    const int first_i = group * gi;
+    const int rows = min(jb.tiles_i - first_i, gi);
     const int in_group = u - group * per_group;
     ti = first_i + in_group % rows;
     tj = in_group / rows;

@@ -60,8 +60,9 @@ def test_tile_traffic_model_closed_forms():
 
 def test_tile_traffic_model_rotation_splits_sharing():
     # rows 32 KiB apart (N = 16384): tiles of the four rotation groups (by tile
-    # column) read the dX panels from different starting slabs, so the 4 x 8 group
-    # fetches 4 x 4 + 8 panels instead of 4 + 8
+    # column) read the dX panels from different starting slabs, so an XCD's 16 dX
+    # tiles (2 tile rows x 8 columns for a rotated job) fetch 2 x 4 + 8 panels instead
+    # of 2 + 8
     M, K, N = 4096, 2048, 16384
     dx_tiles = (M // 256) * (K // 256)          # 128: 16 per XCD, fewer than 32
     assert dx_tiles % 8 == 0
