@@ -64,7 +64,7 @@ def lin_bwd_tiled_bytes(M, K, N, tile=256, cus_per_xcd=32, xcds=8):
     tiles that reads it from the same starting slab, i.e. the tiles share lines in the
     XCD's L2 while they run and keep nothing for the next group.  Outputs: dX bf16 and
     dW fp32 written once.  Measured FETCH_SIZE + WRITE_SIZE of the kernel is this
-    figure within 0.3% on the block's QKV, out and down projections.
+    figure within 0.3-0.8% on the block's QKV, out and down projections.
     """
     def job(I, J, R, rot, offset):
         ti_n, tj_n = -(-I // tile), -(-J // tile)
