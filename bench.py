@@ -56,7 +56,8 @@ def lin_bwd_tiled_bytes(M, K, N, tile=256, cus_per_xcd=32, xcds=8):
     """HBM bytes the MFMA tile kernel must move for lin_bwd at large M, as a model.
 
     Operands: the kernel's tile order (tiles of each XCD gathered into one range and
-    rastered in groups of 4 tile rows, 2 for a job with rotated starts; dX tiles start
+    rastered in groups of 4 tile rows, 2 for a job with rotated starts or a dW job of
+    at most 16 x 16 tiles over a reduction of at most 2048; dX tiles start
     their reduction at one of four rotated slabs when rows are a multiple of 32 KiB
     apart) with each XCD running 32
     tiles at a time.  A panel (the 256 operand rows or columns that one tile row or
@@ -66,7 +67,7 @@ def lin_bwd_tiled_bytes(M, K, N, tile=256, cus_per_xcd=32, xcds=8):
     dW fp32 written once.  Measured FETCH_SIZE + WRITE_SIZE of the kernel is this
     figure within 0.3-0.8% on the block's QKV, out and down projections.
     """
-    def job(I, J, R, rot, offset):
+    def job(I, J, R, rot, offset, dw=False):
         ti_n, tj_n = -(-I // tile), -(-J // tile)
         n = ti_n * tj_n
         nslab = -(-R // 32)
@@ -77,7 +78,7 @@ def lin_bwd_tiled_bytes(M, K, N, tile=256, cus_per_xcd=32, xcds=8):
                 a, b = set(), set()
                 for t in seq[c:c + cus_per_xcd]:
                     u = (t & 7) * (n >> 3) + (t >> 3) if n % 8 == 0 else t
-                    gi = 2 if rot else 4
+                    gi = 2 if rot or (dw and ti_n <= 16 and tj_n <= 16 and R <= 2048) else 4
                     per_group = gi * tj_n
                     first_i = (u // per_group) * gi
                     rows = min(ti_n - first_i, gi)
@@ -95,7 +96,7 @@ def lin_bwd_tiled_bytes(M, K, N, tile=256, cus_per_xcd=32, xcds=8):
     n_dw = -(-K // tile) * -(-N // tile)
     dx_first = N >= M      # the job with the longer reduction takes the first blocks
     dx = job(M, K, N, rot, 0 if dx_first else n_dw)
-    dw = job(K, N, M, 0, n_dx if dx_first else 0)
+    dw = job(K, N, M, 0, n_dx if dx_first else 0, dw=True)
     return dx + dw + 2 * M * K + 4 * K * N
 
 

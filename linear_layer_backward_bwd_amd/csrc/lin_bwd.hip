@@ -308,7 +308,12 @@ __device__ __forceinline__ void slab_barrier() {
 // kGroupIRot rows: measured on M = 16384, N = 16384 (K = 4096) dX alone 1307
 // -> 1407 TFLOP/s, both products 1414 -> 1439, and N = 32768 1349 -> 1428;
 // level (within 0.5%) at M <= 8192 or K = 1024; the same bits.  For all jobs
-// two-row groups made the QKV and down projections 1-1.6% slower.
+// two-row groups made the QKV and down projections 1-1.6% slower.  So does a
+// dW job of at most 16 x 16 tiles over a reduction of at most 2048 (K, N <=
+// 4096, M <= 2048: the calls of a data-parallel shard), where it measured,
+// both products, K = N = 4096: M = 512 56.1 -> 51.9 us, 1024 82.9 -> 80.1,
+// 2048 115.8 -> 113.5 (level with K or N = 2048; 0.5-1.3% slower at M = 4096
+// and 8192, which keep four rows).
 __device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, int &tj, int &sp) {
     int u = t;
     if ((jb.ntiles & 7) == 0)
@@ -317,7 +322,8 @@ __device__ __forceinline__ void tile_coords(const TileJob &jb, int t, int &ti, i
     const int tps = jb.tiles_i * jb.tiles_j;
     sp = u / tps;
     u -= sp * tps;
-    const int gi = jb.rot != 0 ? kGroupIRot : kGroupI;
+    const bool short_dw = jb.kind == JOB_DW && jb.tiles_i <= 16 && jb.tiles_j <= 16 && jb.R <= 2048;
+    const int gi = jb.rot != 0 || short_dw ? kGroupIRot : kGroupI;
     const int per_group = gi * jb.tiles_j;
     const int group = u / per_group;
     const int first_i = group * gi;
